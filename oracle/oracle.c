@@ -1,0 +1,333 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for masked attention, the KV-split merge
+ * and the tile classification of a mask.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this library.  It shares no source with the GPU
+ * library (no headers, helpers or tables): every definition below is written out
+ * again from the pages.
+ *
+ * Sources (the pages this follows):
+ *   [UA]  UltraAttn blog post ("UltraAttn: hierarchical context tiling"), 3 (Full /
+ *         Causal / Empty blocks), 3.1 (Q split: outputs are independent),
+ *         3.2 (KV split: keep a mergeable (max, normaliser, weighted sum) summary,
+ *         merge by rescaling both to the common max), 3.3 (2-D block view).
+ *   [MA]  MagiAttention v1.1.0 news, "Blackwell adaptation" list (flexible masks,
+ *         block-sparse mask generation, CSR mask metadata).
+ *   [FT]  FlashAttention-T post, FlashAttention lineage paragraph (tiling with an
+ *         incremental softmax gives the exact softmax, so the plain two-pass
+ *         softmax below is the definition the tiled kernel must reproduce).
+ *
+ * Readings taken where the pages are silent (each is listed in the design notes):
+ *   - overlapping slices: the mask is the union of the slices' pair sets;
+ *   - a causal slice (q0,q1,k0,k1) admits (i,j) iff j - k1 <= i - q1
+ *     (bottom-right aligned; equals j <= i when k1 == q1);
+ *   - a row with no admitted key: O = 0, LSE = -inf (the merge identity);
+ *   - LSE is the natural log-sum-exp of the scaled scores;
+ *   - GQA: query head h reads key/value head h / (Hq/Hkv).
+ *
+ * Every function here is pinned by tests (brute force, closed forms, split/merge,
+ * mask invariance, tile counts); none is "parity unpinned".
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    int32_t q0, q1, k0, k1, type; /* type 0 = full, 1 = causal */
+} oracle_slice;
+
+/* bf16 -> fp64, exact: a bf16 is the top half of an IEEE binary32. */
+static double bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* ---------------------------------------------------------------------------
+ * Row key set U(i) as a sorted list of disjoint half-open intervals.
+ * U(i) = union over slices s with q0 <= i < q1 of
+ *        { j : k0 <= j < k1 and (full or j - k1 <= i - q1) }.
+ * --------------------------------------------------------------------------- */
+typedef struct {
+    int64_t lo, hi;
+} interval;
+
+static int cmp_interval(const void *a, const void *b)
+{
+    const interval *x = (const interval *)a, *y = (const interval *)b;
+    if (x->lo != y->lo) return x->lo < y->lo ? -1 : 1;
+    if (x->hi != y->hi) return x->hi < y->hi ? -1 : 1;
+    return 0;
+}
+
+/* Writes at most n_slices intervals into out; returns how many after merging. */
+static int row_key_set(const oracle_slice *s, int n_slices, int64_t i, interval *out)
+{
+    int m = 0;
+    for (int t = 0; t < n_slices; ++t) {
+        if (i < s[t].q0 || i >= s[t].q1) continue;
+        int64_t lo = s[t].k0, hi = s[t].k1;
+        if (s[t].type == 1) {
+            int64_t last = i - (int64_t)s[t].q1 + (int64_t)s[t].k1; /* largest admitted j */
+            if (hi > last + 1) hi = last + 1;
+        }
+        if (lo < hi) {
+            out[m].lo = lo;
+            out[m].hi = hi;
+            ++m;
+        }
+    }
+    if (m <= 1) return m;
+    qsort(out, (size_t)m, sizeof(interval), cmp_interval);
+    int w = 0;
+    for (int t = 1; t < m; ++t) {
+        if (out[t].lo <= out[w].hi) { /* overlapping or touching: a set union */
+            if (out[t].hi > out[w].hi) out[w].hi = out[t].hi;
+        } else {
+            out[++w] = out[t];
+        }
+    }
+    return w + 1;
+}
+
+/* Number of admitted (i, j) pairs summed over rows i in [0, sq). */
+int64_t oracle_pair_count(const oracle_slice *s, int32_t n_slices, int32_t sq)
+{
+    interval *buf = (interval *)malloc(sizeof(interval) * (size_t)(n_slices > 0 ? n_slices : 1));
+    int64_t total = 0;
+    for (int64_t i = 0; i < sq; ++i) {
+        int m = row_key_set(s, n_slices, i, buf);
+        for (int t = 0; t < m; ++t) total += buf[t].hi - buf[t].lo;
+    }
+    free(buf);
+    return total;
+}
+
+/* Row key set exported for tests: returns the interval count, fills lo/hi. */
+int32_t oracle_row_key_set(const oracle_slice *s, int32_t n_slices, int64_t i,
+                           int64_t *lo, int64_t *hi)
+{
+    interval *buf = (interval *)malloc(sizeof(interval) * (size_t)(n_slices > 0 ? n_slices : 1));
+    int m = row_key_set(s, n_slices, i, buf);
+    for (int t = 0; t < m; ++t) {
+        lo[t] = buf[t].lo;
+        hi[t] = buf[t].hi;
+    }
+    free(buf);
+    return m;
+}
+
+/* ---------------------------------------------------------------------------
+ * Tile classification ([UA] 3, [MA] CSR metadata).  The (Bq x Bk) tile at
+ * (qt, kt) is Full when every in-range pair is admitted, Empty when none is,
+ * Causal ("partial") otherwise.  Counts are taken row by row from U(i): a
+ * different route from any geometric per-slice compiler.
+ * Output: row_ptr[n_qt + 1], col[nnz] ascending per row, tag[nnz] (1 full,
+ * 2 partial).  Returns 0 on success, -1 when cap is too small (nnz still set).
+ * --------------------------------------------------------------------------- */
+int32_t oracle_tile_csr(const oracle_slice *s, int32_t n_slices, int32_t sq, int32_t sk,
+                        int32_t bq, int32_t bk, int32_t *row_ptr, int32_t *col,
+                        uint8_t *tag, int64_t cap, int64_t *nnz_out)
+{
+    int64_t n_qt = (sq + bq - 1) / bq, n_kt = (sk + bk - 1) / bk;
+    int64_t *count = (int64_t *)calloc((size_t)(n_kt > 0 ? n_kt : 1), sizeof(int64_t));
+    interval *buf = (interval *)malloc(sizeof(interval) * (size_t)(n_slices > 0 ? n_slices : 1));
+    int64_t nnz = 0;
+    int32_t rc = 0;
+    row_ptr[0] = 0;
+    for (int64_t qt = 0; qt < n_qt; ++qt) {
+        int64_t r0 = qt * bq, r1 = r0 + bq < sq ? r0 + bq : sq;
+        memset(count, 0, sizeof(int64_t) * (size_t)n_kt);
+        for (int64_t i = r0; i < r1; ++i) {
+            int m = row_key_set(s, n_slices, i, buf);
+            for (int t = 0; t < m; ++t) {
+                int64_t lo = buf[t].lo < 0 ? 0 : buf[t].lo;
+                int64_t hi = buf[t].hi > sk ? sk : buf[t].hi;
+                /* add the overlap of [lo, hi) with each key tile */
+                for (int64_t j = lo; j < hi;) {
+                    int64_t kt = j / bk, tile_end = (kt + 1) * bk;
+                    int64_t e = hi < tile_end ? hi : tile_end;
+                    count[kt] += e - j;
+                    j = e;
+                }
+            }
+        }
+        for (int64_t kt = 0; kt < n_kt; ++kt) {
+            if (count[kt] == 0) continue;
+            int64_t c0 = kt * bk, c1 = c0 + bk < sk ? c0 + bk : sk;
+            int64_t area = (r1 - r0) * (c1 - c0);
+            if (nnz < cap) {
+                col[nnz] = (int32_t)kt;
+                tag[nnz] = (uint8_t)(count[kt] == area ? 1 : 2);
+            } else {
+                rc = -1;
+            }
+            ++nnz;
+        }
+        row_ptr[qt + 1] = (int32_t)nnz;
+    }
+    free(buf);
+    free(count);
+    *nnz_out = nnz;
+    return rc;
+}
+
+/* ---------------------------------------------------------------------------
+ * Attention forward, plain fp64, two passes, no tiling.
+ * Layouts (contiguous, row-major): q [sq, hq, d], k and v [sk, hkv, d] as bf16
+ * bit patterns.  For each requested (h, i):
+ *   s_j = scale * sum_t q[i,h,t] k[j,g,t]   for j in U(i), g = h / (hq/hkv)
+ *   U(i) empty -> O = 0, LSE = -inf
+ *   else M = max s_j, LSE = M + ln sum_j exp(s_j - M),
+ *        O = sum_j exp(s_j - LSE) v[j,g,:].
+ * Rows are given as (h, i) pairs in rows[2*r], rows[2*r+1]; when rows is NULL
+ * every (h, i) is computed and o is [sq, hq, d], lse [hq, sq].  Otherwise o is
+ * [n_rows, d] and lse [n_rows].
+ * --------------------------------------------------------------------------- */
+typedef struct {
+    const uint16_t *q, *k, *v;
+    int32_t sq, sk, hq, hkv, d;
+    const oracle_slice *s;
+    int32_t n_slices;
+    double scale;
+    const int64_t *rows;
+    int64_t n_rows;
+    double *o, *lse;
+    int32_t n_threads, tid;
+} attn_job;
+
+static void attn_one_row(const attn_job *J, int64_t h, int64_t i, double *o_row, double *lse_out,
+                         interval *ivs, double *scores)
+{
+    const int d = J->d;
+    const int64_t g = h / (J->hq / J->hkv);
+    const int m = row_key_set(J->s, J->n_slices, i, ivs);
+    int64_t n_keys = 0;
+    for (int t = 0; t < m; ++t) {
+        int64_t lo = ivs[t].lo < 0 ? 0 : ivs[t].lo, hi = ivs[t].hi > J->sk ? J->sk : ivs[t].hi;
+        if (lo < hi) n_keys += hi - lo;
+    }
+    for (int t = 0; t < d; ++t) o_row[t] = 0.0;
+    if (n_keys == 0) {
+        *lse_out = -INFINITY;
+        return;
+    }
+    const uint16_t *qi = J->q + ((size_t)i * J->hq + (size_t)h) * d;
+    /* pass 1: scores and their maximum */
+    double mx = -INFINITY;
+    int64_t c = 0;
+    for (int t = 0; t < m; ++t) {
+        int64_t lo = ivs[t].lo < 0 ? 0 : ivs[t].lo, hi = ivs[t].hi > J->sk ? J->sk : ivs[t].hi;
+        for (int64_t j = lo; j < hi; ++j) {
+            const uint16_t *kj = J->k + ((size_t)j * J->hkv + (size_t)g) * d;
+            double acc = 0.0;
+            for (int e = 0; e < d; ++e) acc += bf16_to_double(qi[e]) * bf16_to_double(kj[e]);
+            scores[c] = J->scale * acc;
+            if (scores[c] > mx) mx = scores[c];
+            ++c;
+        }
+    }
+    /* pass 2: normaliser, log-sum-exp, weighted sum of values */
+    double sum = 0.0;
+    for (int64_t t = 0; t < n_keys; ++t) sum += exp(scores[t] - mx);
+    const double lse = mx + log(sum);
+    c = 0;
+    for (int t = 0; t < m; ++t) {
+        int64_t lo = ivs[t].lo < 0 ? 0 : ivs[t].lo, hi = ivs[t].hi > J->sk ? J->sk : ivs[t].hi;
+        for (int64_t j = lo; j < hi; ++j) {
+            const double p = exp(scores[c] - lse);
+            const uint16_t *vj = J->v + ((size_t)j * J->hkv + (size_t)g) * d;
+            for (int e = 0; e < d; ++e) o_row[e] += p * bf16_to_double(vj[e]);
+            ++c;
+        }
+    }
+    *lse_out = lse;
+}
+
+static void *attn_worker(void *arg)
+{
+    const attn_job *J = (const attn_job *)arg;
+    interval *ivs = (interval *)malloc(sizeof(interval) * (size_t)(J->n_slices > 0 ? J->n_slices : 1));
+    double *scores = (double *)malloc(sizeof(double) * (size_t)(J->sk > 0 ? J->sk : 1));
+    const int64_t total = J->rows ? J->n_rows : (int64_t)J->hq * J->sq;
+    for (int64_t r = J->tid; r < total; r += J->n_threads) {
+        int64_t h, i;
+        double *o_row, *lse_ptr;
+        if (J->rows) {
+            h = J->rows[2 * r];
+            i = J->rows[2 * r + 1];
+            o_row = J->o + (size_t)r * J->d;
+            lse_ptr = J->lse + r;
+        } else {
+            h = r / J->sq;
+            i = r % J->sq;
+            o_row = J->o + ((size_t)i * J->hq + (size_t)h) * J->d;
+            lse_ptr = J->lse + (size_t)h * J->sq + (size_t)i;
+        }
+        attn_one_row(J, h, i, o_row, lse_ptr, ivs, scores);
+    }
+    free(scores);
+    free(ivs);
+    return NULL;
+}
+
+int32_t oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int32_t sq,
+                        int32_t sk, int32_t hq, int32_t hkv, int32_t d, const oracle_slice *slices,
+                        int32_t n_slices, double scale, const int64_t *rows, int64_t n_rows,
+                        double *o, double *lse, int32_t n_threads)
+{
+    if (hkv <= 0 || hq % hkv != 0 || d <= 0) return -1;
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > 256) n_threads = 256;
+    pthread_t th[256];
+    attn_job jobs[256];
+    for (int t = 0; t < n_threads; ++t) {
+        attn_job J = {q, k, v, sq, sk, hq, hkv, d, slices, n_slices, scale, rows, n_rows, o, lse,
+                      n_threads, t};
+        jobs[t] = J;
+    }
+    for (int t = 1; t < n_threads; ++t) pthread_create(&th[t], NULL, attn_worker, &jobs[t]);
+    attn_worker(&jobs[0]);
+    for (int t = 1; t < n_threads; ++t) pthread_join(th[t], NULL);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Merge of KV-split partials ([UA] 3.2).  Each partial k carries (LSE_k, O_k)
+ * with O_k already normalised by its own denominator.  With M the largest
+ * finite LSE_k:
+ *   LSE = M + ln sum_k exp(LSE_k - M),  O = sum_k exp(LSE_k - LSE) O_k.
+ * All partials at -inf -> O = 0, LSE = -inf (a partial at -inf is the identity).
+ * o_parts is [n, R, d] and lse_parts [n, R] (fp64); o is [R, d], lse [R].
+ * --------------------------------------------------------------------------- */
+void oracle_merge(const double *o_parts, const double *lse_parts, int32_t n, int64_t n_rows,
+                  int32_t d, double *o, double *lse)
+{
+    for (int64_t r = 0; r < n_rows; ++r) {
+        double mx = -INFINITY;
+        for (int32_t t = 0; t < n; ++t) {
+            double x = lse_parts[(size_t)t * n_rows + r];
+            if (x > mx) mx = x;
+        }
+        double *orow = o + (size_t)r * d;
+        for (int e = 0; e < d; ++e) orow[e] = 0.0;
+        if (mx == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double sum = 0.0;
+        for (int32_t t = 0; t < n; ++t) sum += exp(lse_parts[(size_t)t * n_rows + r] - mx);
+        const double total = mx + log(sum);
+        for (int32_t t = 0; t < n; ++t) {
+            const double w = exp(lse_parts[(size_t)t * n_rows + r] - total);
+            const double *src = o_parts + ((size_t)t * n_rows + r) * d;
+            for (int e = 0; e < d; ++e) orow[e] += w * src[e];
+        }
+        lse[r] = total;
+    }
+}
