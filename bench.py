@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the masked flash-attention path on one MI355X.
+
+One step = the whole path for one batch: mask description -> tile CSR -> schedule
+(host, inside the library) -> metadata upload -> forward kernel, for the varlen
+causal workload (16384 packed tokens in 8 documents, 16 heads, head dim 128,
+bf16).  Q, K and V are resident in HBM before the timed region starts.
+
+Printed: one JSON line with the effective forward TFLOPS (4 * d * unmasked pairs *
+heads / step time), the forward kernel's roofline figures (HIP events on the launch
+stream), the fp64 oracle timed on host cores for a bounded sample, and, unless
+--quick, the other four workloads (KV-split + merge included) measured the same way.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def event_times(fn, reps, stream):
+    """Per-launch durations (ms) of fn() measured with events on the launch stream."""
+    import torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def headline(args, api, W):
+    """Varlen causal workload: timed steps of plan build + upload + forward."""
+    import torch
+    w = W.config2()
+    q, k, v = api.to_device_bf16(w.q), api.to_device_bf16(w.k), api.to_device_bf16(w.v)
+    stream = torch.cuda.current_stream()
+    o = torch.empty((w.sq, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.hq, w.sq), dtype=torch.float32, device="cuda")
+
+    def step():
+        plan = api.Plan.from_varlen(w.cu_seqlens, w.hq, w.hkv, w.d, causal=True).upload(stream)
+        api.attn_fwd(q, k, v, plan, w.scale, out=o, lse=lse, stream=stream)
+        plan.close()     # device metadata freed stream-ordered after the kernel
+
+    info = api.Plan.from_varlen(w.cu_seqlens, w.hq, w.hkv, w.d, causal=True).info()
+    flops = 4.0 * w.d * info["pairs"] * w.hq
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # forward kernel alone, HIP events on its launch stream, inside the same process
+    plan = api.Plan.from_varlen(w.cu_seqlens, w.hq, w.hkv, w.d, causal=True).upload(stream)
+    kt = event_times(lambda: api.attn_fwd(q, k, v, plan, w.scale, out=o, lse=lse, stream=stream),
+                     max(args.steps, 20), stream)
+    kernel_ms = float(np.mean(kt))
+    plan.close()
+    return w, info, flops, ms_per_step, kernel_ms
+
+
+def other_workloads(api, W, reps=10):
+    """Kernel-time figures of the remaining workloads (event-timed, plan prebuilt)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    out = {}
+    for cfg in (1, 3, 4):
+        w = W.CONFIGS[cfg]()
+        q, k, v = api.to_device_bf16(w.q), api.to_device_bf16(w.k), api.to_device_bf16(w.v)
+        plan = api.plan_from_workload(w, stream=stream)
+        info = plan.info()
+        fl = 4.0 * w.d * info["pairs"] * w.hq
+        o = torch.empty((w.sq, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((w.hq, w.sq), dtype=torch.float32, device="cuda")
+        f = lambda: api.attn_fwd(q, k, v, plan, w.scale, out=o, lse=lse, stream=stream)
+        for _ in range(3):
+            f()
+        ms = float(np.median(event_times(f, reps, stream)))
+        out[w.name] = {"kernel_ms": ms, "tflops": fl / ms * 1e-9,
+                       "frac_of_peak": fl / ms * 1e-9 / PEAK_BF16_TFLOPS,
+                       "pairs_per_head": info["pairs"], "tiles_full": info["n_full"],
+                       "tiles_partial": info["n_partial"]}
+        log(f"{w.name}: {ms:.3f} ms  {fl / ms * 1e-9:.1f} TFLOPS")
+        plan.close()
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+
+    # KV split: 8 partial forwards over 8192-token KV chunks, then the merge
+    w = W.config5()
+    c, nc = w.extra["chunk"], w.extra["n_chunks"]
+    q, k, v = api.to_device_bf16(w.q), api.to_device_bf16(w.k), api.to_device_bf16(w.v)
+    plans = [api.Plan.from_slices(sl, c, c, w.hq, w.hkv, w.d).upload(stream)
+             for sl in w.extra["chunk_slices"]]
+    pairs = sum(p.info()["pairs"] for p in plans)
+    fl = 4.0 * w.d * pairs * w.hq
+    os_ = [torch.empty((c, w.hq, w.d), dtype=torch.bfloat16, device="cuda") for _ in range(nc)]
+    ls_ = [torch.empty((w.hq, c), dtype=torch.float32, device="cuda") for _ in range(nc)]
+    om = torch.empty((c, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
+    lm = torch.empty((w.hq, c), dtype=torch.float32, device="cuda")
+
+    def fwd_all():
+        for t in range(nc):
+            api.attn_fwd(q, k[t * c:(t + 1) * c], v[t * c:(t + 1) * c], plans[t], w.scale,
+                         out=os_[t], lse=ls_[t], stream=stream)
+
+    def merge():
+        api.attn_merge(os_, ls_, out=om, lse=lm, stream=stream)
+
+    for _ in range(2):
+        fwd_all()
+        merge()
+    fwd_ms = float(np.median(event_times(fwd_all, reps, stream)))
+    merge_ms = float(np.median(event_times(merge, reps * 2, stream)))
+    merge_bytes = (nc + 1) * c * w.hq * (2 * w.d + 4)
+    out[w.name] = {"forward_ms": fwd_ms, "merge_ms": merge_ms,
+                   "forward_tflops": fl / fwd_ms * 1e-9,
+                   "forward_frac_of_peak": fl / fwd_ms * 1e-9 / PEAK_BF16_TFLOPS,
+                   "forward_plus_merge_tflops": fl / (fwd_ms + merge_ms) * 1e-9,
+                   "merge_gbs": merge_bytes / merge_ms * 1e-6,
+                   "merge_frac_of_hbm_peak": merge_bytes / merge_ms * 1e-6 / PEAK_HBM_GBS,
+                   "pairs_per_head": pairs}
+    log(f"{w.name}: fwd {fwd_ms:.3f} ms ({fl / fwd_ms * 1e-9:.1f} TFLOPS), merge {merge_ms:.3f} ms "
+        f"({merge_bytes / merge_ms * 1e-6:.0f} GB/s)")
+    for p in plans:
+        p.close()
+    return out
+
+
+def cpu_baseline(w, info, target_s):
+    """The fp64 oracle on host cores over a bounded, evenly spread sample of rows."""
+    import oracle
+    threads = min(os.cpu_count() or 1, 16)
+    rng = np.random.default_rng(0)
+    # calibrate: a small sample, then size the real sample to about target_s seconds
+    rows_all = [(h, i) for h in range(w.hq) for i in range(0, w.sq, 7)]
+    rng.shuffle(rows_all)
+    pairs_of = {}
+    cu = w.cu_seqlens
+    def row_pairs(i):
+        doc = int(np.searchsorted(cu, i, side="right")) - 1
+        return i - int(cu[doc]) + 1
+    n = 64
+    while True:
+        rows = rows_all[:n]
+        t0 = time.perf_counter()
+        oracle.attn_fwd(w.q, w.k, w.v, w.slices, w.scale, rows=rows, n_threads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= target_s * 0.5 or n >= len(rows_all):
+            break
+        n = min(len(rows_all), int(n * max(2.0, target_s / max(dt, 1e-3))))
+    pairs = sum(row_pairs(i) for _, i in rows)
+    tflops = 4.0 * w.d * pairs / dt * 1e-12
+    return {"value": tflops, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} (head, row) pairs drawn evenly from the workload "
+                      f"({pairs} unmasked pairs), {dt:.1f} s wall on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="only the headline workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path has no multi-GPU mode here "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_flash_csr_amd import api
+    from block_sparse_flash_csr_amd import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    api.library()
+
+    w, info, flops, ms_per_step, kernel_ms = headline(args, api, W)
+    value = flops / (ms_per_step * 1e-3) * 1e-12
+    achieved = flops / (kernel_ms * 1e-3) * 1e-12
+    log(f"headline: step {ms_per_step:.4f} ms ({value:.1f} TFLOPS), forward kernel {kernel_ms:.4f} ms "
+        f"({achieved:.1f} TFLOPS, {achieved / PEAK_BF16_TFLOPS:.3f} of peak)")
+    others = {} if args.quick else other_workloads(api, W)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, info, args.cpu_seconds)
+
+    result = {
+        "metric": "effective fwd TFLOPS (unmasked pairs) and % of bf16 MFMA peak, 1 GPU",
+        "value": value,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16 N(0,1) Q/K/V; document lengths drawn U[512,4096) and "
+                "rescaled to 16384 tokens, seed 2)",
+        "config": {"workload": w.name, "tokens": w.sq, "documents": len(w.extra["lengths"]),
+                   "doc_lengths": w.extra["lengths"], "heads": w.hq, "head_dim": w.d,
+                   "mask": "varlen causal", "tile": [128, 128], "parallelism": "single GPU",
+                   "step": "plan build (CSR + schedule) + metadata upload + forward"},
+        "frac_of_peak": value / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "attn_fwd_kernel<128>", "kernel_ms": kernel_ms,
+                     "flops_per_launch": flops},
+        "cpu_baseline": cpu,
+        "other_workloads": others,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,280 @@
+"""Thin Python binding over libbsfa.so (include/bsfa.h): argument marshalling only.
+
+Every step of the path (mask compile, schedule, forward, merge) runs inside the
+library.  torch supplies device memory and the current stream.  When the library
+is missing this module raises: there is no Python or CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsfa.so")
+
+BSFA_FULL, BSFA_CAUSAL = 0, 1
+TILE_FULL, TILE_PARTIAL = 1, 2
+MERGE_MAX_PARTS = 16
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "shape mismatch", 3: "misaligned pointer or stride",
+           4: "unsupported head dim or tile size", 5: "invalid mask", 6: "out of memory",
+           7: "HIP runtime error", 8: "plan not uploaded to the current device"}
+
+
+class BsfaError(RuntimeError):
+    def __init__(self, call, status):
+        super().__init__(f"{call}: {_STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+class Slice(ctypes.Structure):
+    _fields_ = [("q0", ctypes.c_int32), ("q1", ctypes.c_int32), ("k0", ctypes.c_int32),
+                ("k1", ctypes.c_int32), ("type", ctypes.c_int32)]
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("stride_tok", ctypes.c_int64),
+                ("stride_head", ctypes.c_int64)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("sq", ctypes.c_int32), ("sk", ctypes.c_int32), ("hq", ctypes.c_int32),
+                ("hkv", ctypes.c_int32), ("d", ctypes.c_int32), ("bq", ctypes.c_int32),
+                ("bk", ctypes.c_int32), ("n_qtiles", ctypes.c_int32), ("n_ktiles", ctypes.c_int32),
+                ("nnz", ctypes.c_int64), ("n_full", ctypes.c_int64), ("n_partial", ctypes.c_int64),
+                ("n_pieces", ctypes.c_int64), ("pairs", ctypes.c_int64), ("n_items", ctypes.c_int32),
+                ("n_bins", ctypes.c_int32), ("makespan", ctypes.c_double),
+                ("total_cost", ctypes.c_double), ("uploaded", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library():
+    """Load libbsfa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m block_sparse_flash_csr_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    lib.bsfa_plan_create.argtypes = [P, I32, I32, I32, I32, I32, I32, I32, I32, PP]
+    lib.bsfa_plan_from_varlen.argtypes = [P, I32, I32, I32, I32, I32, I32, I32, PP]
+    lib.bsfa_plan_from_blocks.argtypes = [P, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, I32, PP]
+    lib.bsfa_plan_upload.argtypes = [P, P]
+    lib.bsfa_plan_destroy.argtypes = [P]
+    lib.bsfa_plan_destroy.restype = None
+    lib.bsfa_plan_get_info.argtypes = [P, ctypes.POINTER(PlanInfo)]
+    lib.bsfa_plan_export_csr.argtypes = [P, P, P, P, I64, ctypes.POINTER(I64)]
+    lib.bsfa_plan_export_schedule.argtypes = [P, P, P, P]
+    lib.bsfa_tile_cost.argtypes = [I32, ctypes.c_double]
+    lib.bsfa_tile_cost.restype = ctypes.c_double
+    lib.bsfa_imbalance_bound.argtypes = [ctypes.c_double, I32]
+    lib.bsfa_imbalance_bound.restype = ctypes.c_double
+    lib.bsfa_lpt_assign.argtypes = [P, I32, I32, P, P]
+    lib.bsfa_lpt_assign.restype = ctypes.c_double
+    lib.bsfa_attn_fwd.argtypes = [ctypes.POINTER(Tensor)] * 3 + [P, ctypes.c_float,
+                                                                 ctypes.POINTER(Tensor), P, I64, P]
+    lib.bsfa_attn_merge.argtypes = [P, P, I32, I64, I64, I64, I32, I32, I32,
+                                    ctypes.POINTER(Tensor), P, P]
+    lib.bsfa_status_str.argtypes = [I32]
+    lib.bsfa_status_str.restype = ctypes.c_char_p
+    for name in ("bsfa_plan_create", "bsfa_plan_from_varlen", "bsfa_plan_from_blocks",
+                 "bsfa_plan_upload", "bsfa_plan_get_info", "bsfa_plan_export_csr",
+                 "bsfa_plan_export_schedule", "bsfa_attn_fwd", "bsfa_attn_merge"):
+        getattr(lib, name).restype = I32
+    _lib = lib
+    return lib
+
+
+def _check(call, status):
+    if status != 0:
+        raise BsfaError(call, status)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream_handle(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Plan:
+    """A compiled mask (tile CSR + pieces) with its schedule.  Host-only until upload()."""
+
+    def __init__(self, handle):
+        self._h = handle
+
+    # -- constructors ---------------------------------------------------------
+    @classmethod
+    def from_slices(cls, slices, sq, sk, hq, hkv, d, bq=128, bk=128):
+        arr = (Slice * max(1, len(slices)))()
+        for t, s in enumerate(slices):
+            arr[t] = Slice(*[int(x) for x in s])
+        h = ctypes.c_void_p()
+        _check("bsfa_plan_create", library().bsfa_plan_create(arr, len(slices), sq, sk, hq, hkv, d,
+                                                               bq, bk, ctypes.byref(h)))
+        return cls(h)
+
+    @classmethod
+    def from_varlen(cls, cu_seqlens, hq, hkv, d, causal=True, bq=128, bk=128):
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        h = ctypes.c_void_p()
+        _check("bsfa_plan_from_varlen", library().bsfa_plan_from_varlen(
+            _ptr(cu), len(cu) - 1, 1 if causal else 0, hq, hkv, d, bq, bk, ctypes.byref(h)))
+        return cls(h)
+
+    @classmethod
+    def from_blocks(cls, codes, block_q, block_k, sq, sk, hq, hkv, d, bq=128, bk=128):
+        c = np.ascontiguousarray(codes, dtype=np.uint8)
+        h = ctypes.c_void_p()
+        _check("bsfa_plan_from_blocks", library().bsfa_plan_from_blocks(
+            _ptr(c), c.shape[0], c.shape[1], block_q, block_k, sq, sk, hq, hkv, d, bq, bk,
+            ctypes.byref(h)))
+        return cls(h)
+
+    # -- lifecycle ------------------------------------------------------------
+    def upload(self, stream=None):
+        _check("bsfa_plan_upload", library().bsfa_plan_upload(self._h, _stream_handle(stream)))
+        return self
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            library().bsfa_plan_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    # -- inspection -----------------------------------------------------------
+    def info(self) -> dict:
+        inf = PlanInfo()
+        _check("bsfa_plan_get_info", library().bsfa_plan_get_info(self._h, ctypes.byref(inf)))
+        return {name: getattr(inf, name) for name, _ in PlanInfo._fields_}
+
+    def csr(self):
+        inf = self.info()
+        row_ptr = np.zeros(inf["n_qtiles"] + 1, np.int32)
+        nnz = inf["nnz"]
+        col = np.zeros(max(1, nnz), np.int32)
+        tag = np.zeros(max(1, nnz), np.uint8)
+        n = ctypes.c_int64(0)
+        _check("bsfa_plan_export_csr", library().bsfa_plan_export_csr(
+            self._h, _ptr(row_ptr), _ptr(col), _ptr(tag), len(col), ctypes.byref(n)))
+        return row_ptr, col[:n.value].copy(), tag[:n.value].copy()
+
+    def schedule(self):
+        inf = self.info()
+        bin_ptr = np.zeros(inf["n_bins"] + 1, np.int32)
+        items = np.zeros(max(1, inf["n_items"]), np.int32)
+        cost = np.zeros(max(1, inf["n_items"]), np.float32)
+        _check("bsfa_plan_export_schedule", library().bsfa_plan_export_schedule(
+            self._h, _ptr(bin_ptr), _ptr(items), _ptr(cost)))
+        return bin_ptr, items[:inf["n_items"]], cost[:inf["n_items"]]
+
+
+def to_device_bf16(bits: np.ndarray, device="cuda"):
+    """Seeded bf16 bit patterns (uint16 numpy) -> a bf16 device tensor of the same shape."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def _tview(t):
+    """bsfa_tensor for a [tokens, heads, d] torch tensor with contiguous last dim."""
+    assert t.dim() == 3 and t.stride(2) == 1, "expected [tokens, heads, d] with d contiguous"
+    return Tensor(ctypes.c_void_p(t.data_ptr()), t.stride(0), t.stride(1))
+
+
+def attn_fwd(q, k, v, plan: Plan, scale: float, out=None, lse=None, stream=None):
+    """Forward over the plan's mask.  q [sq, hq, d], k/v [sk, hkv, d] bf16 CUDA tensors.
+
+    Returns (O [sq, hq, d] bf16, LSE [hq, sq] fp32)."""
+    import torch
+    sq, hq, d = q.shape
+    inf = plan.info()
+    if (sq, hq, d) != (inf["sq"], inf["hq"], inf["d"]):
+        raise ValueError(f"q shape {tuple(q.shape)} does not match the plan "
+                         f"({inf['sq']}, {inf['hq']}, {inf['d']})")
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (inf["sk"], inf["hkv"], inf["d"]):
+            raise ValueError(f"{name} shape {tuple(t.shape)} does not match the plan "
+                             f"({inf['sk']}, {inf['hkv']}, {inf['d']})")
+    if out is None:
+        out = torch.empty((sq, hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((hq, sq), dtype=torch.float32, device=q.device)
+    assert q.dtype == k.dtype == v.dtype == out.dtype == torch.bfloat16
+    assert tuple(out.shape) == (sq, hq, d)
+    assert lse.dtype == torch.float32 and lse.stride(1) == 1 and lse.shape[0] == hq
+    tq, tk, tv, to = _tview(q), _tview(k), _tview(v), _tview(out)
+    _check("bsfa_attn_fwd", library().bsfa_attn_fwd(
+        ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), plan.handle, float(scale),
+        ctypes.byref(to), ctypes.c_void_p(lse.data_ptr()), lse.stride(0), _stream_handle(stream)))
+    return out, lse
+
+
+def attn_merge(o_parts, lse_parts, out=None, lse=None, stream=None):
+    """Merge n partials: o_parts list of [T, H, d] bf16 (same strides), lse_parts list of [H, T] fp32."""
+    import torch
+    n = len(o_parts)
+    assert n == len(lse_parts) and n >= 1
+    t, h, d = o_parts[0].shape
+    st = o_parts[0].stride()
+    for p in o_parts:
+        assert p.shape == (t, h, d) and p.stride() == st and p.dtype == torch.bfloat16
+    lst = lse_parts[0].stride(0)
+    for l in lse_parts:
+        assert l.shape[0] == h and l.stride(0) == lst and l.stride(1) == 1 and l.dtype == torch.float32
+    if out is None:
+        out = torch.empty((t, h, d), dtype=torch.bfloat16, device=o_parts[0].device)
+    if lse is None:
+        lse = torch.empty((h, lst), dtype=torch.float32, device=o_parts[0].device)
+    assert lse.stride(0) == lst
+    optrs = (ctypes.c_void_p * n)(*[p.data_ptr() for p in o_parts])
+    lptrs = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lse_parts])
+    to = _tview(out)
+    _check("bsfa_attn_merge", library().bsfa_attn_merge(
+        optrs, lptrs, n, st[0], st[1], lst, t, h, d, ctypes.byref(to),
+        ctypes.c_void_p(lse.data_ptr()), _stream_handle(stream)))
+    return out, lse[:, :t]
+
+
+def lpt_assign(costs, n_bins):
+    """Scheduler core on an explicit cost list: (bin_of int32 [n], bin_load [n_bins], makespan)."""
+    c = np.ascontiguousarray(costs, dtype=np.float32)
+    bin_of = np.zeros(max(1, len(c)), np.int32)
+    load = np.zeros(max(1, n_bins), np.float64)
+    mk = library().bsfa_lpt_assign(_ptr(c), len(c), n_bins, _ptr(bin_of), _ptr(load))
+    if mk < 0:
+        raise BsfaError("bsfa_lpt_assign", 1)
+    return bin_of[:len(c)], load[:n_bins], mk
+
+
+def plan_from_workload(w, bq=128, bk=128, upload=True, stream=None) -> Plan:
+    """Plan for a workloads.Workload using its native mask form (varlen, blocks or slices)."""
+    if w.cu_seqlens is not None:
+        p = Plan.from_varlen(w.cu_seqlens, w.hq, w.hkv, w.d, causal=True, bq=bq, bk=bk)
+    elif w.block_codes is not None:
+        p = Plan.from_blocks(w.block_codes, w.block[0], w.block[1], w.sq, w.sk, w.hq, w.hkv, w.d,
+                             bq=bq, bk=bk)
+    else:
+        p = Plan.from_slices(w.slices, w.sq, w.sk, w.hq, w.hkv, w.d, bq=bq, bk=bk)
+    if upload:
+        p.upload(stream)
+    return p

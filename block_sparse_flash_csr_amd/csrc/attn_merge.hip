@@ -1,0 +1,103 @@
+// Merge of KV-split partial attention results (UltraAttn blog, 3.2: each key/value
+// shard keeps a mergeable summary; to combine, take the common maximum, rescale
+// every summary to it and add).  With the partial outputs stored normalised, as
+// (O_t, LSE_t):
+//   M = max_t LSE_t,  w_t = exp(LSE_t - M),  LSE = M + ln sum_t w_t,
+//   O = sum_t (w_t / sum_t w_t) O_t;  every LSE_t = -inf  ->  O = 0, LSE = -inf.
+//
+// The kernel is a pure stream: every (token, head) row of every partial is read
+// once and the result written once, so HBM bandwidth bounds it.  A workgroup
+// owns rows (t0 .. t0+R-1, head h): the LSE reads of one partial are then one
+// contiguous run, and each row of O is read as 16-byte pieces by D/8 adjacent
+// lanes.  All n loads of a lane are issued before any arithmetic.
+#include "bsfa_internal.h"
+
+namespace bsfa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.693147180559945309f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int D>
+__global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a)
+{
+    constexpr int TPR = D / 8;               // lanes per row (16 bytes each)
+    constexpr int RPB = kThreads / TPR;      // rows per workgroup
+    const int tid = threadIdx.x;
+    const int t = blockIdx.x * RPB + tid / TPR;
+    const int chunk = tid % TPR;
+    const int h = blockIdx.y;
+    if (t >= a.n_tok) return;
+
+    float lse[BSFA_MERGE_MAX_PARTS];
+    u32x4 ov[BSFA_MERGE_MAX_PARTS];
+    const int64_t lse_off = (int64_t)h * a.lse_sh + t;
+    const int64_t o_off = (int64_t)t * a.p_st + (int64_t)h * a.p_sh + chunk * 8;
+#pragma unroll
+    for (int i = 0; i < BSFA_MERGE_MAX_PARTS; ++i) {
+        if (i < a.n) {
+            lse[i] = a.lse_parts[i][lse_off];
+            ov[i] = *(const u32x4 *)((const __bf16 *)a.o_parts[i] + o_off);
+        }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < BSFA_MERGE_MAX_PARTS; ++i)
+        if (i < a.n) m = fmaxf(m, lse[i]);
+
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float out_lse = -INFINITY;
+    if (m != -INFINITY) {
+        float w[BSFA_MERGE_MAX_PARTS];
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < BSFA_MERGE_MAX_PARTS; ++i) {
+            if (i < a.n) {
+                w[i] = __builtin_amdgcn_exp2f((lse[i] - m) * kLog2e);
+                sum += w[i];
+            }
+        }
+        const float inv = 1.0f / sum;
+#pragma unroll
+        for (int i = 0; i < BSFA_MERGE_MAX_PARTS; ++i) {
+            if (i < a.n) {
+                const float wi = w[i] * inv;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[2 * j] += wi * bf16_lo(ov[i][j]);
+                    acc[2 * j + 1] += wi * bf16_hi(ov[i][j]);
+                }
+            }
+        }
+        out_lse = m + __log2f(sum) * kLn2;
+    }
+    u32x4 res;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const __bf16 lo = (__bf16)acc[2 * j], hi = (__bf16)acc[2 * j + 1];
+        res[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *(u32x4 *)((__bf16 *)a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + chunk * 8) = res;
+    if (chunk == 0) a.lse[lse_off] = out_lse;
+}
+
+}  // namespace
+
+hipError_t launch_attn_merge(const MergeArgs &a, int d, hipStream_t stream)
+{
+    if (a.n_tok <= 0 || a.n_head <= 0) return hipSuccess;
+    const int rpb = kThreads / (d / 8);
+    dim3 grid((a.n_tok + rpb - 1) / rpb, a.n_head);
+    if (d == 128)
+        hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(attn_merge_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace bsfa

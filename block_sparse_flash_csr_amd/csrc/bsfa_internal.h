@@ -1,0 +1,112 @@
+// Internal declarations of libbsfa: the plan (compiled mask + schedule), the
+// device-side metadata layout and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/bsfa.h"
+
+namespace bsfa {
+
+// A slice clipped to one tile.  Pair (i, j) is admitted by the piece iff
+// q_lo <= i < q_hi, k_lo <= j < k_hi and j <= i + diag.  A causal slice
+// (q0, q1, k0, k1) keeps diag = k1 - q1 after clipping, so its diagonal does not
+// move; a full slice uses kDiagFull (no constraint for any i >= 0).
+struct Piece {
+    int32_t q_lo, q_hi, k_lo, k_hi, diag, pad0, pad1, pad2;
+};
+static_assert(sizeof(Piece) == 32, "Piece is two 16-byte words");
+
+// Device form of one CSR entry: key-tile column, first piece, piece count
+// (0 for a full tile) and the tag.
+struct Entry {
+    int32_t col, piece_begin, piece_count, tag;
+};
+static_assert(sizeof(Entry) == 16, "Entry is one 16-byte word");
+
+constexpr int32_t kDiagFull = 1 << 30;
+constexpr int kKernelBq = 128;   // query rows per work item (4 waves x 32)
+constexpr int kKernelBk = 64;    // keys per inner step of the forward kernel
+constexpr int kNumXcd = 8;       // MI355X: 8 accelerator complex dies, 32 CUs each
+constexpr int kNumCu = 256;
+
+// Scheduler cost model, in units of one full 64-key inner step of one item.
+// A partial tile runs the same matrix work plus the per-element mask; the
+// per-item constant covers the Q load and the O/LSE epilogue.
+constexpr double kCostPartial = 1.15;
+constexpr double kCostItem = 1.0;
+
+struct DeviceMeta {
+    const int32_t *row_ptr = nullptr;
+    const Entry *entries = nullptr;
+    const Piece *pieces = nullptr;
+    const int32_t *bin_ptr = nullptr;
+    const int32_t *bin_items = nullptr;
+};
+
+}  // namespace bsfa
+
+struct bsfa_plan {
+    int32_t sq = 0, sk = 0, hq = 0, hkv = 0, d = 0, bq = 0, bk = 0;
+    int32_t n_qt = 0, n_kt = 0;
+    // tile CSR
+    std::vector<int32_t> row_ptr;
+    std::vector<int32_t> col;
+    std::vector<uint8_t> tag;
+    std::vector<int32_t> piece_ptr;    // [nnz + 1]; empty range for full tiles
+    std::vector<bsfa::Piece> pieces;
+    int64_t n_full = 0, n_partial = 0, pairs = 0;
+    // schedule
+    std::vector<float> item_cost;      // by item id = h * n_qt + qt
+    std::vector<int32_t> bin_ptr;      // [n_bins + 1]
+    std::vector<int32_t> bin_items;    // item ids in execution order per bin
+    double makespan = 0.0, total_cost = 0.0;
+    // device copy
+    int device = -1;
+    void *dbuf = nullptr;
+    hipStream_t ustream = nullptr;
+    bool dbuf_async = false;
+    bsfa::DeviceMeta dev;
+    std::vector<uint8_t> staging;   // host image of the device metadata (kept until destroy)
+    hipEvent_t copied = nullptr;    // recorded after the upload copy
+};
+
+namespace bsfa {
+
+// Mask compiler: validated slices -> tile CSR with pieces and the pair count.
+bsfa_status compile_mask(const bsfa_slice *slices, int32_t n_slices, bsfa_plan &p);
+// Scheduler: items, costs and the per-bin lists.
+void build_schedule(bsfa_plan &p, int n_bins_max);
+// Min-heap greedy (LPT) of the given items onto the given bins; appends to lists/load.
+void lpt(const std::vector<int32_t> &items, const std::vector<float> &cost,
+         const std::vector<int32_t> &bins, std::vector<std::vector<int32_t>> &lists,
+         std::vector<double> &load);
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh, lse_sh;
+    int32_t sq, sk, hq, hkv, n_qt, bk_plan;
+    float c;  // scale * log2(e)
+    DeviceMeta meta;
+    int32_t n_bins;
+};
+hipError_t launch_attn_fwd(const FwdArgs &a, int d, hipStream_t stream);
+
+struct MergeArgs {
+    const void *o_parts[BSFA_MERGE_MAX_PARTS];
+    const float *lse_parts[BSFA_MERGE_MAX_PARTS];
+    int32_t n;
+    int64_t p_st, p_sh, lse_sh;
+    int32_t n_tok, n_head;
+    void *o;
+    float *lse;
+    int64_t o_st, o_sh;
+};
+hipError_t launch_attn_merge(const MergeArgs &a, int d, hipStream_t stream);
+
+}  // namespace bsfa

@@ -1,0 +1,371 @@
+// C ABI of libbsfa: argument checks, plan lifecycle and kernel dispatch.
+// The declarations and their contracts are in include/bsfa.h.
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "bsfa_internal.h"
+
+using namespace bsfa;
+
+namespace {
+
+constexpr int kBinsPerCu = 2;  // forward workgroups resident per CU (LDS and VGPR budget)
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool stride_ok(int64_t s) { return s >= 0 && (s & 7) == 0; }
+
+bsfa_status check_slices(const bsfa_slice *s, int32_t n, int32_t sq, int32_t sk)
+{
+    for (int32_t t = 0; t < n; ++t) {
+        const bsfa_slice &x = s[t];
+        if (x.type != BSFA_FULL && x.type != BSFA_CAUSAL) return BSFA_ERR_MASK;
+        if (x.q0 < 0 || x.k0 < 0 || x.q1 < x.q0 || x.k1 < x.k0) return BSFA_ERR_MASK;
+        if (x.q1 > sq || x.k1 > sk) return BSFA_ERR_MASK;
+    }
+    return BSFA_OK;
+}
+
+bsfa_status build_plan(const bsfa_slice *slices, int32_t n_slices, int32_t sq, int32_t sk,
+                       int32_t hq, int32_t hkv, int32_t d, int32_t bq, int32_t bk, bsfa_plan **out)
+{
+    if (!out) return BSFA_ERR_ARG;
+    *out = nullptr;
+    if (n_slices < 0 || (n_slices > 0 && !slices)) return BSFA_ERR_ARG;
+    if (sq < 0 || sk < 0 || hq <= 0 || hkv <= 0 || d <= 0 || bq <= 0 || bk <= 0) return BSFA_ERR_ARG;
+    if (sq >= (1 << 30) || sk >= (1 << 30)) return BSFA_ERR_ARG;
+    if (hq % hkv != 0) return BSFA_ERR_SHAPE;
+    if ((int64_t)hq * ((sq + bq - 1) / bq) >= (int64_t)1 << 31) return BSFA_ERR_ARG;
+    bsfa_status st = check_slices(slices, n_slices, sq, sk);
+    if (st != BSFA_OK) return st;
+    bsfa_plan *p = new (std::nothrow) bsfa_plan;
+    if (!p) return BSFA_ERR_OOM;
+    p->sq = sq;
+    p->sk = sk;
+    p->hq = hq;
+    p->hkv = hkv;
+    p->d = d;
+    p->bq = bq;
+    p->bk = bk;
+    st = compile_mask(slices, n_slices, *p);
+    if (st == BSFA_OK) {
+        try {
+            build_schedule(*p, kNumCu * kBinsPerCu);
+        } catch (const std::bad_alloc &) {
+            st = BSFA_ERR_OOM;
+        }
+    }
+    if (st != BSFA_OK) {
+        delete p;
+        return st;
+    }
+    *out = p;
+    return BSFA_OK;
+}
+
+template <class T>
+size_t place(size_t &off, size_t count)
+{
+    off = (off + 255) & ~size_t(255);
+    const size_t at = off;
+    off += count * sizeof(T);
+    return at;
+}
+
+}  // namespace
+
+extern "C" {
+
+bsfa_status bsfa_plan_create(const bsfa_slice *slices, int32_t n_slices, int32_t sq, int32_t sk,
+                             int32_t hq, int32_t hkv, int32_t d, int32_t bq, int32_t bk,
+                             bsfa_plan **out)
+{
+    return build_plan(slices, n_slices, sq, sk, hq, hkv, d, bq, bk, out);
+}
+
+bsfa_status bsfa_plan_from_varlen(const int32_t *cu_seqlens, int32_t n_docs, int32_t causal,
+                                  int32_t hq, int32_t hkv, int32_t d, int32_t bq, int32_t bk,
+                                  bsfa_plan **out)
+{
+    if (!out) return BSFA_ERR_ARG;
+    *out = nullptr;
+    if (!cu_seqlens || n_docs < 0) return BSFA_ERR_ARG;
+    if (cu_seqlens[0] != 0) return BSFA_ERR_MASK;
+    std::vector<bsfa_slice> sl;
+    try {
+        sl.reserve((size_t)n_docs);
+        for (int32_t t = 0; t < n_docs; ++t) {
+            const int32_t a = cu_seqlens[t], b = cu_seqlens[t + 1];
+            if (b < a) return BSFA_ERR_MASK;
+            if (b > a) sl.push_back({a, b, a, b, causal ? BSFA_CAUSAL : BSFA_FULL});
+        }
+    } catch (const std::bad_alloc &) {
+        return BSFA_ERR_OOM;
+    }
+    const int32_t total = cu_seqlens[n_docs];
+    return build_plan(sl.data(), (int32_t)sl.size(), total, total, hq, hkv, d, bq, bk, out);
+}
+
+bsfa_status bsfa_plan_from_blocks(const uint8_t *codes, int32_t nbq, int32_t nbk,
+                                  int32_t block_q, int32_t block_k, int32_t sq, int32_t sk,
+                                  int32_t hq, int32_t hkv, int32_t d, int32_t bq, int32_t bk,
+                                  bsfa_plan **out)
+{
+    if (!out) return BSFA_ERR_ARG;
+    *out = nullptr;
+    if (nbq < 0 || nbk < 0 || block_q <= 0 || block_k <= 0 || sq < 0 || sk < 0) return BSFA_ERR_ARG;
+    if ((int64_t)nbq * nbk > 0 && !codes) return BSFA_ERR_ARG;
+    std::vector<bsfa_slice> sl;
+    try {
+        for (int64_t i = 0; i < nbq; ++i)
+            for (int64_t j = 0; j < nbk; ++j) {
+                const uint8_t c = codes[i * nbk + j];
+                if (c == 0) continue;
+                if (c > 2) return BSFA_ERR_MASK;
+                const int64_t q0 = i * block_q, k0 = j * block_k;
+                const int64_t q1 = std::min<int64_t>(q0 + block_q, sq), k1 = std::min<int64_t>(k0 + block_k, sk);
+                if (q0 >= sq || k0 >= sk) continue;
+                sl.push_back({(int32_t)q0, (int32_t)q1, (int32_t)k0, (int32_t)k1,
+                              c == 1 ? BSFA_FULL : BSFA_CAUSAL});
+            }
+    } catch (const std::bad_alloc &) {
+        return BSFA_ERR_OOM;
+    }
+    return build_plan(sl.data(), (int32_t)sl.size(), sq, sk, hq, hkv, d, bq, bk, out);
+}
+
+bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
+{
+    if (!p) return BSFA_ERR_ARG;
+    if (p->dbuf) return BSFA_ERR_STATE;
+    hipStream_t s = (hipStream_t)stream;
+    // one image: row_ptr | entries | pieces | bin_ptr | bin_items
+    size_t off = 0;
+    const size_t nnz = p->col.size();
+    const size_t o_row = place<int32_t>(off, p->row_ptr.size());
+    const size_t o_ent = place<Entry>(off, nnz);
+    const size_t o_pc = place<Piece>(off, p->pieces.size());
+    const size_t o_bp = place<int32_t>(off, p->bin_ptr.size());
+    const size_t o_bi = place<int32_t>(off, p->bin_items.size());
+    const size_t bytes = (off + 255) & ~size_t(255);
+    try {
+        p->staging.assign(bytes, 0);
+    } catch (const std::bad_alloc &) {
+        return BSFA_ERR_OOM;
+    }
+    uint8_t *h = p->staging.data();
+    std::memcpy(h + o_row, p->row_ptr.data(), p->row_ptr.size() * sizeof(int32_t));
+    Entry *ent = (Entry *)(h + o_ent);
+    for (size_t e = 0; e < nnz; ++e)
+        ent[e] = Entry{p->col[e], p->piece_ptr[e], p->piece_ptr[e + 1] - p->piece_ptr[e], p->tag[e]};
+    if (!p->pieces.empty()) std::memcpy(h + o_pc, p->pieces.data(), p->pieces.size() * sizeof(Piece));
+    std::memcpy(h + o_bp, p->bin_ptr.data(), p->bin_ptr.size() * sizeof(int32_t));
+    if (!p->bin_items.empty())
+        std::memcpy(h + o_bi, p->bin_items.data(), p->bin_items.size() * sizeof(int32_t));
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BSFA_ERR_HIP;
+    int pools = 0;
+    (void)hipDeviceGetAttribute(&pools, hipDeviceAttributeMemoryPoolsSupported, dev);
+    void *d = nullptr;
+    hipError_t err;
+    if (pools) {
+        err = hipMallocAsync(&d, bytes, s);
+        p->dbuf_async = true;
+    } else {
+        err = hipMalloc(&d, bytes);
+        p->dbuf_async = false;
+    }
+    if (err == hipErrorOutOfMemory) return BSFA_ERR_OOM;
+    if (err != hipSuccess) return BSFA_ERR_HIP;
+    if (hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipEventCreateWithFlags(&p->copied, hipEventDisableTiming) != hipSuccess ||
+        hipEventRecord(p->copied, s) != hipSuccess) {
+        if (p->dbuf_async) (void)hipFreeAsync(d, s); else (void)hipFree(d);
+        return BSFA_ERR_HIP;
+    }
+    uint8_t *base = (uint8_t *)d;
+    p->dev.row_ptr = (const int32_t *)(base + o_row);
+    p->dev.entries = (const Entry *)(base + o_ent);
+    p->dev.pieces = (const Piece *)(base + o_pc);
+    p->dev.bin_ptr = (const int32_t *)(base + o_bp);
+    p->dev.bin_items = (const int32_t *)(base + o_bi);
+    p->dbuf = d;
+    p->device = dev;
+    p->ustream = s;
+    return BSFA_OK;
+}
+
+void bsfa_plan_destroy(bsfa_plan *p)
+{
+    if (!p) return;
+    if (p->copied) {
+        (void)hipEventSynchronize(p->copied);  // the staging image must outlive its copy
+        (void)hipEventDestroy(p->copied);
+    }
+    if (p->dbuf) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        if (cur != p->device) (void)hipSetDevice(p->device);
+        if (p->dbuf_async) (void)hipFreeAsync(p->dbuf, p->ustream);
+        else (void)hipFree(p->dbuf);
+        if (cur != p->device) (void)hipSetDevice(cur);
+    }
+    delete p;
+}
+
+bsfa_status bsfa_plan_get_info(const bsfa_plan *p, bsfa_plan_info *info)
+{
+    if (!p || !info) return BSFA_ERR_ARG;
+    info->sq = p->sq;
+    info->sk = p->sk;
+    info->hq = p->hq;
+    info->hkv = p->hkv;
+    info->d = p->d;
+    info->bq = p->bq;
+    info->bk = p->bk;
+    info->n_qtiles = p->n_qt;
+    info->n_ktiles = p->n_kt;
+    info->nnz = (int64_t)p->col.size();
+    info->n_full = p->n_full;
+    info->n_partial = p->n_partial;
+    info->n_pieces = (int64_t)p->pieces.size();
+    info->pairs = p->pairs;
+    info->n_items = (int32_t)p->item_cost.size();
+    info->n_bins = (int32_t)p->bin_ptr.size() - 1;
+    info->makespan = p->makespan;
+    info->total_cost = p->total_cost;
+    info->uploaded = p->dbuf ? 1 : 0;
+    return BSFA_OK;
+}
+
+bsfa_status bsfa_plan_export_csr(const bsfa_plan *p, int32_t *row_ptr, int32_t *col, uint8_t *tag,
+                                 int64_t cap, int64_t *nnz)
+{
+    if (!p || !nnz) return BSFA_ERR_ARG;
+    *nnz = (int64_t)p->col.size();
+    if (cap < *nnz) return BSFA_ERR_ARG;
+    if (!row_ptr || (*nnz > 0 && (!col || !tag))) return BSFA_ERR_ARG;
+    std::memcpy(row_ptr, p->row_ptr.data(), p->row_ptr.size() * sizeof(int32_t));
+    if (*nnz > 0) {
+        std::memcpy(col, p->col.data(), p->col.size() * sizeof(int32_t));
+        std::memcpy(tag, p->tag.data(), p->tag.size());
+    }
+    return BSFA_OK;
+}
+
+bsfa_status bsfa_plan_export_schedule(const bsfa_plan *p, int32_t *bin_ptr, int32_t *items,
+                                      float *item_cost)
+{
+    if (!p) return BSFA_ERR_ARG;
+    if (bin_ptr) std::memcpy(bin_ptr, p->bin_ptr.data(), p->bin_ptr.size() * sizeof(int32_t));
+    if (items && !p->bin_items.empty())
+        std::memcpy(items, p->bin_items.data(), p->bin_items.size() * sizeof(int32_t));
+    if (item_cost && !p->item_cost.empty())
+        std::memcpy(item_cost, p->item_cost.data(), p->item_cost.size() * sizeof(float));
+    return BSFA_OK;
+}
+
+bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
+                          const bsfa_plan *p, float scale, bsfa_tensor *o, float *lse,
+                          int64_t lse_stride_head, void *stream)
+{
+    if (!q || !k || !v || !p || !o || !lse) return BSFA_ERR_ARG;
+    if (!(scale > 0.f) || !std::isfinite(scale)) return BSFA_ERR_ARG;
+    if (p->d != 64 && p->d != 128) return BSFA_ERR_UNSUPPORTED;
+    if (p->bq != kKernelBq || p->bk % kKernelBk != 0) return BSFA_ERR_UNSUPPORTED;
+    if (!p->dbuf) return BSFA_ERR_STATE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BSFA_ERR_HIP;
+    if (dev != p->device) return BSFA_ERR_STATE;
+    if (lse_stride_head < p->sq) return BSFA_ERR_ARG;
+    const bool need_q = p->sq > 0, need_k = p->sk > 0;
+    if ((need_q && (!q->ptr || !o->ptr)) || (need_k && (!k->ptr || !v->ptr))) return BSFA_ERR_ARG;
+    for (const bsfa_tensor *t : {q, k, v, (const bsfa_tensor *)o}) {
+        if (t->ptr && !aligned16(t->ptr)) return BSFA_ERR_ALIGN;
+        if (!stride_ok(t->stride_tok) || !stride_ok(t->stride_head)) return BSFA_ERR_ALIGN;
+    }
+    FwdArgs a{};
+    a.q = q->ptr;
+    a.k = k->ptr;
+    a.v = v->ptr;
+    a.o = o->ptr;
+    a.lse = lse;
+    a.q_st = q->stride_tok;
+    a.q_sh = q->stride_head;
+    a.k_st = k->stride_tok;
+    a.k_sh = k->stride_head;
+    a.v_st = v->stride_tok;
+    a.v_sh = v->stride_head;
+    a.o_st = o->stride_tok;
+    a.o_sh = o->stride_head;
+    a.lse_sh = lse_stride_head;
+    a.sq = p->sq;
+    a.sk = p->sk;
+    a.hq = p->hq;
+    a.hkv = p->hkv;
+    a.n_qt = p->n_qt;
+    a.bk_plan = p->bk;
+    a.c = scale * 1.4426950408889634f;
+    a.meta = p->dev;
+    a.n_bins = (int32_t)p->bin_ptr.size() - 1;
+    if (p->sq == 0) return BSFA_OK;
+    if (launch_attn_fwd(a, p->d, (hipStream_t)stream) != hipSuccess) return BSFA_ERR_HIP;
+    return BSFA_OK;
+}
+
+bsfa_status bsfa_attn_merge(const void *const *o_parts, const float *const *lse_parts, int32_t n,
+                            int64_t part_stride_tok, int64_t part_stride_head,
+                            int64_t lse_stride_head, int32_t n_tok, int32_t n_head, int32_t d,
+                            bsfa_tensor *o, float *lse, void *stream)
+{
+    if (!o_parts || !lse_parts || !o || !lse) return BSFA_ERR_ARG;
+    if (n < 1 || n > BSFA_MERGE_MAX_PARTS || n_tok < 0 || n_head < 0 || n_head > 65535)
+        return BSFA_ERR_ARG;
+    if (d != 64 && d != 128) return BSFA_ERR_UNSUPPORTED;
+    if (lse_stride_head < n_tok) return BSFA_ERR_ARG;
+    if (!stride_ok(part_stride_tok) || !stride_ok(part_stride_head) || !stride_ok(o->stride_tok) ||
+        !stride_ok(o->stride_head))
+        return BSFA_ERR_ALIGN;
+    if (!o->ptr) return BSFA_ERR_ARG;
+    if (!aligned16(o->ptr)) return BSFA_ERR_ALIGN;
+    MergeArgs a{};
+    for (int32_t t = 0; t < n; ++t) {
+        if (!o_parts[t] || !lse_parts[t]) return BSFA_ERR_ARG;
+        if (!aligned16(o_parts[t]) || ((uintptr_t)lse_parts[t] & 3u)) return BSFA_ERR_ALIGN;
+        a.o_parts[t] = o_parts[t];
+        a.lse_parts[t] = lse_parts[t];
+    }
+    a.n = n;
+    a.p_st = part_stride_tok;
+    a.p_sh = part_stride_head;
+    a.lse_sh = lse_stride_head;
+    a.n_tok = n_tok;
+    a.n_head = n_head;
+    a.o = o->ptr;
+    a.lse = lse;
+    a.o_st = o->stride_tok;
+    a.o_sh = o->stride_head;
+    if (launch_attn_merge(a, d, (hipStream_t)stream) != hipSuccess) return BSFA_ERR_HIP;
+    return BSFA_OK;
+}
+
+const char *bsfa_status_str(bsfa_status s)
+{
+    switch (s) {
+    case BSFA_OK: return "ok";
+    case BSFA_ERR_ARG: return "invalid argument";
+    case BSFA_ERR_SHAPE: return "shape mismatch";
+    case BSFA_ERR_ALIGN: return "misaligned pointer or stride";
+    case BSFA_ERR_UNSUPPORTED: return "unsupported head dim or tile size";
+    case BSFA_ERR_MASK: return "invalid mask";
+    case BSFA_ERR_OOM: return "out of memory";
+    case BSFA_ERR_HIP: return "HIP runtime error";
+    case BSFA_ERR_STATE: return "plan not uploaded to the current device";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"
+

@@ -1,0 +1,161 @@
+// Mask compiler: a list of slices -> the CSR of non-empty (bq x bk) tiles per
+// query tile, each tagged full or partial, with the clipped slice pieces of every
+// partial tile.
+//
+// Follows the MagiAttention v1.1.0 news ("Blackwell adaptation" list: generate the
+// block-sparse structure without instantiating a dense mask, keep mask metadata
+// CSR-compressed) and the UltraAttn blog, 3 (a block is Full when every position
+// is valid, Causal when some are, Empty when none are) and 3.3 (Empty blocks are
+// skipped).  The work is geometric: each slice visits only the tiles its
+// rectangle and diagonal reach, so the cost is O(sum of tiles touched), never
+// O(Sq * Sk).  A tile no single slice covers is still full when the union of its
+// pieces covers it; that case is settled by counting the union row by row over
+// the tile's pieces.
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+#include "bsfa_internal.h"
+
+namespace bsfa {
+namespace {
+
+struct Touch {
+    int32_t qt, kt, slice;
+    int32_t covers;  // 1 when this slice alone admits every in-range pair of the tile
+};
+
+// Largest admitted key + 1 for row i of a piece/slice with the given bounds.
+inline int64_t row_hi(int64_t i, int64_t k_hi, int64_t diag)
+{
+    const int64_t lim = i + diag + 1;
+    return lim < k_hi ? lim : k_hi;
+}
+
+// Admitted pairs of the union of pieces inside rows [r0, r1) x keys [c0, c1).
+int64_t union_count(const std::vector<Piece> &pc, int64_t r0, int64_t r1, int64_t c0, int64_t c1,
+                    std::vector<std::pair<int64_t, int64_t>> &ivs)
+{
+    int64_t total = 0;
+    for (int64_t i = r0; i < r1; ++i) {
+        ivs.clear();
+        for (const Piece &p : pc) {
+            if (i < p.q_lo || i >= p.q_hi) continue;
+            int64_t lo = std::max<int64_t>(p.k_lo, c0);
+            int64_t hi = std::min<int64_t>(row_hi(i, p.k_hi, p.diag), c1);
+            if (lo < hi) ivs.emplace_back(lo, hi);
+        }
+        std::sort(ivs.begin(), ivs.end());
+        int64_t cur_lo = -1, cur_hi = -1;
+        for (auto &iv : ivs) {
+            if (iv.first > cur_hi) {
+                total += cur_hi - cur_lo;
+                cur_lo = iv.first;
+                cur_hi = iv.second;
+            } else if (iv.second > cur_hi) {
+                cur_hi = iv.second;
+            }
+        }
+        total += cur_hi - cur_lo;
+    }
+    return total;
+}
+
+}  // namespace
+
+bsfa_status compile_mask(const bsfa_slice *slices, int32_t n_slices, bsfa_plan &p)
+{
+    const int64_t bq = p.bq, bk = p.bk, sq = p.sq, sk = p.sk;
+    p.n_qt = (int32_t)((sq + bq - 1) / bq);
+    p.n_kt = (int32_t)((sk + bk - 1) / bk);
+    try {
+        // 1. every (tile, slice) incidence with at least one admitted pair
+        std::vector<Touch> touches;
+        for (int32_t s = 0; s < n_slices; ++s) {
+            const bsfa_slice &sl = slices[s];
+            if (sl.q0 >= sl.q1 || sl.k0 >= sl.k1) continue;
+            const int64_t diag = sl.type == BSFA_CAUSAL ? (int64_t)sl.k1 - sl.q1 : kDiagFull;
+            for (int64_t qt = sl.q0 / bq; qt * bq < sl.q1; ++qt) {
+                const int64_t r0 = qt * bq, r1 = std::min(r0 + bq, sq);
+                const int64_t a = std::max<int64_t>(sl.q0, r0), b = std::min<int64_t>(sl.q1, r1);
+                const int64_t j_lo = sl.k0, j_hi = row_hi(b - 1, sl.k1, diag);
+                if (j_lo >= j_hi) continue;
+                const bool rows_all = a == r0 && b == r1;
+                for (int64_t kt = j_lo / bk; kt * bk < j_hi; ++kt) {
+                    const int64_t c0 = kt * bk, c1 = std::min(c0 + bk, sk);
+                    const bool covers = rows_all && sl.k0 <= c0 && sl.k1 >= c1 &&
+                                        (c1 - 1) <= r0 + diag;
+                    touches.push_back({(int32_t)qt, (int32_t)kt, s, covers ? 1 : 0});
+                }
+            }
+        }
+        std::sort(touches.begin(), touches.end(), [](const Touch &x, const Touch &y) {
+            if (x.qt != y.qt) return x.qt < y.qt;
+            if (x.kt != y.kt) return x.kt < y.kt;
+            return x.slice < y.slice;
+        });
+
+        // 2. one CSR entry per distinct tile
+        p.row_ptr.assign((size_t)p.n_qt + 1, 0);
+        p.col.clear();
+        p.tag.clear();
+        p.piece_ptr.assign(1, 0);
+        p.pieces.clear();
+        p.n_full = p.n_partial = p.pairs = 0;
+        std::vector<Piece> cand;
+        std::vector<std::pair<int64_t, int64_t>> ivs;
+        size_t t = 0;
+        while (t < touches.size()) {
+            size_t u = t;
+            bool covered = false;
+            while (u < touches.size() && touches[u].qt == touches[t].qt &&
+                   touches[u].kt == touches[t].kt) {
+                covered |= touches[u].covers != 0;
+                ++u;
+            }
+            const int64_t qt = touches[t].qt, kt = touches[t].kt;
+            const int64_t r0 = qt * bq, r1 = std::min(r0 + bq, sq);
+            const int64_t c0 = kt * bk, c1 = std::min(c0 + bk, sk);
+            const int64_t area = (r1 - r0) * (c1 - c0);
+            bool full = covered;
+            int64_t count = area;
+            if (!covered) {
+                cand.clear();
+                for (size_t x = t; x < u; ++x) {
+                    const bsfa_slice &sl = slices[touches[x].slice];
+                    Piece pc;
+                    pc.q_lo = std::max<int32_t>(sl.q0, (int32_t)r0);
+                    pc.q_hi = std::min<int32_t>(sl.q1, (int32_t)r1);
+                    pc.k_lo = std::max<int32_t>(sl.k0, (int32_t)c0);
+                    pc.k_hi = std::min<int32_t>(sl.k1, (int32_t)c1);
+                    pc.diag = sl.type == BSFA_CAUSAL ? sl.k1 - sl.q1 : kDiagFull;
+                    pc.pad0 = pc.pad1 = pc.pad2 = 0;
+                    cand.push_back(pc);
+                }
+                count = union_count(cand, r0, r1, c0, c1, ivs);
+                full = count == area;
+            }
+            p.col.push_back((int32_t)kt);
+            if (full) {
+                p.tag.push_back(BSFA_TILE_FULL);
+                ++p.n_full;
+            } else {
+                p.tag.push_back(BSFA_TILE_PARTIAL);
+                ++p.n_partial;
+                p.pieces.insert(p.pieces.end(), cand.begin(), cand.end());
+            }
+            p.piece_ptr.push_back((int32_t)p.pieces.size());
+            p.pairs += count;
+            p.row_ptr[(size_t)qt + 1] = (int32_t)p.col.size();
+            t = u;
+        }
+        // rows with no entry inherit the running count
+        for (int32_t qt = 0; qt < p.n_qt; ++qt)
+            if (p.row_ptr[(size_t)qt + 1] < p.row_ptr[qt]) p.row_ptr[(size_t)qt + 1] = p.row_ptr[qt];
+    } catch (const std::bad_alloc &) {
+        return BSFA_ERR_OOM;
+    }
+    return BSFA_OK;
+}
+
+}  // namespace bsfa

@@ -1,0 +1,172 @@
+// Work items, their cost and the min-heap greedy (longest processing time first)
+// assignment of items to the persistent workgroups of the forward kernel.
+//
+// Follows the MagiAttention v1.1.0 news ("system-level co-optimisation": a
+// Dispatch Solver built on a min-heap greedy keeps every unit's load balanced
+// under any mask so that no straggler sets the pace) and the UltraAttn blog, 4.1
+// (block weights: full 1, causal about half a full block, empty 0, adjustable from
+// profiling; imbalance bound ceil(avg)/avg - 1).  Here the units are workgroup
+// slots on the GPU's compute units instead of devices, and the weights are
+// calibrated to this forward kernel, which runs a partial tile at the cost of a
+// full one plus its per-element mask.
+//
+// Item = (query head h, query tile qt); id = h * n_qt + qt.  Items of one key/value
+// head share K/V tiles, so they are kept on one accelerator die (XCD) when that
+// costs little balance: MI355X hands workgroups to its 8 XCDs round-robin, so bin
+// b runs on XCD b % 8, and each XCD has its own L2.
+#include <algorithm>
+#include <cmath>
+#include <queue>
+#include <utility>
+
+#include "bsfa_internal.h"
+
+namespace bsfa {
+
+// LPT onto the given bins: heaviest item first (ties by id), each to the least
+// loaded bin (ties by bin id).  Appends to per-bin lists and loads.
+void lpt(const std::vector<int32_t> &items, const std::vector<float> &cost,
+         const std::vector<int32_t> &bins, std::vector<std::vector<int32_t>> &lists,
+         std::vector<double> &load)
+{
+    std::vector<int32_t> order(items);
+    std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+        if (cost[a] != cost[b]) return cost[a] > cost[b];
+        return a < b;
+    });
+    using Key = std::pair<double, int32_t>;
+    std::priority_queue<Key, std::vector<Key>, std::greater<Key>> heap;
+    for (int32_t b : bins) heap.push({load[b], b});
+    for (int32_t it : order) {
+        Key k = heap.top();
+        heap.pop();
+        lists[k.second].push_back(it);
+        load[k.second] = k.first + cost[it];
+        heap.push({load[k.second], k.second});
+    }
+}
+
+void build_schedule(bsfa_plan &p, int n_bins_max)
+{
+    const int32_t n_items = p.hq * p.n_qt;
+    p.item_cost.assign((size_t)n_items, 0.f);
+    // cost of one query tile row (same for every head): inner 64-key steps weighted by tag
+    std::vector<double> row_cost((size_t)p.n_qt, 0.0);
+    for (int32_t qt = 0; qt < p.n_qt; ++qt) {
+        double c = kCostItem;
+        for (int32_t e = p.row_ptr[qt]; e < p.row_ptr[(size_t)qt + 1]; ++e) {
+            const int64_t c0 = (int64_t)p.col[e] * p.bk;
+            const int64_t keys = std::min<int64_t>(c0 + p.bk, p.sk) - c0;
+            const double steps = (double)((keys + kKernelBk - 1) / kKernelBk);
+            c += steps * bsfa_tile_cost(p.tag[e], kCostPartial);
+        }
+        row_cost[qt] = c;
+    }
+    double total = 0.0;
+    for (int32_t h = 0; h < p.hq; ++h)
+        for (int32_t qt = 0; qt < p.n_qt; ++qt) {
+            p.item_cost[(size_t)h * p.n_qt + qt] = (float)row_cost[qt];
+            total += row_cost[qt];
+        }
+    p.total_cost = total;
+
+    const int32_t n_bins = std::max(1, std::min(n_items, n_bins_max));
+    std::vector<std::vector<int32_t>> lists((size_t)n_bins);
+    std::vector<double> load((size_t)n_bins, 0.0);
+
+    bool placed = false;
+    const int32_t group = p.hq / p.hkv;  // query heads per key/value head
+    if (n_bins % kNumXcd == 0 && p.hkv >= kNumXcd) {
+        // level 1: key/value heads onto XCDs (LPT on head totals)
+        std::vector<double> head_cost((size_t)p.hkv, 0.0);
+        for (int32_t g = 0; g < p.hkv; ++g)
+            for (int32_t h = g * group; h < (g + 1) * group; ++h)
+                for (int32_t qt = 0; qt < p.n_qt; ++qt) head_cost[g] += row_cost[qt];
+        std::vector<int32_t> gorder((size_t)p.hkv);
+        for (int32_t g = 0; g < p.hkv; ++g) gorder[g] = g;
+        std::sort(gorder.begin(), gorder.end(), [&](int32_t a, int32_t b) {
+            if (head_cost[a] != head_cost[b]) return head_cost[a] > head_cost[b];
+            return a < b;
+        });
+        std::vector<double> xload(kNumXcd, 0.0);
+        std::vector<std::vector<int32_t>> xheads(kNumXcd);
+        for (int32_t g : gorder) {
+            int32_t best = 0;
+            for (int32_t x = 1; x < kNumXcd; ++x)
+                if (xload[x] < xload[best]) best = x;
+            xheads[best].push_back(g);
+            xload[best] += head_cost[g];
+        }
+        const double xmax = *std::max_element(xload.begin(), xload.end());
+        const double xavg = total / kNumXcd;
+        if (xavg > 0 && xmax / xavg - 1.0 <= 0.03) {
+            // level 2: within each XCD, LPT over the bins that XCD runs
+            for (int32_t x = 0; x < kNumXcd; ++x) {
+                std::vector<int32_t> items, bins;
+                for (int32_t g : xheads[x])
+                    for (int32_t h = g * group; h < (g + 1) * group; ++h)
+                        for (int32_t qt = 0; qt < p.n_qt; ++qt) items.push_back(h * p.n_qt + qt);
+                for (int32_t b = x; b < n_bins; b += kNumXcd) bins.push_back(b);
+                lpt(items, p.item_cost, bins, lists, load);
+            }
+            placed = true;
+        }
+    }
+    if (!placed) {
+        std::vector<int32_t> items((size_t)n_items), bins((size_t)n_bins);
+        for (int32_t i = 0; i < n_items; ++i) items[i] = i;
+        for (int32_t b = 0; b < n_bins; ++b) bins[b] = b;
+        lpt(items, p.item_cost, bins, lists, load);
+    }
+
+    p.bin_ptr.assign((size_t)n_bins + 1, 0);
+    p.bin_items.clear();
+    p.makespan = 0.0;
+    for (int32_t b = 0; b < n_bins; ++b) {
+        p.bin_items.insert(p.bin_items.end(), lists[b].begin(), lists[b].end());
+        p.bin_ptr[(size_t)b + 1] = (int32_t)p.bin_items.size();
+        p.makespan = std::max(p.makespan, load[b]);
+    }
+}
+
+}  // namespace bsfa
+
+extern "C" double bsfa_tile_cost(int32_t tag, double w_partial)
+{
+    if (tag == BSFA_TILE_FULL) return 1.0;
+    if (tag == BSFA_TILE_PARTIAL) return w_partial;
+    return 0.0;
+}
+
+extern "C" double bsfa_lpt_assign(const float *cost, int32_t n_items, int32_t n_bins,
+                                  int32_t *bin_of, double *bin_load)
+{
+    if (n_items < 0 || n_bins < 1 || (n_items > 0 && (!cost || !bin_of))) return -1.0;
+    for (int32_t i = 0; i < n_items; ++i)
+        if (!(cost[i] >= 0.f) || !std::isfinite(cost[i])) return -1.0;
+    try {
+        std::vector<float> c(cost, cost + n_items);
+        std::vector<int32_t> items((size_t)n_items), bins((size_t)n_bins);
+        for (int32_t i = 0; i < n_items; ++i) items[i] = i;
+        for (int32_t b = 0; b < n_bins; ++b) bins[b] = b;
+        std::vector<std::vector<int32_t>> lists((size_t)n_bins);
+        std::vector<double> load((size_t)n_bins, 0.0);
+        bsfa::lpt(items, c, bins, lists, load);
+        double mk = 0.0;
+        for (int32_t b = 0; b < n_bins; ++b) {
+            for (int32_t it : lists[b]) bin_of[it] = b;
+            if (bin_load) bin_load[b] = load[b];
+            mk = std::max(mk, load[b]);
+        }
+        return mk;
+    } catch (...) {
+        return -1.0;
+    }
+}
+
+extern "C" double bsfa_imbalance_bound(double total_cost, int32_t n_bins)
+{
+    if (n_bins <= 0 || total_cost <= 0.0) return 0.0;
+    const double avg = total_cost / n_bins;
+    return std::ceil(avg) / avg - 1.0;
+}

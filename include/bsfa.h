@@ -1,0 +1,197 @@
+/*
+ * bsfa.h -- C ABI of libbsfa.so: masked flash-attention forward over a tile CSR
+ * and the merge of KV-split partials, for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (titles as published):
+ *   [MA] "Sand.ai releases MagiAttention v1.1.0" (news), list "Blackwell adaptation":
+ *        flexible masks, block-sparse mask generation without a dense mask,
+ *        CSR-compressed mask metadata, cheap kernel launches; list "system-level
+ *        co-optimisation": Dispatch Solver, a min-heap greedy balancer.
+ *   [UA] "UltraAttn: hierarchical context tiling" (blog), 3 (Full / Causal / Empty
+ *        blocks), 3.1 (Q split), 3.2 (KV split and the mergeable summary),
+ *        3.3 (2-D block view), 4.1 (block weights 1 / 0.5 / 0 and the imbalance
+ *        bound), 8 (strided block-sparse pattern).
+ *   [F4] QbitAI article on FlashAttention-4, "three techniques" part
+ *        (conditional softmax rescaling; softmax overlapped with matrix products).
+ *   [FT] "FlashAttention-T: tensor-vector parallel optimisation" (blog),
+ *        FlashAttention lineage (tiling + incremental softmax), double-buffered
+ *        on-chip staging, numerical-stability parameters.
+ *
+ * Conventions for every call:
+ *   - Status codes only; nothing throws across this boundary.  Arguments are
+ *     validated before any device work is enqueued; a rejected call writes nothing.
+ *   - Device pointers are HIP device memory owned by the caller.  "stream" is a
+ *     hipStream_t passed as void* (NULL = the default stream).  Device work is
+ *     enqueued on that stream and the call returns without synchronising.
+ *   - Tensors are bf16 with the head dimension contiguous; token and head strides
+ *     are given in elements, must be multiples of 8, and base pointers must be
+ *     16-byte aligned.
+ */
+#ifndef BSFA_H
+#define BSFA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BSFA_OK = 0,
+    BSFA_ERR_ARG = 1,         /* null pointer, bad count, value out of range */
+    BSFA_ERR_SHAPE = 2,       /* shapes disagree with the plan, Hq % Hkv != 0, ... */
+    BSFA_ERR_ALIGN = 3,       /* base pointer not 16-byte aligned or stride not a multiple of 8 */
+    BSFA_ERR_UNSUPPORTED = 4, /* head dim / tile size the kernels do not implement */
+    BSFA_ERR_MASK = 5,        /* slice outside [0, S), q1 < q0, k1 < k0, unknown type or code */
+    BSFA_ERR_OOM = 6,         /* host or device allocation failed */
+    BSFA_ERR_HIP = 7,         /* a HIP runtime call failed (including a sticky earlier fault) */
+    BSFA_ERR_STATE = 8        /* plan not uploaded to the current device */
+} bsfa_status;
+
+/* One mask slice ([MA] flexible masks; [UA] 3): the pairs (i, j) with q0 <= i < q1 and
+ * k0 <= j < k1; type BSFA_FULL admits all of them, BSFA_CAUSAL only those with
+ * j - k1 <= i - q1 (causal aligned at the slice's bottom-right corner, which is
+ * plain j <= i when k1 == q1).  A mask is the union of its slices' pair sets. */
+typedef struct {
+    int32_t q0, q1, k0, k1, type;
+} bsfa_slice;
+
+enum { BSFA_FULL = 0, BSFA_CAUSAL = 1 };
+enum { BSFA_TILE_FULL = 1, BSFA_TILE_PARTIAL = 2 };
+
+/* A bf16 [tokens, heads, head_dim] tensor view: element (t, h, e) lives at
+ * ptr + t * stride_tok + h * stride_head + e  (strides in elements). */
+typedef struct {
+    void *ptr;
+    int64_t stride_tok;
+    int64_t stride_head;
+} bsfa_tensor;
+
+typedef struct bsfa_plan bsfa_plan;
+
+typedef struct {
+    int32_t sq, sk, hq, hkv, d, bq, bk;
+    int32_t n_qtiles, n_ktiles;
+    int64_t nnz;          /* non-empty (bq x bk) tiles in the CSR */
+    int64_t n_full;       /* tiles tagged BSFA_TILE_FULL */
+    int64_t n_partial;    /* tiles tagged BSFA_TILE_PARTIAL */
+    int64_t n_pieces;     /* clipped slice pieces stored for partial tiles */
+    int64_t pairs;        /* admitted (query, key) pairs of one head */
+    int32_t n_items;      /* work items = (query head, query tile) */
+    int32_t n_bins;       /* persistent workgroups of the forward launch */
+    double makespan;      /* largest bin cost of the schedule (cost units) */
+    double total_cost;    /* sum of item costs */
+    int32_t uploaded;     /* 1 once bsfa_plan_upload has run */
+} bsfa_plan_info;
+
+/* ---- plans: mask compiler + scheduler (host) --------------------------------
+ * A plan is the compiled form of one mask for fixed shapes: a CSR of the non-empty
+ * (bq x bk) tiles of every query tile ([MA] CSR metadata; [UA] 3.3 skip Empty
+ * blocks), each tagged full or partial ([UA] 3 block classes), the slice pieces of
+ * each partial tile, and a schedule of (query head, query tile) items over the
+ * persistent workgroups built by a min-heap greedy on a tile-count cost ([MA]
+ * Dispatch Solver; [UA] 4.1 weights).  Creation is host-only and never touches
+ * the GPU.  The kernels need bq == 128 and bk a multiple of 64; other tile sizes
+ * build a plan whose CSR can be exported but which bsfa_attn_fwd rejects.
+ * A plan is immutable after creation; the caller frees it with bsfa_plan_destroy.
+ * Errors: BSFA_ERR_ARG (null out, n_slices < 0, bad sizes), BSFA_ERR_SHAPE
+ * (hq % hkv), BSFA_ERR_MASK (slice outside [0,sq) x [0,sk], q1 < q0, k1 < k0, unknown
+ * type), BSFA_ERR_OOM. */
+bsfa_status bsfa_plan_create(const bsfa_slice *slices, int32_t n_slices, int32_t sq, int32_t sk,
+                             int32_t hq, int32_t hkv, int32_t d, int32_t bq, int32_t bk,
+                             bsfa_plan **out);
+
+/* Packed variable-length documents ([MA] varlen masks): document t covers tokens
+ * [cu_seqlens[t], cu_seqlens[t+1]) on both axes, causal when causal != 0, full
+ * otherwise; no pair crosses documents.  cu_seqlens has n_docs + 1 nondecreasing
+ * host int32 entries starting at 0; the total length is cu_seqlens[n_docs]. */
+bsfa_status bsfa_plan_from_varlen(const int32_t *cu_seqlens, int32_t n_docs, int32_t causal,
+                                  int32_t hq, int32_t hkv, int32_t d, int32_t bq, int32_t bk,
+                                  bsfa_plan **out);
+
+/* Block pattern ([MA] block-sparse masks; [UA] 8 strided pattern): codes is a host
+ * uint8 [nbq, nbk] row-major map over (block_q x block_k) blocks, 0 = empty,
+ * 1 = full, 2 = causal inside the block; blocks are clipped to [0, sq) x [0, sk). */
+bsfa_status bsfa_plan_from_blocks(const uint8_t *codes, int32_t nbq, int32_t nbk,
+                                  int32_t block_q, int32_t block_k, int32_t sq, int32_t sk,
+                                  int32_t hq, int32_t hkv, int32_t d, int32_t bq, int32_t bk,
+                                  bsfa_plan **out);
+
+/* Copy the plan's metadata to the current HIP device, enqueued on stream.  The
+ * device buffer is allocated here (stream-ordered) and released by
+ * bsfa_plan_destroy on the same stream.  Must precede bsfa_attn_fwd.  Errors:
+ * BSFA_ERR_ARG, BSFA_ERR_STATE (already uploaded), BSFA_ERR_OOM, BSFA_ERR_HIP. */
+bsfa_status bsfa_plan_upload(bsfa_plan *plan, void *stream);
+
+/* Releases host memory and, if uploaded, the device buffer (stream-ordered on the
+ * upload stream: work already enqueued there that reads the plan stays valid;
+ * work on other streams must be complete).  NULL is accepted. */
+void bsfa_plan_destroy(bsfa_plan *plan);
+
+bsfa_status bsfa_plan_get_info(const bsfa_plan *plan, bsfa_plan_info *info);
+
+/* Copy out the tile CSR (for bit-exact checks): row_ptr [n_qtiles + 1], col [nnz]
+ * (ascending within a row), tag [nnz] (BSFA_TILE_FULL / BSFA_TILE_PARTIAL), all host
+ * memory.  cap is the capacity of col and tag; *nnz is always set.  Returns
+ * BSFA_ERR_ARG if cap < nnz (nothing but *nnz written). */
+bsfa_status bsfa_plan_export_csr(const bsfa_plan *plan, int32_t *row_ptr, int32_t *col,
+                                 uint8_t *tag, int64_t cap, int64_t *nnz);
+
+/* Copy out the schedule: bin_ptr [n_bins + 1], items [n_items] (item = h * n_qtiles
+ * + qtile, in execution order within a bin) and item_cost [n_items] (indexed by item
+ * id), host memory.  Any pointer may be NULL to skip it. */
+bsfa_status bsfa_plan_export_schedule(const bsfa_plan *plan, int32_t *bin_ptr, int32_t *items,
+                                      float *item_cost);
+
+/* Cost of one tile under the scheduler's model ([UA] 4.1: full = 1, causal/partial =
+ * w_partial, empty = 0) and the page's imbalance bound ceil(avg)/avg - 1 for a total
+ * cost split over n_bins units of integral capacity. */
+double bsfa_tile_cost(int32_t tag, double w_partial);
+double bsfa_imbalance_bound(double total_cost, int32_t n_bins);
+
+/* The scheduler's core, usable on any list of costs ([MA] Dispatch Solver, a
+ * min-heap greedy): items in order of decreasing cost (ties: lower index first) go
+ * one by one to the least-loaded bin (ties: lower bin index).  bin_of[n_items]
+ * receives each item's bin, bin_load[n_bins] (may be NULL) the final loads.
+ * Returns the makespan (largest load), or -1 on bad arguments (n_items < 0,
+ * n_bins < 1, null cost/bin_of with n_items > 0, a negative or non-finite cost). */
+double bsfa_lpt_assign(const float *cost, int32_t n_items, int32_t n_bins, int32_t *bin_of,
+                       double *bin_load);
+
+/* ---- forward ([FT] tiling + incremental softmax; [UA] 3.1-3.3; [F4]) --------
+ * O[i, h, :] = sum_j softmax_j(scale * q_i . k_j) v_j over the plan's admitted keys of
+ * row i, for every query row i < sq and query head h; LSE[h * lse_stride_head + i] =
+ * natural log-sum-exp of the scaled scores.  A row with no admitted key gets O = 0
+ * and LSE = -inf.  Query head h reads key/value head h / (hq / hkv).
+ * q, o: [sq, hq, d]; k, v: [sk, hkv, d]; lse: fp32, lse_stride_head >= sq.
+ * Shapes come from the plan, which must be uploaded to the current device.
+ * No allocation, no synchronisation; deterministic (no atomics).
+ * Errors: BSFA_ERR_ARG, BSFA_ERR_ALIGN, BSFA_ERR_UNSUPPORTED (d not 64/128, bq != 128,
+ * bk % 64 != 0), BSFA_ERR_STATE (plan not on this device), BSFA_ERR_HIP. */
+bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
+                          const bsfa_plan *plan, float scale, bsfa_tensor *o, float *lse,
+                          int64_t lse_stride_head, void *stream);
+
+/* ---- merge of KV-split partials ([UA] 3.2) -----------------------------------
+ * For n partial results (O_t, LSE_t) of the same queries over disjoint key sets:
+ *   M = max_t LSE_t, LSE = M + ln sum_t exp(LSE_t - M), O = sum_t exp(LSE_t - LSE) O_t;
+ * rows where every LSE_t is -inf get O = 0, LSE = -inf.
+ * o_parts / lse_parts: host arrays of n device pointers; every O_t is a bf16
+ * [n_tok, n_head, d] tensor with the strides of o_parts_view, every LSE_t an fp32
+ * [n_head, lse_stride_head] array.  o (bf16, strides from o->stride_*) and lse receive
+ * the result and must not overlap any partial.  1 <= n <= BSFA_MERGE_MAX_PARTS,
+ * d in {64, 128}.
+ * Errors: BSFA_ERR_ARG, BSFA_ERR_ALIGN, BSFA_ERR_UNSUPPORTED, BSFA_ERR_HIP. */
+enum { BSFA_MERGE_MAX_PARTS = 16 };
+bsfa_status bsfa_attn_merge(const void *const *o_parts, const float *const *lse_parts, int32_t n,
+                            int64_t part_stride_tok, int64_t part_stride_head,
+                            int64_t lse_stride_head, int32_t n_tok, int32_t n_head, int32_t d,
+                            bsfa_tensor *o, float *lse, void *stream);
+
+const char *bsfa_status_str(bsfa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSFA_H */

@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every symbol include/bsfa.h declares, and rejects
+bad arguments with the documented status codes (host-only calls, no GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from block_sparse_flash_csr_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "bsfa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsfa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 14
+    lib = api.library()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (bsfa_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_status_strings():
+    lib = api.library()
+    for s in range(0, 9):
+        assert lib.bsfa_status_str(s)
+
+
+def _create(slices, sq, sk, hq=2, hkv=1, d=128, bq=128, bk=128):
+    arr = (api.Slice * max(1, len(slices)))()
+    for t, s in enumerate(slices):
+        arr[t] = api.Slice(*s)
+    h = ctypes.c_void_p()
+    st = api.library().bsfa_plan_create(arr, len(slices), sq, sk, hq, hkv, d, bq, bk, ctypes.byref(h))
+    if st == 0:
+        api.library().bsfa_plan_destroy(h)
+    return st
+
+
+@pytest.mark.parametrize("slices,code", [
+    ([(0, 10, 0, 10, 2)], 5),          # unknown type
+    ([(5, 4, 0, 10, 0)], 5),           # q1 < q0
+    ([(0, 10, 6, 5, 1)], 5),           # k1 < k0
+    ([(0, 300, 0, 10, 0)], 5),         # q1 > sq
+    ([(0, 10, 0, 300, 0)], 5),         # k1 > sk
+    ([(-1, 10, 0, 10, 0)], 5),         # negative
+])
+def test_bad_slices_rejected(slices, code):
+    assert _create(slices, 256, 256) == code
+
+
+def test_bad_shapes_rejected():
+    assert _create([], 256, 256, hq=3, hkv=2) == 2
+    assert _create([], 256, 256, hq=0) == 1
+    assert _create([], -1, 256) == 1
+    assert _create([], 256, 256, bq=0) == 1
+    lib = api.library()
+    h = ctypes.c_void_p()
+    assert lib.bsfa_plan_create(None, 1, 8, 8, 1, 1, 64, 128, 128, ctypes.byref(h)) == 1
+    assert lib.bsfa_plan_create(None, 0, 8, 8, 1, 1, 64, 128, 128, None) == 1
+
+
+def test_varlen_and_blocks_errors():
+    lib = api.library()
+    h = ctypes.c_void_p()
+    cu = np.array([0, 10, 5], np.int32)   # decreasing
+    assert lib.bsfa_plan_from_varlen(cu.ctypes.data_as(ctypes.c_void_p), 2, 1, 1, 1, 64, 128, 128,
+                                     ctypes.byref(h)) == 5
+    cu = np.array([3, 10], np.int32)      # does not start at 0
+    assert lib.bsfa_plan_from_varlen(cu.ctypes.data_as(ctypes.c_void_p), 1, 1, 1, 1, 64, 128, 128,
+                                     ctypes.byref(h)) == 5
+    codes = np.array([[3]], np.uint8)     # unknown code
+    assert lib.bsfa_plan_from_blocks(codes.ctypes.data_as(ctypes.c_void_p), 1, 1, 16, 16, 16, 16, 1,
+                                     1, 64, 128, 128, ctypes.byref(h)) == 5
+
+
+def test_forward_rejects_unuploaded_and_unsupported():
+    """Checks that fail before any HIP call: no plan upload, unsupported tiles or head dim."""
+    lib = api.library()
+    p = api.Plan.from_slices([(0, 64, 0, 64, 1)], 64, 64, 1, 1, 128, bq=64, bk=64)
+    t = api.Tensor(ctypes.c_void_p(16), 8, 8)
+    lse = ctypes.c_void_p(16)
+    st = lib.bsfa_attn_fwd(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), p.handle, 0.1,
+                           ctypes.byref(t), lse, 64, None)
+    assert st == 4  # bq != 128
+    p = api.Plan.from_slices([(0, 64, 0, 64, 1)], 64, 64, 1, 1, 96)
+    st = lib.bsfa_attn_fwd(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), p.handle, 0.1,
+                           ctypes.byref(t), lse, 64, None)
+    assert st == 4  # d = 96
+    p = api.Plan.from_slices([(0, 64, 0, 64, 1)], 64, 64, 1, 1, 128)
+    st = lib.bsfa_attn_fwd(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), p.handle, 0.1,
+                           ctypes.byref(t), lse, 64, None)
+    assert st == 8  # not uploaded
+    st = lib.bsfa_attn_fwd(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), p.handle, -1.0,
+                           ctypes.byref(t), lse, 64, None)
+    assert st == 1  # non-positive scale
+
+
+def test_merge_rejects_bad_arguments():
+    lib = api.library()
+    t = api.Tensor(ctypes.c_void_p(16), 1024, 128)
+    ptrs = (ctypes.c_void_p * 2)(16, 32)
+    lptr = (ctypes.c_void_p * 2)(16, 32)
+    assert lib.bsfa_attn_merge(ptrs, lptr, 0, 1024, 128, 64, 64, 8, 128, ctypes.byref(t),
+                               ctypes.c_void_p(16), None) == 1
+    assert lib.bsfa_attn_merge(ptrs, lptr, 17, 1024, 128, 64, 64, 8, 128, ctypes.byref(t),
+                               ctypes.c_void_p(16), None) == 1
+    assert lib.bsfa_attn_merge(ptrs, lptr, 2, 1024, 128, 64, 64, 8, 96, ctypes.byref(t),
+                               ctypes.c_void_p(16), None) == 4
+    assert lib.bsfa_attn_merge(ptrs, lptr, 2, 1020, 128, 64, 64, 8, 128, ctypes.byref(t),
+                               ctypes.c_void_p(16), None) == 3
+    bad = (ctypes.c_void_p * 2)(16, 40)
+    assert lib.bsfa_attn_merge(bad, lptr, 2, 1024, 128, 64, 64, 8, 128, ctypes.byref(t),
+                               ctypes.c_void_p(16), None) == 3
+    assert lib.bsfa_attn_merge(ptrs, lptr, 2, 1024, 128, 10, 64, 8, 128, ctypes.byref(t),
+                               ctypes.c_void_p(16), None) == 1

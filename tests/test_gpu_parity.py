@@ -1,0 +1,229 @@
+"""GPU parity of the forward and merge kernels against the fp64 oracle, called through
+the C-ABI library.  Tolerances: max|dO| <= 1e-2, max|dLSE| <= 1e-3."""
+import numpy as np
+import pytest
+
+import oracle
+from block_sparse_flash_csr_amd import api
+from block_sparse_flash_csr_amd import workloads as W
+
+from gpu_helpers import compare, dev_bf16, host_bits, say, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    api.library()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_fwd(qb, kb, vb, slices, scale, sq, sk, hq, hkv, d, bk=128, plan=None):
+    import torch
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    own = plan is None
+    if own:
+        plan = api.Plan.from_slices(slices, sq, sk, hq, hkv, d, bk=bk).upload()
+    o, lse = api.attn_fwd(q, k, v, plan, scale)
+    torch.cuda.synchronize()
+    out = W.bf16_to_f32(host_bits(o)), lse.cpu().numpy()
+    if own:
+        plan.close()
+    return out
+
+
+def full_check(qb, kb, vb, slices, scale, what, bk=128):
+    sq, hq, d = qb.shape
+    sk, hkv, _ = kb.shape
+    say(f"{what}: sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} slices={len(slices)} bk={bk}")
+    o, lse = run_fwd(qb, kb, vb, slices, scale, sq, sk, hq, hkv, d, bk=bk)
+    o_ref, lse_ref = oracle.attn_fwd(qb, kb, vb, slices, scale)
+    return compare(o, lse, o_ref, lse_ref, what)
+
+
+# ---------------------------------------------------------------------------
+# element-by-element at sizes the oracle finishes in seconds
+# ---------------------------------------------------------------------------
+def test_config1_full():
+    w = W.config1()
+    full_check(w.q, w.k, w.v, w.slices, w.scale, "config1 causal S=256 d=64")
+
+
+@pytest.mark.parametrize("seed,sq,sk,hq,hkv,d,n", [
+    (1, 300, 300, 2, 2, 128, 4),
+    (2, 517, 389, 4, 2, 128, 6),
+    (3, 640, 640, 2, 1, 64, 3),
+    (4, 129, 700, 2, 2, 128, 8),
+    (5, 700, 129, 3, 3, 64, 5),
+    (6, 1, 50, 1, 1, 128, 2),
+])
+def test_random_masks_full(seed, sq, sk, hq, hkv, d, n):
+    rng = np.random.default_rng(seed)
+    slices = W.random_slices(rng, sq, sk, n)
+    qb, kb, vb = W.random_inputs(rng, sq, sk, hq, hkv, d)
+    full_check(qb, kb, vb, slices, 1.0 / np.sqrt(d), f"random seed={seed}")
+
+
+def test_every_partial_offset():
+    """Causal slices whose diagonal enters the tile at every offset 0..127 and ragged tails."""
+    sq, sk, d = 400, 400, 128
+    rng = np.random.default_rng(77)
+    qb, kb, vb = W.random_inputs(rng, sq, sk, 2, 1, d)
+    slices = [(0, sq, 0, sk - 61, 1), (3, 131, 200, 333, 1), (150, 151, 0, 400, 0)]
+    full_check(qb, kb, vb, slices, 1.0 / np.sqrt(d), "partial offsets")
+    slices = [(q0, q0 + 1, 0, q0 + 1 + (q0 % 7), 0) for q0 in range(0, sq)]
+    full_check(qb, kb, vb, slices, 1.0 / np.sqrt(d), "per-row ragged windows")
+
+
+def test_bk64_plan():
+    rng = np.random.default_rng(5)
+    sq = sk = 333
+    slices = W.random_slices(rng, sq, sk, 5)
+    qb, kb, vb = W.random_inputs(rng, sq, sk, 2, 2, 128)
+    full_check(qb, kb, vb, slices, 1.0 / np.sqrt(128), "plan bk=64", bk=64)
+
+
+def test_large_logits_exercise_rescale():
+    """Q scaled x8: tile maxima jump by more than the rescale threshold."""
+    rng = np.random.default_rng(9)
+    sq = sk = 512
+    qf = rng.standard_normal((sq, 2, 128), dtype=np.float32) * 8.0
+    qb = W.bf16_bits(qf)
+    _, kb, vb = W.random_inputs(rng, sq, sk, 2, 2, 128)
+    full_check(qb, kb, vb, [(0, sq, 0, sk, 1)], 1.0 / np.sqrt(128), "Q x8 causal")
+    # increasing scores along keys: the max moves on every tile
+    kf = W.bf16_to_f32(kb).copy()
+    kf += np.linspace(0, 6, sk, dtype=np.float32)[:, None, None] * np.sign(
+        W.bf16_to_f32(qb).mean(axis=0, keepdims=True))
+    full_check(qb, W.bf16_bits(kf), vb, [(0, sq, 0, sk, 0)], 1.0 / np.sqrt(128),
+               "growing max full")
+
+
+def test_fully_masked_rows_and_empty_tiles():
+    sq, sk, d = 384, 256, 128
+    rng = np.random.default_rng(10)
+    qb, kb, vb = W.random_inputs(rng, sq, sk, 2, 2, d)
+    # rows 128..255 have no key at all; rows 300..383 only via a rectangular causal slice
+    slices = [(0, 128, 0, 256, 1), (256, 384, 100, 140, 1)]
+    full_check(qb, kb, vb, slices, 0.1, "masked rows")
+    full_check(qb, kb, vb, [], 0.1, "empty mask")
+
+
+def test_deterministic_and_masked_perturbation_invisible():
+    import torch
+    sq = sk = 384
+    d = 128
+    rng = np.random.default_rng(12)
+    qb, kb, vb = W.random_inputs(rng, sq, sk, 2, 1, d)
+    slices = [(0, 200, 0, 200, 1), (200, 384, 64, 300, 0)]
+    say("determinism + masked perturbation")
+    o1, l1 = run_fwd(qb, kb, vb, slices, 0.1, sq, sk, 2, 1, d)
+    o2, l2 = run_fwd(qb, kb, vb, slices, 0.1, sq, sk, 2, 1, d)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # keys >= 300 are masked for every row; keys 200..299 for rows < 200
+    big = W.bf16_bits(np.array([3.0e4], np.float32))[0]
+    kb2, vb2 = kb.copy(), vb.copy()
+    kb2[300:] = big
+    vb2[300:] = big
+    kb2[200:300, :, 1::3] = big
+    vb2[200:300] = big
+    o3, l3 = run_fwd(qb, kb2, vb2, slices, 0.1, sq, sk, 2, 1, d)
+    assert np.array_equal(o1[:200], o3[:200]) and np.array_equal(l1[:, :200], l3[:, :200])
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# full sizes, sampled rows, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+def sampled_check(w, plan, rows, what):
+    import torch
+    q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    say(f"{what}: launching forward")
+    o, lse = api.attn_fwd(q, k, v, plan, w.scale)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o.float()).any().item(), "NaN in O"
+    r = np.array(rows, np.int64)
+    hs = torch.from_numpy(r[:, 0]).cuda()
+    is_ = torch.from_numpy(r[:, 1]).cuda()
+    o_s = W.bf16_to_f32(host_bits(o[is_, hs]))
+    l_s = lse[hs, is_].cpu().numpy()
+    o_ref, lse_ref = oracle.attn_fwd(w.q, w.k, w.v, w.slices, w.scale, rows=rows)
+    compare(o_s, l_s, o_ref, lse_ref, what)
+    return o, lse
+
+
+def test_config2_sampled():
+    w = W.config2()
+    plan = api.plan_from_workload(w)
+    cu = w.cu_seqlens
+    extra = list(cu[:-1]) + list(cu[:-1] + 1) + list(cu[1:] - 1) + list(cu[1:] - 2)
+    sampled_check(w, plan, sample_rows(w, 256, 2, extra), "config2 varlen causal")
+
+
+def test_config3_sampled():
+    w = W.config3()
+    plan = api.plan_from_workload(w)
+    extra = [128 * 8 * t + o for t in range(0, 32, 5) for o in (0, 1, 127)]
+    sampled_check(w, plan, sample_rows(w, 256, 3, extra), "config3 block-sparse strided")
+
+
+def test_config4_sampled():
+    w = W.config4()
+    plan = api.plan_from_workload(w)
+    extra = [s[0] for s in w.slices[16:40]] + [s[1] - 1 for s in w.slices[16:40]]
+    sampled_check(w, plan, sample_rows(w, 256, 4, extra), "config4 range slices GQA")
+
+
+@pytest.mark.parametrize("q_chunk", [7, 3])
+def test_config5_split_merge_sampled(q_chunk):
+    import torch
+    w = W.config5(q_chunk=q_chunk)
+    c, nc = w.extra["chunk"], w.extra["n_chunks"]
+    q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    plans = [api.Plan.from_slices(sl, c, c, w.hq, w.hkv, w.d).upload()
+             for sl in w.extra["chunk_slices"]]
+    say(f"config5 q_chunk={q_chunk}: 8 partial forwards + merge")
+    parts = [api.attn_fwd(q, k[t * c:(t + 1) * c], v[t * c:(t + 1) * c], plans[t], w.scale)
+             for t in range(nc)]
+    o, lse = api.attn_merge([p[0] for p in parts], [p[1] for p in parts])
+    torch.cuda.synchronize()
+    rows = sample_rows(w, 192, 5)
+    r = np.array(rows, np.int64)
+    hs = torch.from_numpy(r[:, 0]).cuda()
+    is_ = torch.from_numpy(r[:, 1]).cuda()
+    o_s = W.bf16_to_f32(host_bits(o[is_, hs]))
+    l_s = lse[hs, is_].cpu().numpy()
+    o_ref, lse_ref = oracle.attn_fwd(w.q, w.k, w.v, w.slices, w.scale, rows=rows)
+    compare(o_s, l_s, o_ref, lse_ref, f"config5 split+merge q_chunk={q_chunk}")
+    for p in plans:
+        p.close()
+
+
+# ---------------------------------------------------------------------------
+# merge kernel on synthetic partials
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,t,h,d", [(1, 77, 3, 128), (3, 300, 4, 64), (8, 1000, 5, 128),
+                                     (16, 129, 2, 128)])
+def test_merge_synthetic(n, t, h, d):
+    import torch
+    rng = np.random.default_rng(n * 1000 + t)
+    # partial outputs: averages of value rows, so std ~0.5; LSEs spread over a few units
+    o_bits = W.bf16_bits(0.5 * rng.standard_normal((n, t, h, d), dtype=np.float32))
+    lse_p = (3.0 * rng.standard_normal((n, h, t))).astype(np.float32)
+    lse_p[rng.random((n, h, t)) < 0.2] = -np.inf
+    lse_p[:, 0, :5] = -np.inf          # rows where every partial is empty
+    say(f"merge n={n} t={t} h={h} d={d}")
+    parts = [dev_bf16(o_bits[i]) for i in range(n)]
+    lses = [torch.from_numpy(lse_p[i]).cuda() for i in range(n)]
+    o, lse = api.attn_merge(parts, lses)
+    torch.cuda.synchronize()
+    o_f = W.bf16_to_f32(o_bits).astype(np.float64)          # [n, t, h, d]
+    po = o_f.transpose(0, 2, 1, 3).reshape(n, h * t, d)
+    pl = lse_p.reshape(n, h * t).astype(np.float64)
+    om, lm = oracle.merge(po, pl)
+    o_gpu = W.bf16_to_f32(host_bits(o)).transpose(1, 0, 2).reshape(h * t, d)
+    compare(o_gpu, lse.cpu().numpy().reshape(h * t), om, lm, f"merge n={n}")
