@@ -41,6 +41,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -194,7 +195,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
         f32x16 oacc[C::DB];
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16{};
-        float m_run = kMFloor, l_run = 0.f;
+        float m_run = kMFloor, l_run = 0.f, lb_run = 0.f;  // max, fp32 sum, bf16-weight sum
 
         const int e0 = a.meta.row_ptr[qt], e1 = a.meta.row_ptr[qt + 1];
         if (e0 < e1) {
@@ -274,26 +275,46 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
                 mx = wave_cross_half_max(mx) * a.c;   // tile max of t = c * s (c > 0)
+                // Each row moves its max only when its own tile max exceeds it by more
+                // than tau; other rows keep m and get alpha = 2^0 = 1 exactly, so a row's
+                // result never depends on the scores of another row.
                 const bool need = mx > m_run + kTau;
                 if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                    const float m_new = fmaxf(m_run, mx);
+                    const float m_new = need ? fmaxf(m_run, mx) : m_run;
                     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                     l_run *= alpha;
+                    lb_run *= alpha;
 #pragma unroll
                     for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
                     m_run = m_new;
                 }
-                float psum = 0.f;
                 bf16x8 pb[4];
+                float e0 = 0.f, e1 = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], a.c, -m_run));
-                        psum += p;
+                        if (r & 1) e1 += p; else e0 += p;
                         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
                     }
-                l_run += psum;
+                l_run += e0 + e1;
+                // O's normaliser sums the same bf16 weights that multiply V, so O is an
+                // exact weighted average of the rounded weights (in a peaked row the
+                // dominant weight's rounding cancels); v_dot2 adds two weights at once.
+                // The LSE keeps the fp32 sum above.
+                {
+                    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+                    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int t = 0; t < 4; t += 2) {
+                            s0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[j][2 * t], pb[j][2 * t + 1]}, ones, s0, false);
+                            s1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[j][2 * t + 2], pb[j][2 * t + 3]}, ones, s1, false);
+                        }
+                    lb_run += s0 + s1;
+                }
 
                 // ---- O^T += V^T P^T: A = V^T rows (head dims), B = P^T (from the score layout)
 #pragma unroll
@@ -323,11 +344,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
             }
         }
 
-        // ---- epilogue: O = O^T columns / l, LSE = ln2 * (m + log2 l)
+        // ---- epilogue: O = O^T columns / (sum of bf16 weights), LSE = ln2 * (m + log2 l)
         const float l_tot = wave_cross_half_sum(l_run);
+        const float lb_tot = wave_cross_half_sum(lb_run);
         if (qvalid) {
             const bool any = l_tot > 0.f;
-            const float inv = any ? 1.0f / l_tot : 0.f;
+            const float inv = any ? 1.0f / lb_tot : 0.f;
             __bf16 *op = (__bf16 *)a.o + (int64_t)qrow * a.o_st + (int64_t)h * a.o_sh;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
