@@ -89,7 +89,8 @@ struct FwdArgs {
     const void *q, *k, *v;
     void *o;
     float *lse;
-    int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh, lse_sh;
+    // element strides; validated to fit 32 bits (token strides at most 2^24)
+    int32_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh, lse_sh;
     int32_t sq, sk, hq, hkv, n_qt, bk_plan;
     float c;  // scale * log2(e)
     DeviceMeta meta;

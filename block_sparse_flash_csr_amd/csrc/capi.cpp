@@ -1,5 +1,6 @@
 // C ABI of libbsfa: argument checks, plan lifecycle and kernel dispatch.
 // The declarations and their contracts are in include/bsfa.h.
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -282,25 +283,34 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     if (lse_stride_head < p->sq) return BSFA_ERR_ARG;
     const bool need_q = p->sq > 0, need_k = p->sk > 0;
     if ((need_q && (!q->ptr || !o->ptr)) || (need_k && (!k->ptr || !v->ptr))) return BSFA_ERR_ARG;
-    for (const bsfa_tensor *t : {q, k, v, (const bsfa_tensor *)o}) {
-        if (t->ptr && !aligned16(t->ptr)) return BSFA_ERR_ALIGN;
-        if (!stride_ok(t->stride_tok) || !stride_ok(t->stride_head)) return BSFA_ERR_ALIGN;
+    // Strides: multiples of 8 elements (16-byte rows), a token row never overlapped by
+    // the next token's row (stride_tok >= d), and small enough for 32-bit offsets.
+    const int32_t n_tok[4] = {p->sq, p->sk, p->sk, p->sq};
+    const int32_t n_head[4] = {p->hq, p->hkv, p->hkv, p->hq};
+    const bsfa_tensor *ts[4] = {q, k, v, o};
+    for (int t = 0; t < 4; ++t) {
+        if (ts[t]->ptr && !aligned16(ts[t]->ptr)) return BSFA_ERR_ALIGN;
+        if (!stride_ok(ts[t]->stride_tok) || !stride_ok(ts[t]->stride_head)) return BSFA_ERR_ALIGN;
+        if (n_tok[t] > 1 && ts[t]->stride_tok < p->d) return BSFA_ERR_SHAPE;
+        if (n_head[t] > 1 && ts[t]->stride_head < p->d) return BSFA_ERR_SHAPE;
+        if (ts[t]->stride_tok > (1 << 24) || ts[t]->stride_head > INT32_MAX) return BSFA_ERR_UNSUPPORTED;
     }
+    if (lse_stride_head > INT32_MAX) return BSFA_ERR_UNSUPPORTED;
     FwdArgs a{};
     a.q = q->ptr;
     a.k = k->ptr;
     a.v = v->ptr;
     a.o = o->ptr;
     a.lse = lse;
-    a.q_st = q->stride_tok;
-    a.q_sh = q->stride_head;
-    a.k_st = k->stride_tok;
-    a.k_sh = k->stride_head;
-    a.v_st = v->stride_tok;
-    a.v_sh = v->stride_head;
-    a.o_st = o->stride_tok;
-    a.o_sh = o->stride_head;
-    a.lse_sh = lse_stride_head;
+    a.q_st = (int32_t)q->stride_tok;
+    a.q_sh = (int32_t)q->stride_head;
+    a.k_st = (int32_t)k->stride_tok;
+    a.k_sh = (int32_t)k->stride_head;
+    a.v_st = (int32_t)v->stride_tok;
+    a.v_sh = (int32_t)v->stride_head;
+    a.o_st = (int32_t)o->stride_tok;
+    a.o_sh = (int32_t)o->stride_head;
+    a.lse_sh = (int32_t)lse_stride_head;
     a.sq = p->sq;
     a.sk = p->sk;
     a.hq = p->hq;
