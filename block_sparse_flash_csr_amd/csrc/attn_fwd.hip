@@ -86,8 +86,10 @@ struct Cfg {
 // 16-byte chunk c of K row r sits at chunk c ^ kswz(r); of V row r at c ^ vswz(r).
 template <int D>
 __device__ __forceinline__ int kswz(int r) { return (r >> Cfg<D>::SWS) & (Cfg<D>::NCH - 1); }
+// The V swizzle keeps transpose reads conflict-free in 32-lane phases: the 4 rows a
+// 16-lane group reads land in 4 different 4-chunk groups of banks.
 template <int D>
-__device__ __forceinline__ int vswz(int r) { return 2 * (r & (Cfg<D>::NCH / 2 - 1)); }
+__device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 2 * (r & 3); }
 
 __device__ __forceinline__ float wave_cross_half_max(float x)
 {
@@ -169,7 +171,12 @@ __device__ __forceinline__ void load_tile(const void *src, int32_t st_elems, int
                                           char *lds_tile, int wave)
 {
     using C = Cfg<D>;
-    const __amdgpu_buffer_rsrc_t r = rsrc(src, (uint32_t)max(n, 0) * (uint32_t)st_elems * 2u);
+    // every operand of the resource is wave-uniform; say so, so that it lives in SGPRs
+    const uint64_t addr = (uint64_t)src;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)max(n, 0) * (uint32_t)st_elems * 2u);
+    const __amdgpu_buffer_rsrc_t r = rsrc((const void *)(((uint64_t)hi << 32) | lo), bytes);
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -363,7 +370,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
     using C = Cfg<D>;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_B];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform within a wave
     const int l32 = lane & 31, hh = lane >> 5;
     const int i0 = cload(a.meta.bin_ptr, (int)blockIdx.x), i1 = cload(a.meta.bin_ptr, (int)blockIdx.x + 1);
     const int group = a.hq / a.hkv;
