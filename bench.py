@@ -68,9 +68,11 @@ def headline(args, api, W):
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
+    t_host = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    host_ms = (t_host - t0) * 1e3 / args.steps   # host issue time per step (overlaps the GPU)
 
     # forward kernel alone, HIP events on its launch stream, inside the same process
     plan = api.Plan.from_varlen(w.cu_seqlens, w.hq, w.hkv, w.d, causal=True).upload(stream)
@@ -78,7 +80,7 @@ def headline(args, api, W):
                      max(args.steps, 20), stream)
     kernel_ms = float(np.mean(kt))
     plan.close()
-    return w, info, flops, ms_per_step, kernel_ms
+    return w, info, flops, ms_per_step, kernel_ms, host_ms
 
 
 def other_workloads(api, W, reps=10):
@@ -205,10 +207,11 @@ def main():
         return
     api.library()
 
-    w, info, flops, ms_per_step, kernel_ms = headline(args, api, W)
+    w, info, flops, ms_per_step, kernel_ms, host_ms = headline(args, api, W)
     value = flops / (ms_per_step * 1e-3) * 1e-12
     achieved = flops / (kernel_ms * 1e-3) * 1e-12
-    log(f"headline: step {ms_per_step:.4f} ms ({value:.1f} TFLOPS), forward kernel {kernel_ms:.4f} ms "
+    log(f"headline: step {ms_per_step:.4f} ms ({value:.1f} TFLOPS; host issue {host_ms:.4f} ms), "
+        f"forward kernel {kernel_ms:.4f} ms "
         f"({achieved:.1f} TFLOPS, {achieved / PEAK_BF16_TFLOPS:.3f} of peak)")
     others = {} if args.quick else other_workloads(api, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, info, args.cpu_seconds)
@@ -221,6 +224,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "host_ms_per_step": host_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -112,6 +112,7 @@ class Plan:
 
     def __init__(self, handle):
         self._h = handle
+        self._info = None
 
     # -- constructors ---------------------------------------------------------
     @classmethod
@@ -163,9 +164,19 @@ class Plan:
 
     # -- inspection -----------------------------------------------------------
     def info(self) -> dict:
+        """Plan statistics; shapes and counts are fixed at creation, so they are cached."""
         inf = PlanInfo()
         _check("bsfa_plan_get_info", library().bsfa_plan_get_info(self._h, ctypes.byref(inf)))
-        return {name: getattr(inf, name) for name, _ in PlanInfo._fields_}
+        d = {name: getattr(inf, name) for name, _ in PlanInfo._fields_}
+        self._info = d
+        return d
+
+    def shapes(self):
+        """(sq, sk, hq, hkv, d) of the plan."""
+        if self._info is None:
+            self.info()
+        i = self._info
+        return i["sq"], i["sk"], i["hq"], i["hkv"], i["d"]
 
     def csr(self):
         inf = self.info()
@@ -207,14 +218,13 @@ def attn_fwd(q, k, v, plan: Plan, scale: float, out=None, lse=None, stream=None)
     Returns (O [sq, hq, d] bf16, LSE [hq, sq] fp32)."""
     import torch
     sq, hq, d = q.shape
-    inf = plan.info()
-    if (sq, hq, d) != (inf["sq"], inf["hq"], inf["d"]):
-        raise ValueError(f"q shape {tuple(q.shape)} does not match the plan "
-                         f"({inf['sq']}, {inf['hq']}, {inf['d']})")
+    psq, psk, phq, phkv, pd = plan.shapes()
+    if (sq, hq, d) != (psq, phq, pd):
+        raise ValueError(f"q shape {tuple(q.shape)} does not match the plan ({psq}, {phq}, {pd})")
     for name, t in (("k", k), ("v", v)):
-        if tuple(t.shape) != (inf["sk"], inf["hkv"], inf["d"]):
+        if tuple(t.shape) != (psk, phkv, pd):
             raise ValueError(f"{name} shape {tuple(t.shape)} does not match the plan "
-                             f"({inf['sk']}, {inf['hkv']}, {inf['d']})")
+                             f"({psk}, {phkv}, {pd})")
     if out is None:
         out = torch.empty((sq, hq, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:

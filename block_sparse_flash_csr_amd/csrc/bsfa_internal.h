@@ -70,8 +70,6 @@ struct bsfa_plan {
     hipStream_t ustream = nullptr;
     bool dbuf_async = false;
     bsfa::DeviceMeta dev;
-    std::vector<uint8_t> staging;   // host image of the device metadata (kept until destroy)
-    hipEvent_t copied = nullptr;    // recorded after the upload copy
 };
 
 namespace bsfa {
@@ -80,9 +78,10 @@ namespace bsfa {
 bsfa_status compile_mask(const bsfa_slice *slices, int32_t n_slices, bsfa_plan &p);
 // Scheduler: items, costs and the per-bin lists.
 void build_schedule(bsfa_plan &p, int n_bins_max);
-// Min-heap greedy (LPT) of the given items onto the given bins; appends to lists/load.
+// Min-heap greedy (LPT) of the given items onto the given bins; appends (bin, item)
+// pairs in assignment order and updates the loads.
 void lpt(const std::vector<int32_t> &items, const std::vector<float> &cost,
-         const std::vector<int32_t> &bins, std::vector<std::vector<int32_t>> &lists,
+         const std::vector<int32_t> &bins, std::vector<std::pair<int32_t, int32_t>> &assign,
          std::vector<double> &load);
 
 struct FwdArgs {

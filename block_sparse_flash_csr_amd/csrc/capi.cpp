@@ -3,6 +3,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -72,6 +73,63 @@ size_t place(size_t &off, size_t count)
     const size_t at = off;
     off += count * sizeof(T);
     return at;
+}
+
+// Pinned host images of plan metadata, reused across uploads.  An image is busy
+// from its upload until the copy recorded behind it has run; uploads never wait for
+// it, they take another image (or pin a new one).  Images live until process exit.
+struct Staging {
+    void *host = nullptr;
+    size_t cap = 0;
+    int device = -1;
+    hipEvent_t copied = nullptr;
+    bool busy = false;
+};
+std::mutex g_staging_mu;
+std::vector<Staging *> g_staging;
+
+bsfa_status staging_acquire(int dev, size_t bytes, Staging **out)
+{
+    std::lock_guard<std::mutex> lk(g_staging_mu);
+    for (Staging *st : g_staging) {
+        if (st->device != dev || st->cap < bytes) continue;
+        if (st->busy && hipEventQuery(st->copied) != hipSuccess) continue;
+        st->busy = true;
+        *out = st;
+        return BSFA_OK;
+    }
+    Staging *st = new (std::nothrow) Staging;
+    if (!st) return BSFA_ERR_OOM;
+    size_t cap = 64 * 1024;
+    while (cap < bytes) cap *= 2;
+    if (hipHostMalloc(&st->host, cap, hipHostMallocDefault) != hipSuccess) {
+        delete st;
+        return BSFA_ERR_OOM;
+    }
+    if (hipEventCreateWithFlags(&st->copied, hipEventDisableTiming) != hipSuccess) {
+        (void)hipHostFree(st->host);
+        delete st;
+        return BSFA_ERR_HIP;
+    }
+    st->cap = cap;
+    st->device = dev;
+    st->busy = true;
+    try {
+        g_staging.push_back(st);
+    } catch (const std::bad_alloc &) {
+        (void)hipEventDestroy(st->copied);
+        (void)hipHostFree(st->host);
+        delete st;
+        return BSFA_ERR_OOM;
+    }
+    *out = st;
+    return BSFA_OK;
+}
+
+void staging_release_now(Staging *st)
+{
+    std::lock_guard<std::mutex> lk(g_staging_mu);
+    st->busy = false;
 }
 
 }  // namespace
@@ -150,12 +208,13 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     const size_t o_bp = place<int32_t>(off, p->bin_ptr.size());
     const size_t o_bi = place<int32_t>(off, p->bin_items.size());
     const size_t bytes = (off + 255) & ~size_t(255);
-    try {
-        p->staging.assign(bytes, 0);
-    } catch (const std::bad_alloc &) {
-        return BSFA_ERR_OOM;
-    }
-    uint8_t *h = p->staging.data();
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BSFA_ERR_HIP;
+    Staging *stg = nullptr;
+    bsfa_status st = staging_acquire(dev, bytes, &stg);
+    if (st != BSFA_OK) return st;
+    uint8_t *h = (uint8_t *)stg->host;
     std::memcpy(h + o_row, p->row_ptr.data(), p->row_ptr.size() * sizeof(int32_t));
     Entry *ent = (Entry *)(h + o_ent);
     for (size_t e = 0; e < nnz; ++e)
@@ -165,8 +224,6 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     if (!p->bin_items.empty())
         std::memcpy(h + o_bi, p->bin_items.data(), p->bin_items.size() * sizeof(int32_t));
 
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return BSFA_ERR_HIP;
     int pools = 0;
     (void)hipDeviceGetAttribute(&pools, hipDeviceAttributeMemoryPoolsSupported, dev);
     void *d = nullptr;
@@ -178,12 +235,15 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
         err = hipMalloc(&d, bytes);
         p->dbuf_async = false;
     }
-    if (err == hipErrorOutOfMemory) return BSFA_ERR_OOM;
-    if (err != hipSuccess) return BSFA_ERR_HIP;
+    if (err != hipSuccess) {
+        staging_release_now(stg);
+        return err == hipErrorOutOfMemory ? BSFA_ERR_OOM : BSFA_ERR_HIP;
+    }
+    // the pinned image stays reserved until the copy has run on the stream
     if (hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
-        hipEventCreateWithFlags(&p->copied, hipEventDisableTiming) != hipSuccess ||
-        hipEventRecord(p->copied, s) != hipSuccess) {
+        hipEventRecord(stg->copied, s) != hipSuccess) {
         if (p->dbuf_async) (void)hipFreeAsync(d, s); else (void)hipFree(d);
+        staging_release_now(stg);
         return BSFA_ERR_HIP;
     }
     uint8_t *base = (uint8_t *)d;
@@ -201,10 +261,6 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
 void bsfa_plan_destroy(bsfa_plan *p)
 {
     if (!p) return;
-    if (p->copied) {
-        (void)hipEventSynchronize(p->copied);  // the staging image must outlive its copy
-        (void)hipEventDestroy(p->copied);
-    }
     if (p->dbuf) {
         int cur = 0;
         (void)hipGetDevice(&cur);

@@ -32,6 +32,27 @@ inline int64_t row_hi(int64_t i, int64_t k_hi, int64_t diag)
     return lim < k_hi ? lim : k_hi;
 }
 
+// Admitted pairs of one piece inside rows [r0, r1) x keys [c0, c1), in closed form:
+// row i admits [lo, min(hi, i + diag + 1)) with lo = max(k_lo, c0), hi = min(k_hi, c1).
+int64_t piece_count(const Piece &p, int64_t r0, int64_t r1, int64_t c0, int64_t c1)
+{
+    const int64_t a = std::max<int64_t>(p.q_lo, r0), b = std::min<int64_t>(p.q_hi, r1);
+    const int64_t lo = std::max<int64_t>(p.k_lo, c0), hi = std::min<int64_t>(p.k_hi, c1);
+    if (a >= b || lo >= hi) return 0;
+    // width(i) = clamp(i + diag + 1 - lo, 0, hi - lo): zero below i0, full from i1 on
+    const int64_t i0 = lo - p.diag;            // first row with width >= 1
+    const int64_t i1 = hi - p.diag - 1;        // first row with full width
+    int64_t total = 0;
+    const int64_t ra = std::max(a, i0), rb = std::min(b, i1);   // rows on the ramp
+    if (ra < rb) {
+        const int64_t w0 = ra + p.diag + 1 - lo, w1 = rb - 1 + p.diag + 1 - lo;
+        total += (w0 + w1) * (rb - ra) / 2;
+    }
+    const int64_t fa = std::max(a, std::max(i1, i0));           // rows at full width
+    if (fa < b) total += (b - fa) * (hi - lo);
+    return total;
+}
+
 // Admitted pairs of the union of pieces inside rows [r0, r1) x keys [c0, c1).
 int64_t union_count(const std::vector<Piece> &pc, int64_t r0, int64_t r1, int64_t c0, int64_t c1,
                     std::vector<std::pair<int64_t, int64_t>> &ivs)
@@ -69,31 +90,44 @@ bsfa_status compile_mask(const bsfa_slice *slices, int32_t n_slices, bsfa_plan &
     p.n_qt = (int32_t)((sq + bq - 1) / bq);
     p.n_kt = (int32_t)((sk + bk - 1) / bk);
     try {
-        // 1. every (tile, slice) incidence with at least one admitted pair
-        std::vector<Touch> touches;
-        for (int32_t s = 0; s < n_slices; ++s) {
-            const bsfa_slice &sl = slices[s];
-            if (sl.q0 >= sl.q1 || sl.k0 >= sl.k1) continue;
-            const int64_t diag = sl.type == BSFA_CAUSAL ? (int64_t)sl.k1 - sl.q1 : kDiagFull;
-            for (int64_t qt = sl.q0 / bq; qt * bq < sl.q1; ++qt) {
-                const int64_t r0 = qt * bq, r1 = std::min(r0 + bq, sq);
-                const int64_t a = std::max<int64_t>(sl.q0, r0), b = std::min<int64_t>(sl.q1, r1);
-                const int64_t j_lo = sl.k0, j_hi = row_hi(b - 1, sl.k1, diag);
-                if (j_lo >= j_hi) continue;
-                const bool rows_all = a == r0 && b == r1;
-                for (int64_t kt = j_lo / bk; kt * bk < j_hi; ++kt) {
-                    const int64_t c0 = kt * bk, c1 = std::min(c0 + bk, sk);
-                    const bool covers = rows_all && sl.k0 <= c0 && sl.k1 >= c1 &&
-                                        (c1 - 1) <= r0 + diag;
-                    touches.push_back({(int32_t)qt, (int32_t)kt, s, covers ? 1 : 0});
+        // 1. every (tile, slice) incidence with at least one admitted pair, bucketed by
+        //    query-tile row (slices visit rows in order, so a counting pass suffices)
+        std::vector<int64_t> row_count((size_t)p.n_qt + 1, 0);
+        auto walk = [&](auto &&emit) {
+            for (int32_t s = 0; s < n_slices; ++s) {
+                const bsfa_slice &sl = slices[s];
+                if (sl.q0 >= sl.q1 || sl.k0 >= sl.k1) continue;
+                const int64_t diag = sl.type == BSFA_CAUSAL ? (int64_t)sl.k1 - sl.q1 : kDiagFull;
+                for (int64_t qt = sl.q0 / bq; qt * bq < sl.q1; ++qt) {
+                    const int64_t r0 = qt * bq, r1 = std::min(r0 + bq, sq);
+                    const int64_t a = std::max<int64_t>(sl.q0, r0), b = std::min<int64_t>(sl.q1, r1);
+                    const int64_t j_lo = sl.k0, j_hi = row_hi(b - 1, sl.k1, diag);
+                    if (j_lo >= j_hi) continue;
+                    const bool rows_all = a == r0 && b == r1;
+                    for (int64_t kt = j_lo / bk; kt * bk < j_hi; ++kt) {
+                        const int64_t c0 = kt * bk, c1 = std::min(c0 + bk, sk);
+                        const bool covers = rows_all && sl.k0 <= c0 && sl.k1 >= c1 &&
+                                            (c1 - 1) <= r0 + diag;
+                        emit(Touch{(int32_t)qt, (int32_t)kt, s, covers ? 1 : 0});
+                    }
                 }
             }
+        };
+        walk([&](const Touch &t) { ++row_count[(size_t)t.qt + 1]; });
+        for (int32_t qt = 0; qt < p.n_qt; ++qt) row_count[(size_t)qt + 1] += row_count[qt];
+        std::vector<Touch> touches((size_t)row_count[p.n_qt]);
+        {
+            std::vector<int64_t> fill(row_count.begin(), row_count.end() - 1);
+            walk([&](const Touch &t) { touches[(size_t)fill[t.qt]++] = t; });
         }
-        std::sort(touches.begin(), touches.end(), [](const Touch &x, const Touch &y) {
-            if (x.qt != y.qt) return x.qt < y.qt;
+        auto by_col = [](const Touch &x, const Touch &y) {
             if (x.kt != y.kt) return x.kt < y.kt;
             return x.slice < y.slice;
-        });
+        };
+        for (int32_t qt = 0; qt < p.n_qt; ++qt) {
+            auto b = touches.begin() + row_count[qt], e = touches.begin() + row_count[(size_t)qt + 1];
+            if (!std::is_sorted(b, e, by_col)) std::sort(b, e, by_col);
+        }
 
         // 2. one CSR entry per distinct tile
         p.row_ptr.assign((size_t)p.n_qt + 1, 0);
@@ -101,6 +135,9 @@ bsfa_status compile_mask(const bsfa_slice *slices, int32_t n_slices, bsfa_plan &
         p.tag.clear();
         p.piece_ptr.assign(1, 0);
         p.pieces.clear();
+        p.col.reserve(touches.size());
+        p.tag.reserve(touches.size());
+        p.piece_ptr.reserve(touches.size() + 1);
         p.n_full = p.n_partial = p.pairs = 0;
         std::vector<Piece> cand;
         std::vector<std::pair<int64_t, int64_t>> ivs;
@@ -132,7 +169,10 @@ bsfa_status compile_mask(const bsfa_slice *slices, int32_t n_slices, bsfa_plan &
                     pc.pad0 = pc.pad1 = pc.pad2 = 0;
                     cand.push_back(pc);
                 }
-                count = union_count(cand, r0, r1, c0, c1, ivs);
+                // one piece that does not cover the tile leaves it partial; several
+                // pieces may still cover it together, which the union count settles
+                count = cand.size() == 1 ? piece_count(cand[0], r0, r1, c0, c1)
+                                         : union_count(cand, r0, r1, c0, c1, ivs);
                 full = count == area;
             }
             p.col.push_back((int32_t)kt);

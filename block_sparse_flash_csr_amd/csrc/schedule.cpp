@@ -15,6 +15,7 @@
 // costs little balance: MI355X hands workgroups to its 8 XCDs round-robin, so bin
 // b runs on XCD b % 8, and each XCD has its own L2.
 #include <algorithm>
+#include <functional>
 #include <cmath>
 #include <queue>
 #include <utility>
@@ -23,10 +24,30 @@
 
 namespace bsfa {
 
-// LPT onto the given bins: heaviest item first (ties by id), each to the least
-// loaded bin (ties by bin id).  Appends to per-bin lists and loads.
+// LPT of items already in decreasing-cost order onto the given bins: each item to
+// the least-loaded bin (ties by bin id).  Appends (bin, item) in assignment order.
+void lpt_sorted(const std::vector<int32_t> &order, const std::vector<float> &cost,
+                const std::vector<int32_t> &bins, std::vector<std::pair<int32_t, int32_t>> &assign,
+                std::vector<double> &load)
+{
+    using Key = std::pair<double, int32_t>;
+    std::vector<Key> heap;
+    heap.reserve(bins.size());
+    for (int32_t b : bins) heap.push_back({load[b], b});
+    std::make_heap(heap.begin(), heap.end(), std::greater<Key>());
+    for (int32_t it : order) {
+        std::pop_heap(heap.begin(), heap.end(), std::greater<Key>());
+        Key &k = heap.back();
+        assign.push_back({k.second, it});
+        k.first += cost[it];
+        load[k.second] = k.first;
+        std::push_heap(heap.begin(), heap.end(), std::greater<Key>());
+    }
+}
+
+// LPT onto the given bins: heaviest item first (ties by id).
 void lpt(const std::vector<int32_t> &items, const std::vector<float> &cost,
-         const std::vector<int32_t> &bins, std::vector<std::vector<int32_t>> &lists,
+         const std::vector<int32_t> &bins, std::vector<std::pair<int32_t, int32_t>> &assign,
          std::vector<double> &load)
 {
     std::vector<int32_t> order(items);
@@ -34,16 +55,7 @@ void lpt(const std::vector<int32_t> &items, const std::vector<float> &cost,
         if (cost[a] != cost[b]) return cost[a] > cost[b];
         return a < b;
     });
-    using Key = std::pair<double, int32_t>;
-    std::priority_queue<Key, std::vector<Key>, std::greater<Key>> heap;
-    for (int32_t b : bins) heap.push({load[b], b});
-    for (int32_t it : order) {
-        Key k = heap.top();
-        heap.pop();
-        lists[k.second].push_back(it);
-        load[k.second] = k.first + cost[it];
-        heap.push({load[k.second], k.second});
-    }
+    lpt_sorted(order, cost, bins, assign, load);
 }
 
 void build_schedule(bsfa_plan &p, int n_bins_max)
@@ -71,7 +83,8 @@ void build_schedule(bsfa_plan &p, int n_bins_max)
     p.total_cost = total;
 
     const int32_t n_bins = std::max(1, std::min(n_items, n_bins_max));
-    std::vector<std::vector<int32_t>> lists((size_t)n_bins);
+    std::vector<std::pair<int32_t, int32_t>> assign;   // (bin, item) in assignment order
+    assign.reserve((size_t)n_items);
     std::vector<double> load((size_t)n_bins, 0.0);
 
     bool placed = false;
@@ -100,14 +113,25 @@ void build_schedule(bsfa_plan &p, int n_bins_max)
         const double xmax = *std::max_element(xload.begin(), xload.end());
         const double xavg = total / kNumXcd;
         if (xavg > 0 && xmax / xavg - 1.0 <= 0.03) {
-            // level 2: within each XCD, LPT over the bins that XCD runs
+            // level 2: within each XCD, LPT over the bins that XCD runs.  Every head has
+            // the same per-tile costs, so the query tiles are sorted once: items go in
+            // order of decreasing cost, ties by query tile, then head.
+            std::vector<int32_t> qorder((size_t)p.n_qt);
+            for (int32_t qt = 0; qt < p.n_qt; ++qt) qorder[qt] = qt;
+            std::stable_sort(qorder.begin(), qorder.end(),
+                             [&](int32_t x, int32_t y) { return row_cost[x] > row_cost[y]; });
+            std::vector<int32_t> items, bins;
             for (int32_t x = 0; x < kNumXcd; ++x) {
-                std::vector<int32_t> items, bins;
+                items.clear();
+                bins.clear();
+                std::vector<int32_t> heads;
                 for (int32_t g : xheads[x])
-                    for (int32_t h = g * group; h < (g + 1) * group; ++h)
-                        for (int32_t qt = 0; qt < p.n_qt; ++qt) items.push_back(h * p.n_qt + qt);
+                    for (int32_t h = g * group; h < (g + 1) * group; ++h) heads.push_back(h);
+                std::sort(heads.begin(), heads.end());
+                for (int32_t qt : qorder)
+                    for (int32_t h : heads) items.push_back(h * p.n_qt + qt);
                 for (int32_t b = x; b < n_bins; b += kNumXcd) bins.push_back(b);
-                lpt(items, p.item_cost, bins, lists, load);
+                lpt_sorted(items, p.item_cost, bins, assign, load);
             }
             placed = true;
         }
@@ -116,17 +140,20 @@ void build_schedule(bsfa_plan &p, int n_bins_max)
         std::vector<int32_t> items((size_t)n_items), bins((size_t)n_bins);
         for (int32_t i = 0; i < n_items; ++i) items[i] = i;
         for (int32_t b = 0; b < n_bins; ++b) bins[b] = b;
-        lpt(items, p.item_cost, bins, lists, load);
+        lpt(items, p.item_cost, bins, assign, load);
     }
 
+    // per-bin lists in assignment order (counting sort by bin)
     p.bin_ptr.assign((size_t)n_bins + 1, 0);
-    p.bin_items.clear();
-    p.makespan = 0.0;
-    for (int32_t b = 0; b < n_bins; ++b) {
-        p.bin_items.insert(p.bin_items.end(), lists[b].begin(), lists[b].end());
-        p.bin_ptr[(size_t)b + 1] = (int32_t)p.bin_items.size();
-        p.makespan = std::max(p.makespan, load[b]);
+    for (const auto &ba : assign) ++p.bin_ptr[(size_t)ba.first + 1];
+    for (int32_t b = 0; b < n_bins; ++b) p.bin_ptr[(size_t)b + 1] += p.bin_ptr[b];
+    p.bin_items.assign((size_t)n_items, 0);
+    {
+        std::vector<int32_t> fill(p.bin_ptr.begin(), p.bin_ptr.end() - 1);
+        for (const auto &ba : assign) p.bin_items[(size_t)fill[ba.first]++] = ba.second;
     }
+    p.makespan = 0.0;
+    for (int32_t b = 0; b < n_bins; ++b) p.makespan = std::max(p.makespan, load[b]);
 }
 
 }  // namespace bsfa
@@ -149,12 +176,12 @@ extern "C" double bsfa_lpt_assign(const float *cost, int32_t n_items, int32_t n_
         std::vector<int32_t> items((size_t)n_items), bins((size_t)n_bins);
         for (int32_t i = 0; i < n_items; ++i) items[i] = i;
         for (int32_t b = 0; b < n_bins; ++b) bins[b] = b;
-        std::vector<std::vector<int32_t>> lists((size_t)n_bins);
+        std::vector<std::pair<int32_t, int32_t>> assign;
         std::vector<double> load((size_t)n_bins, 0.0);
-        bsfa::lpt(items, c, bins, lists, load);
+        bsfa::lpt(items, c, bins, assign, load);
         double mk = 0.0;
+        for (const auto &ba : assign) bin_of[ba.second] = ba.first;
         for (int32_t b = 0; b < n_bins; ++b) {
-            for (int32_t it : lists[b]) bin_of[it] = b;
             if (bin_load) bin_load[b] = load[b];
             mk = std::max(mk, load[b]);
         }
