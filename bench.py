@@ -62,6 +62,12 @@ def headline(args, api, W):
     info = api.Plan.from_varlen(w.cu_seqlens, w.hq, w.hkv, w.d, causal=True).info()
     flops = 4.0 * w.d * info["pairs"] * w.hq
 
+    # untimed: bring the GPU to its sustained clock, then the W warmup steps
+    t_end = time.perf_counter() + args.prewarm_s
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -176,9 +182,11 @@ def cpu_baseline(w, info, target_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="only the headline workload")
+    ap.add_argument("--prewarm-s", type=float, default=1.0,
+                    help="untimed seconds of headline steps before the warmup steps (GPU clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",

@@ -29,7 +29,11 @@
 //     double-buffered staging): while the exponentials of step j run on the vector
 //     ALU, the matrix cores already form the scores of step j+1; while P_j V_j runs,
 //     the vector ALU sums step j's weights and takes step j+1's row maximum.  K is
-//     loaded two steps ahead and V one step ahead; one barrier per step.
+//     loaded two steps ahead and V one step ahead; one barrier per step.  The step
+//     body is straight-line, split into groups of one matrix product each (operands
+//     read from LDS two products ahead, the vector work of the group beside it), and
+//     its four LDS tiles are distinct restrict pointers, so no operand read waits for
+//     the direct loads in flight into the other two tiles.
 //   * Softmax in base 2 with a single FMA for scale and shift, and conditional
 //     rescaling (FlashAttention-4 article: rescale only when needed): a row's running
 //     max moves only when its tile max exceeds it by more than tau = 8.
@@ -91,11 +95,15 @@ __device__ __forceinline__ int kswz(int r) { return (r >> Cfg<D>::SWS) & (Cfg<D>
 template <int D>
 __device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 2 * (r & 3); }
 
+// IEEE 754-2019 maximum (NaN-propagating): lowers to v_maximum3_f32 chains with no
+// quieting of the matrix-core results that fmaxf would insert.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float wave_cross_half_max(float x)
 {
     // lanes l and l ^ 32 hold the same query: swap halves and take the max
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+    return vmax(__int_as_float(r[0]), __int_as_float(r[1]));
 }
 
 __device__ __forceinline__ float wave_cross_half_sum(float x)
@@ -199,7 +207,8 @@ __device__ __forceinline__ void load_v(const FwdArgs &a, const Step &st, int g, 
     load_tile<D>(base, a.v_st, min(kBkS, st.kv_end - st.kv0), ln.vg, lds_tile, wave);
 }
 
-// S^T (64 keys x 32 queries) = K Q^T from an LDS K tile, as two interleaved 32x32 chains.
+// S^T (64 keys x 32 queries) = K Q^T from an LDS K tile, as two interleaved 32x32
+// chains (the first step's scores; later steps form theirs inside the pipeline).
 template <int D>
 __device__ __forceinline__ void scores(const char *ktile, const Lane<D> &ln, const bf16x8 (&qf)[Cfg<D>::KS],
                                        f32x16 (&s)[2])
@@ -215,64 +224,60 @@ __device__ __forceinline__ void scores(const char *ktile, const Lane<D> &ln, con
     }
 }
 
-// Scores -inf where the step's mask rejects them.  off(kb, r) = kb*32 + 8*(r>>2) + (r&3)
-// is the key offset from base = kv0 + 4*hh of accumulator register r of block kb.
-__device__ __forceinline__ void apply_mask(const FwdArgs &a, const Step &cur, int qrow, int hh,
-                                           f32x16 (&sacc)[2])
+// Mask of one step for this lane's query row as a bit set over the 64 key offsets
+// from base = kv0 + 4*hh (bit o set: key base + o is admitted): the union of the
+// tile's slice pieces, cut at the end of the keys.
+__device__ __forceinline__ uint64_t range_bits(int lo, int hi)
+{
+    lo = max(lo, 0);
+    hi = min(hi, 64);
+    if (lo >= hi) return 0ull;
+    const uint64_t upto_hi = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
+    return upto_hi & ~((1ull << lo) - 1ull);
+}
+
+__device__ __forceinline__ uint64_t mask_bits(const FwdArgs &a, const Step &cur, int qrow, int hh)
 {
     const int base = cur.kv0 + 4 * hh;
-    const int kv_hi = min(cur.kv0 + kBkS, cur.kv_end);
-    const int tail = kv_hi - base;
+    const int tail = min(cur.kv0 + kBkS, cur.kv_end) - base;
+    if (!cur.partial) return range_bits(0, tail);
     const Entry en = cload(a.meta.entries, cur.entry);
-    if (!cur.partial || en.piece_count == 1) {
-        int lo = INT_MIN / 2, hi = tail;
-        if (cur.partial) {
-            const Piece pc = cload(a.meta.pieces, en.piece_begin);
-            const bool inq = qrow >= pc.q_lo && qrow < pc.q_hi;
-            lo = pc.k_lo - base;
-            hi = inq ? min(min(pc.k_hi, qrow + pc.diag + 1) - base, tail) : INT_MIN / 2;
-        }
-        if (__builtin_amdgcn_ballot_w64(lo > 0) == 0) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-                    sacc[kb][r] = off < hi ? sacc[kb][r] : -INFINITY;
-                }
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-                    sacc[kb][r] = (off >= lo && off < hi) ? sacc[kb][r] : -INFINITY;
-                }
-        }
-        return;
-    }
-    // several pieces: union of their intervals as a 64-bit mask over the offsets
     uint64_t m = 0;
     for (int pi = 0; pi < en.piece_count; ++pi) {
         const Piece pc = cload(a.meta.pieces, en.piece_begin + pi);
         if (qrow < pc.q_lo || qrow >= pc.q_hi) continue;
-        const int lo = max(pc.k_lo - base, 0);
-        const int hi = min(min(pc.k_hi, qrow + pc.diag + 1) - base, 64);
-        if (lo >= hi) continue;
-        const uint64_t upto_hi = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
-        m |= upto_hi & ~((1ull << lo) - 1ull);
+        m |= range_bits(pc.k_lo - base, min(pc.k_hi, qrow + pc.diag + 1) - base);
     }
-    if (tail < 64) m &= tail <= 0 ? 0ull : ((1ull << tail) - 1ull);
+    return m & range_bits(0, tail);
+}
+
+// Rejected scores become -inf: bit off of the mask word, sign-extended to a full
+// word (v_bfe_i32), selects between the score and -inf bit by bit (v_bfi_b32).
+// off(kb, r) = kb*32 + 8*(r>>2) + (r&3) is the offset of accumulator register r of
+// block kb from base.
+__device__ __forceinline__ void apply_bits(uint64_t m, f32x16 (&s)[2])
+{
+    const int32_t ninf = __float_as_int(-INFINITY);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+        const int32_t w = (int32_t)(kb ? (uint32_t)(m >> 32) : (uint32_t)m);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-            sacc[kb][r] = ((m >> off) & 1ull) ? sacc[kb][r] : -INFINITY;
+            const int off = 8 * (r >> 2) + (r & 3);   // < 32 within the block
+            const int32_t keep = (w << (31 - off)) >> 31;
+            s[kb][r] = __int_as_float((keep & __float_as_int(s[kb][r])) | (~keep & ninf));
         }
+    }
 }
 
 __device__ __forceinline__ bool needs_mask(const Step &st) { return st.partial || st.kv_end - st.kv0 < kBkS; }
+
+// Group q of a running max over elements 0..14 of one score block: 3 elements per group.
+__device__ __forceinline__ float max3_step(const f32x16 &b, int q, float mx)
+{
+    const float t = vmax(vmax(b[3 * q], b[3 * q + 1]), b[3 * q + 2]);
+    return q == 0 ? t : vmax(mx, t);
+}
 
 // Tile max of t = c * s for this lane's query (c > 0).
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[2], float c)
@@ -281,7 +286,7 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2], float c)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        for (int r = 0; r < 16; ++r) mx = vmax(mx, s[kb][r]);
     return wave_cross_half_max(mx) * c;
 }
 
@@ -310,58 +315,114 @@ __device__ __forceinline__ void rescale_for(float mx, Acc<D> &acc)
     }
 }
 
-// Exponentials of step j against the running max: bf16 weights and their fp32 sum.
-__device__ __forceinline__ void softmax_weights(const f32x16 (&s)[2], float c, float m_run, bf16x8 (&pb)[4],
-                                                float &psum)
-{
-    float e0 = 0.f, e1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        f32x8 pf;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            pf[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j >> 1][(j & 1) * 8 + r], c, -m_run));
-            if (r & 1) e1 += pf[r]; else e0 += pf[r];
-        }
-        pb[j] = __builtin_convertvector(pf, bf16x8);   // v_cvt_pk_bf16_f32 x 4
-    }
-    psum = e0 + e1;
-}
-
-// Sum of the bf16 weights (O's normaliser: O is then an exact weighted average of
-// the rounded weights, so in a peaked row the dominant weight's rounding cancels);
-// v_dot2 adds two weights at once.
-__device__ __forceinline__ float bf16_sum(const bf16x8 (&pb)[4])
-{
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int t = 0; t < 8; t += 4) {
-            s0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[j][t], pb[j][t + 1]}, ones, s0, false);
-            s1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[j][t + 2], pb[j][t + 3]}, ones, s1, false);
-        }
-    return s0 + s1;
-}
-
 // O^T += V^T P^T from an LDS V tile: A = V^T rows via transpose reads, B = P^T.
 template <int D>
-__device__ __forceinline__ void pv(const char *vtile, const Lane<D> &ln, const bf16x8 (&pb)[4],
-                                   f32x16 (&o)[Cfg<D>::DB])
+__device__ __forceinline__ bf16x8 v_operand(const char *vtile, const Lane<D> &ln, int i)
 {
     using C = Cfg<D>;
+    // PV product i: k-step i / DB (16 keys), O^T block i % DB (32 head dims)
+    const char *p = vtile + ln.vr[i % C::DB] + 16 * (i / C::DB) * C::ROWB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(p));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(p + 8 * C::ROWB));
+    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+}
+
+// K operand of score product i: k-step i / 2 (16 head dims), key block i % 2.
+template <int D>
+__device__ __forceinline__ bf16x8 k_operand(const char *ktile, const Lane<D> &ln, int i)
+{
+    return *(const bf16x8 *)(ktile + ln.kr[i >> 1] + (i & 1) * 32 * Cfg<D>::ROWB);
+}
+
+// Global source of one step's K or V tile, with the number of keys that exist.
+struct TileSrc {
+    const void *base;
+    int32_t st, n;
+};
+
+// The LDS-touching body of one pipelined step, straight-line and software-pipelined:
+//   phase 1: the 2*KS score products of step j+1 (K operand read two products ahead)
+//            with the exponentials of step j spread between them;
+//   phase 2: the 4*DB products P_j V_j (V^T operand read two products ahead) with the
+//            bf16 weight sums and the raw (unmasked) row max of step j+1 between them.
+// The four LDS tiles are separate restrict pointers: the direct loads into k_dst/v_dst
+// never overlap the reads of k_src/v_src, so no read waits for the loads in flight.
+template <int D>
+__device__ __forceinline__ void step_body(char *__restrict__ k_dst, char *__restrict__ v_dst,
+                                          const char *__restrict__ k_src, const char *__restrict__ v_src,
+                                          const TileSrc &kld, bool do_k, const TileSrc &vld, bool do_v,
+                                          const Lane<D> &ln, int wave, const bf16x8 (&qf)[Cfg<D>::KS],
+                                          const f32x16 (&cur)[2], float c, Acc<D> &acc, f32x16 (&nxt)[2],
+                                          float &mx_raw)
+{
+    using C = Cfg<D>;
+    constexpr int NS = 2 * C::KS;   // score products
+    constexpr int NP = 4 * C::DB;   // PV products
+    constexpr int EPG = 32 / NS;    // exponentials per score product
+    constexpr int DPG = 16 / NP;    // dot2 sums per PV product
+    static_assert(EPG * NS == 32 && DPG * NP == 16 && EPG % 2 == 0, "even split of the vector work");
+
+    if (do_k) load_tile<D>(kld.base, kld.st, kld.n, ln.kg, k_dst, wave);
+    if (do_v) load_tile<D>(vld.base, vld.st, vld.n, ln.vg, v_dst, wave);
+
+    const float nm = -acc.m;
+    bf16x8 pb[4];
+    f32x8 pf;
+    float e0, e1;
+    bf16x8 kop[3], vop[3];
+    kop[0] = k_operand<D>(k_src, ln, 0);
+    kop[1] = k_operand<D>(k_src, ln, 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int i = 0; i < NS; ++i) {
+        if (i + 2 < NS) kop[(i + 2) % 3] = k_operand<D>(k_src, ln, i + 2);
+        else vop[i + 2 - NS] = v_operand<D>(v_src, ln, i + 2 - NS);
+        const int kb = i & 1;
+        nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i % 3], qf[i >> 1], i < 2 ? f32x16{} : nxt[kb],
+                                                          0, 0, 0);
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-            const char *p = vtile + ln.vr[db] + 16 * ks * C::ROWB;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(p));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(p + 8 * C::ROWB));
-            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-            const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], o[db], 0, 0, 0);
+        for (int u = 0; u < EPG; ++u) {
+            const int v = EPG * i + u, j = v >> 3, r = v & 7;   // weight v -> pb[j][r]
+            pf[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[j >> 1][(j & 1) * 8 + r], c, nm));
+            float &ex = (r & 1) ? e1 : e0;
+            ex = v < 2 ? pf[r] : ex + pf[r];
+            if (r == 7) pb[j] = __builtin_convertvector(pf, bf16x8);   // v_cvt_pk_bf16_f32 x 4
         }
+        // keep the sums in this group (left alone they sink past the matrix products)
+        asm volatile("" : "+v"(e0), "+v"(e1));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    acc.l += e0 + e1;
+
+    // Phase 2 also takes the unmasked tile max of the new scores (block 0 once its
+    // chain has finished, block 1 two products later).
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float s0 = 0.f, s1 = 0.f, mx0 = 0.f, mx1 = 0.f;
+    constexpr int MG = 5, B0 = 2, B1 = NP >= 8 + MG ? 8 : NP;   // B1 == NP: after the loop
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        if (i + 2 < NP) vop[(i + 2) % 3] = v_operand<D>(v_src, ln, i + 2);
+        acc.o[i % C::DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[i % 3], pb[i / C::DB], acc.o[i % C::DB],
+                                                                   0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < DPG; ++u) {
+            const int t = DPG * i + u, j = t >> 2, e = 2 * (t & 3);   // pair t -> pb[j][e, e+1]
+            float &sx = (t & 1) ? s1 : s0;
+            sx = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[j][e], pb[j][e + 1]}, ones, sx, false);
+        }
+        // max over 16 scores of one block: a 3-way max per group on groups B0.. (block 0)
+        // and B1.. (block 1), the last element folded in at the end
+        if (i >= B0 && i < B0 + MG) mx0 = max3_step(nxt[0], i - B0, mx0);
+        if (i >= B1 && i < B1 + MG) mx1 = max3_step(nxt[1], i - B1, mx1);
+        asm volatile("" : "+v"(s0), "+v"(s1), "+v"(mx0), "+v"(mx1));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    acc.lb += s0 + s1;
+    if (B1 == NP)
+#pragma unroll
+        for (int q = 0; q < MG; ++q) mx1 = max3_step(nxt[1], q, mx1);
+    mx_raw = vmax(vmax(mx0, nxt[0][15]), vmax(mx1, nxt[1][15]));
 }
 
 template <int D>
@@ -414,7 +475,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
         {
             const int rows = max(0, min(32, a.sq - qrow0));
             const __bf16 *qb = (const __bf16 *)a.q + (int64_t)qrow0 * a.q_st + (int64_t)h * a.q_sh;
-            const __amdgpu_buffer_rsrc_t rq = rsrc(qb, (uint32_t)rows * (uint32_t)a.q_st * 2u);
+            const uint32_t qbytes = __builtin_amdgcn_readfirstlane((uint32_t)rows * (uint32_t)a.q_st * 2u);
+            const __amdgpu_buffer_rsrc_t rq = rsrc(qb, qbytes);
             const uint32_t qo = (uint32_t)(l32 * a.q_st * 2 + 16 * hh);
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16(rq, qo + 32 * ks));
@@ -450,8 +512,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
             __syncthreads();
             f32x16 sA[2], sB[2];
             scores<D>(smem + C::K_OFF0, ln, qf, sA);
-            if (needs_mask(st0)) apply_mask(a, st0, qrow, hh, sA);
+            if (needs_mask(st0)) apply_bits(mask_bits(a, st0, qrow, hh), sA);
             float mxA = tile_max(sA, c), mxB = 0.f;
+            acc.m = fmaxf(acc.m, mxA);   // O, l are still zero: start at the first tile's max
 
             // Pipelined step j (LDS buffers by parity P = j & 1): cur = S_j, nxt = S_{j+1}.
             auto step = [&](auto par_tag, f32x16(&cur)[2], const float mx_cur, f32x16(&nxt)[2], float &mx_nxt,
@@ -464,30 +527,25 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
                 const bool has1 = j + 1 < n, has2 = j + 2 < n;
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();   // K_{j+1}, V_j in LDS; every wave is done with step j-1
-                Step sj2 = sj1;
-                if (has2) {
-                    sj2 = next_step();
-                    load_k<D>(a, sj2, g, ln, smem + K_FREE, wave);
-                }
-                if (has1) load_v<D>(a, sj1, g, ln, smem + V_NEXT, wave);
-
-                // rescale first (needs only step j's tile max), then one branch-free block:
-                // exponentials of step j with the scores of step j+1 on the matrix cores,
-                // P_j V_j with the weight sums
-                rescale_for<D>(mx_cur, acc);
-                float psum;
-                bf16x8 pb[4];
-                softmax_weights(cur, c, acc.m, pb, psum);
-                // Unconditional so that it shares the block with the exponentials; on the
-                // last step it reads a stale (valid) tile and is discarded.
-                scores<D>(smem + K_NEXT, ln, qf, nxt);
-                pv<D>(smem + V_CUR, ln, pb, acc.o);
-                acc.l += psum;
-                acc.lb += bf16_sum(pb);
-                // step j+1's mask and row max
+                const Step sj2 = has2 ? next_step() : sj1;
+                const TileSrc kld{(const __bf16 *)a.k + (int64_t)g * a.k_sh + (int64_t)sj2.kv0 * a.k_st, a.k_st,
+                                  min(kBkS, sj2.kv_end - sj2.kv0)};
+                const TileSrc vld{(const __bf16 *)a.v + (int64_t)g * a.v_sh + (int64_t)sj1.kv0 * a.v_st, a.v_st,
+                                  min(kBkS, sj1.kv_end - sj1.kv0)};
+                rescale_for<D>(mx_cur, acc);   // needs only step j's tile max
+                __builtin_amdgcn_sched_barrier(0);
+                // The score products run unconditionally so the block stays straight-line;
+                // on the last step they read a stale (valid) tile and are discarded.
+                float mx_raw;
+                step_body<D>(smem + K_FREE, smem + V_NEXT, smem + K_NEXT, smem + V_CUR, kld, has2, vld, has1, ln,
+                             wave, qf, cur, c, acc, nxt, mx_raw);
                 if (has1) {
-                    if (needs_mask(sj1)) apply_mask(a, sj1, qrow, hh, nxt);
-                    mx_nxt = tile_max(nxt, c);
+                    if (needs_mask(sj1)) {
+                        apply_bits(mask_bits(a, sj1, qrow, hh), nxt);
+                        mx_nxt = tile_max(nxt, c);
+                    } else {
+                        mx_nxt = wave_cross_half_max(mx_raw) * c;
+                    }
                 }
                 return sj2;
             };

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "../../include/bsfa.h"
@@ -64,11 +65,14 @@ struct bsfa_plan {
     std::vector<int32_t> bin_ptr;      // [n_bins + 1]
     std::vector<int32_t> bin_items;    // item ids in execution order per bin
     double makespan = 0.0, total_cost = 0.0;
-    // device copy
+    // device copy: a pooled buffer, handed back when the plan is destroyed and reused
+    // only once the work enqueued on every stream that used it has run
     int device = -1;
     void *dbuf = nullptr;
-    hipStream_t ustream = nullptr;
-    bool dbuf_async = false;
+    void *slot = nullptr;                   // the pool slot that owns dbuf
+    hipStream_t ustream = nullptr;          // upload stream
+    mutable std::mutex streams_mu;
+    mutable std::vector<hipStream_t> used_streams;  // launch streams other than ustream
     bsfa::DeviceMeta dev;
 };
 

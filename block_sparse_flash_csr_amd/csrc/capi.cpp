@@ -2,6 +2,7 @@
 // The declarations and their contracts are in include/bsfa.h.
 #include <climits>
 #include <cmath>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -132,6 +133,93 @@ void staging_release_now(Staging *st)
     st->busy = false;
 }
 
+// Device buffers for plan metadata, reused across plans.  A buffer is lent to one
+// plan from its upload to its destruction; destruction records one event per stream
+// the plan was used on, and the buffer is lent again only once all of them have
+// completed.  Nothing waits and nothing is freed: buffers live until process exit.
+struct DevSlot {
+    void *ptr = nullptr;
+    size_t cap = 0;
+    int device = -1;
+    bool lent = false;
+    std::vector<hipEvent_t> released;   // recorded at destruction, one per stream
+    int n_released = 0;                 // how many of them the last destruction recorded
+};
+std::mutex g_dev_mu;
+std::vector<DevSlot *> g_dev;
+
+bool slot_idle(const DevSlot *d)
+{
+    for (int i = 0; i < d->n_released; ++i)
+        if (hipEventQuery(d->released[(size_t)i]) != hipSuccess) return false;
+    return true;
+}
+
+bsfa_status dev_acquire(int dev, size_t bytes, DevSlot **out)
+{
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    for (DevSlot *d : g_dev) {
+        if (d->device != dev || d->cap < bytes || d->lent || !slot_idle(d)) continue;
+        d->lent = true;
+        d->n_released = 0;
+        *out = d;
+        return BSFA_OK;
+    }
+    DevSlot *d = new (std::nothrow) DevSlot;
+    if (!d) return BSFA_ERR_OOM;
+    size_t cap = 64 * 1024;
+    while (cap < bytes) cap *= 2;
+    const hipError_t e = hipMalloc(&d->ptr, cap);
+    if (e != hipSuccess) {
+        delete d;
+        return e == hipErrorOutOfMemory ? BSFA_ERR_OOM : BSFA_ERR_HIP;
+    }
+    d->cap = cap;
+    d->device = dev;
+    d->lent = true;
+    try {
+        g_dev.push_back(d);
+    } catch (const std::bad_alloc &) {
+        (void)hipFree(d->ptr);
+        delete d;
+        return BSFA_ERR_OOM;
+    }
+    *out = d;
+    return BSFA_OK;
+}
+
+// Hands the buffer back behind the work already enqueued on the given streams.  If an
+// event cannot be made or recorded, the buffer is never lent again (leaked, not reused
+// early).
+void dev_release(DevSlot *d, const std::vector<hipStream_t> &streams)
+{
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    bool ok = true;
+    d->n_released = 0;
+    for (hipStream_t s : streams) {
+        if ((size_t)d->n_released == d->released.size()) {
+            hipEvent_t ev = nullptr;
+            if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+                ok = false;
+                break;
+            }
+            try {
+                d->released.push_back(ev);
+            } catch (const std::bad_alloc &) {
+                (void)hipEventDestroy(ev);
+                ok = false;
+                break;
+            }
+        }
+        if (hipEventRecord(d->released[(size_t)d->n_released], s) != hipSuccess) {
+            ok = false;
+            break;
+        }
+        ++d->n_released;
+    }
+    if (ok) d->lent = false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -224,25 +312,17 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     if (!p->bin_items.empty())
         std::memcpy(h + o_bi, p->bin_items.data(), p->bin_items.size() * sizeof(int32_t));
 
-    int pools = 0;
-    (void)hipDeviceGetAttribute(&pools, hipDeviceAttributeMemoryPoolsSupported, dev);
-    void *d = nullptr;
-    hipError_t err;
-    if (pools) {
-        err = hipMallocAsync(&d, bytes, s);
-        p->dbuf_async = true;
-    } else {
-        err = hipMalloc(&d, bytes);
-        p->dbuf_async = false;
-    }
-    if (err != hipSuccess) {
+    DevSlot *slot = nullptr;
+    st = dev_acquire(dev, bytes, &slot);
+    if (st != BSFA_OK) {
         staging_release_now(stg);
-        return err == hipErrorOutOfMemory ? BSFA_ERR_OOM : BSFA_ERR_HIP;
+        return st;
     }
+    void *d = slot->ptr;
     // the pinned image stays reserved until the copy has run on the stream
     if (hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
         hipEventRecord(stg->copied, s) != hipSuccess) {
-        if (p->dbuf_async) (void)hipFreeAsync(d, s); else (void)hipFree(d);
+        dev_release(slot, std::vector<hipStream_t>{s});
         staging_release_now(stg);
         return BSFA_ERR_HIP;
     }
@@ -253,6 +333,7 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     p->dev.bin_ptr = (const int32_t *)(base + o_bp);
     p->dev.bin_items = (const int32_t *)(base + o_bi);
     p->dbuf = d;
+    p->slot = slot;
     p->device = dev;
     p->ustream = s;
     return BSFA_OK;
@@ -261,12 +342,19 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
 void bsfa_plan_destroy(bsfa_plan *p)
 {
     if (!p) return;
-    if (p->dbuf) {
+    if (p->slot) {
         int cur = 0;
         (void)hipGetDevice(&cur);
         if (cur != p->device) (void)hipSetDevice(p->device);
-        if (p->dbuf_async) (void)hipFreeAsync(p->dbuf, p->ustream);
-        else (void)hipFree(p->dbuf);
+        std::vector<hipStream_t> streams;
+        try {
+            streams.push_back(p->ustream);
+            std::lock_guard<std::mutex> lk(p->streams_mu);
+            streams.insert(streams.end(), p->used_streams.begin(), p->used_streams.end());
+            dev_release((DevSlot *)p->slot, streams);
+        } catch (const std::bad_alloc &) {
+            // the buffer stays lent forever rather than being reused too early
+        }
         if (cur != p->device) (void)hipSetDevice(cur);
     }
     delete p;
@@ -377,7 +465,19 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     a.meta = p->dev;
     a.n_bins = (int32_t)p->bin_ptr.size() - 1;
     if (p->sq == 0) return BSFA_OK;
-    if (launch_attn_fwd(a, p->d, (hipStream_t)stream) != hipSuccess) return BSFA_ERR_HIP;
+    const hipStream_t s = (hipStream_t)stream;
+    if (s != p->ustream) {
+        // remember the stream: the plan's device buffer is released behind it
+        std::lock_guard<std::mutex> lk(p->streams_mu);
+        if (std::find(p->used_streams.begin(), p->used_streams.end(), s) == p->used_streams.end()) {
+            try {
+                p->used_streams.push_back(s);
+            } catch (const std::bad_alloc &) {
+                return BSFA_ERR_OOM;
+            }
+        }
+    }
+    if (launch_attn_fwd(a, p->d, s) != hipSuccess) return BSFA_ERR_HIP;
     return BSFA_OK;
 }
 

@@ -118,14 +118,17 @@ bsfa_status bsfa_plan_from_blocks(const uint8_t *codes, int32_t nbq, int32_t nbk
                                   bsfa_plan **out);
 
 /* Copy the plan's metadata to the current HIP device, enqueued on stream.  The
- * device buffer is allocated here (stream-ordered) and released by
- * bsfa_plan_destroy on the same stream.  Must precede bsfa_attn_fwd.  Errors:
- * BSFA_ERR_ARG, BSFA_ERR_STATE (already uploaded), BSFA_ERR_OOM, BSFA_ERR_HIP. */
+ * device buffer comes from a per-device pool the library owns: buffers are
+ * allocated on first need, reused by later plans and held until process exit, so a
+ * steady stream of plans allocates nothing and never synchronises.  Must precede
+ * bsfa_attn_fwd.  Errors: BSFA_ERR_ARG, BSFA_ERR_STATE (already uploaded),
+ * BSFA_ERR_OOM, BSFA_ERR_HIP. */
 bsfa_status bsfa_plan_upload(bsfa_plan *plan, void *stream);
 
-/* Releases host memory and, if uploaded, the device buffer (stream-ordered on the
- * upload stream: work already enqueued there that reads the plan stays valid;
- * work on other streams must be complete).  NULL is accepted. */
+/* Releases host memory and, if uploaded, hands the device buffer back to the pool
+ * behind the work enqueued so far on the upload stream and on every stream the plan
+ * was launched on (an event is recorded on each; the buffer is reused only after all
+ * of them have completed).  Never waits.  NULL is accepted. */
 void bsfa_plan_destroy(bsfa_plan *plan);
 
 bsfa_status bsfa_plan_get_info(const bsfa_plan *plan, bsfa_plan_info *info);
@@ -165,7 +168,8 @@ double bsfa_lpt_assign(const float *cost, int32_t n_items, int32_t n_bins, int32
  * and LSE = -inf.  Query head h reads key/value head h / (hq / hkv).
  * q, o: [sq, hq, d]; k, v: [sk, hkv, d]; lse: fp32, lse_stride_head >= sq.
  * Shapes come from the plan, which must be uploaded to the current device.
- * No allocation, no synchronisation; deterministic (no atomics).
+ * No allocation, no synchronisation; deterministic (no atomics).  The stream is
+ * remembered so that bsfa_plan_destroy releases the plan's buffer behind it.
  * Errors: BSFA_ERR_ARG, BSFA_ERR_ALIGN, BSFA_ERR_UNSUPPORTED (d not 64/128, bq != 128,
  * bk % 64 != 0), BSFA_ERR_STATE (plan not on this device), BSFA_ERR_HIP. */
 bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,

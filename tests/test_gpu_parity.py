@@ -228,3 +228,47 @@ def test_merge_synthetic(n, t, h, d):
     om, lm = oracle.merge(po, pl)
     o_gpu = W.bf16_to_f32(host_bits(o)).transpose(1, 0, 2).reshape(h * t, d)
     compare(o_gpu, lse.cpu().numpy().reshape(h * t), om, lm, f"merge n={n}")
+
+
+# ---------------------------------------------------------------------------
+# plan churn: device metadata buffers are pooled and reused without waiting
+# ---------------------------------------------------------------------------
+def test_plan_churn_reuses_buffers_safely():
+    """Plans of two different masks are built, uploaded, launched and destroyed back to
+    back with no synchronisation, some of them launched on a second stream; every
+    output must equal (bitwise) the output of a plan that lived alone."""
+    import torch
+    sq = sk = 640
+    d = 128
+    rng = np.random.default_rng(21)
+    qb, kb, vb = W.random_inputs(rng, sq, sk, 2, 2, d)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    masks = [[(0, sq, 0, sk, 1)], W.random_slices(rng, sq, sk, 9)]
+    say("plan churn: references")
+    ref = []
+    for m in masks:
+        p = api.Plan.from_slices(m, sq, sk, 2, 2, d).upload()
+        o, l = api.attn_fwd(q, k, v, p, 0.09)
+        torch.cuda.synchronize()
+        ref.append((o.clone(), l.clone()))
+        p.close()
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    outs = []
+    say("plan churn: 24 plans without synchronisation")
+    for i in range(24):
+        m = i % 2
+        p = api.Plan.from_slices(masks[m], sq, sk, 2, 2, d).upload(main)
+        o = torch.empty((sq, 2, d), dtype=torch.bfloat16, device="cuda")
+        l = torch.empty((2, sq), dtype=torch.float32, device="cuda")
+        if i % 3 == 2:
+            side.wait_stream(main)
+            api.attn_fwd(q, k, v, p, 0.09, out=o, lse=l, stream=side)
+            main.wait_stream(side)
+        else:
+            api.attn_fwd(q, k, v, p, 0.09, out=o, lse=l, stream=main)
+        p.close()
+        outs.append((m, o, l))
+    torch.cuda.synchronize()
+    for i, (m, o, l) in enumerate(outs):
+        assert torch.equal(o, ref[m][0]) and torch.equal(l, ref[m][1]), f"plan {i} (mask {m}) differs"
