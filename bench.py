@@ -28,6 +28,35 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_fwd_varlen_causal_t16384_h16_d128_hbm_traffic.md")
+KERNEL_SOURCES = ("block_sparse_flash_csr_amd/csrc/attn_fwd.hip",
+                  "block_sparse_flash_csr_amd/csrc/bsfa_internal.h",
+                  "block_sparse_flash_csr_amd/csrc/schedule.cpp")
+
+
+def kernel_digest() -> str:
+    """sha256 over the sources that decide the forward kernel's memory traffic."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary, or None
+    when the kernel sources have changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            fields = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+        if fields.get("kernel_source_sha256", "").strip() != kernel_digest():
+            return None
+        return int(fields["traffic_bytes_per_launch"].split()[0])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -245,7 +274,9 @@ def main():
                    "step": "plan build (CSR + schedule) + metadata upload + forward"},
         "frac_of_peak": value / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                     "traffic_unit": "bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, copy-calibrated)",
+                     "algorithmic_bytes": w.sq * w.hq * (4 * w.d + 4) + w.sk * w.hkv * 4 * w.d,
                      "kernel": "attn_fwd_kernel<128>", "kernel_ms": kernel_ms,
                      "flops_per_launch": flops},
         "cpu_baseline": cpu,
