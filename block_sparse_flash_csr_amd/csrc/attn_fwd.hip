@@ -145,22 +145,47 @@ __device__ __forceinline__ Piece cload(const Piece *p, int i)
 }
 
 // One 64-key step of a CSR entry: keys [kv0, min(kv0 + 64, kv_end)) exist.  A step
-// past the end of the keys (kv0 >= kv_end) is fully masked.
+// past the end of the keys (kv0 >= kv_end) is fully masked.  A partial step carries
+// its tile's slice pieces [pbeg, pbeg + pcnt).
 struct Step {
-    int32_t kv0, kv_end, entry, partial;
+    int32_t kv0, kv_end, partial, pbeg, pcnt;
 };
 
-__device__ __forceinline__ Step make_step(const FwdArgs &a, int e, int s)
+__device__ __forceinline__ Step make_step(const FwdArgs &a, const Entry &en, int s)
 {
-    const Entry en = cload(a.meta.entries, e);
     Step st;
     const int32_t c0 = en.col * a.bk_plan;
     st.kv0 = c0 + s * kBkS;
     st.kv_end = min(c0 + a.bk_plan, a.sk);
-    st.entry = e;
     st.partial = en.tag == BSFA_TILE_PARTIAL ? 1 : 0;
+    st.pbeg = en.piece_begin;
+    st.pcnt = en.piece_count;
     return st;
 }
+
+// Entry and slice pieces fetched a step ahead with vector loads (the step's own wait
+// for its K/V tiles covers them; a scalar load would have to be waited on at once).
+__device__ __forceinline__ i32x4 vload16(__amdgpu_buffer_rsrc_t r, int byte_off)
+{
+    return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ Entry uniform_entry(const i32x4 v)
+{
+    Entry en;
+    en.col = __builtin_amdgcn_readfirstlane(v[0]);
+    en.piece_begin = __builtin_amdgcn_readfirstlane(v[1]);
+    en.piece_count = __builtin_amdgcn_readfirstlane(v[2]);
+    en.tag = __builtin_amdgcn_readfirstlane(v[3]);
+    return en;
+}
+
+// Up to two pieces of a partial step held in registers: (q_lo, q_hi, k_lo, k_hi), diag.
+struct PiecePair {
+    i32x4 r0, r1;
+    int32_t d0, d1;
+};
+constexpr int kPfPieces = 2;
 
 // Per-lane constants for the whole launch.
 template <int D>
@@ -236,18 +261,42 @@ __device__ __forceinline__ uint64_t range_bits(int lo, int hi)
     return upto_hi & ~((1ull << lo) - 1ull);
 }
 
+// One score through the mask: bit off of w keeps it, else -inf (v_bfe_i32 + v_bfi_b32).
+__device__ __forceinline__ float masked(float x, int32_t w, int off)
+{
+    const int32_t keep = (w << (31 - off)) >> 31;
+    return __int_as_float((keep & __float_as_int(x)) | (~keep & __float_as_int(-INFINITY)));
+}
+
+__device__ __forceinline__ uint64_t piece_bits(int qrow, int base, int q_lo, int q_hi, int k_lo, int k_hi,
+                                               int diag)
+{
+    if (qrow < q_lo || qrow >= q_hi) return 0ull;
+    return range_bits(k_lo - base, min(k_hi, qrow + diag + 1) - base);
+}
+
+// Any number of pieces, read with scalar loads.
 __device__ __forceinline__ uint64_t mask_bits(const FwdArgs &a, const Step &cur, int qrow, int hh)
 {
     const int base = cur.kv0 + 4 * hh;
     const int tail = min(cur.kv0 + kBkS, cur.kv_end) - base;
     if (!cur.partial) return range_bits(0, tail);
-    const Entry en = cload(a.meta.entries, cur.entry);
     uint64_t m = 0;
-    for (int pi = 0; pi < en.piece_count; ++pi) {
-        const Piece pc = cload(a.meta.pieces, en.piece_begin + pi);
-        if (qrow < pc.q_lo || qrow >= pc.q_hi) continue;
-        m |= range_bits(pc.k_lo - base, min(pc.k_hi, qrow + pc.diag + 1) - base);
+    for (int pi = 0; pi < cur.pcnt; ++pi) {
+        const Piece pc = cload(a.meta.pieces, cur.pbeg + pi);
+        m |= piece_bits(qrow, base, pc.q_lo, pc.q_hi, pc.k_lo, pc.k_hi, pc.diag);
     }
+    return m & range_bits(0, tail);
+}
+
+// At most kPfPieces pieces, already in registers.
+__device__ __forceinline__ uint64_t mask_bits_pf(const Step &cur, const PiecePair &pp, int qrow, int hh)
+{
+    const int base = cur.kv0 + 4 * hh;
+    const int tail = min(cur.kv0 + kBkS, cur.kv_end) - base;
+    if (!cur.partial) return range_bits(0, tail);
+    uint64_t m = piece_bits(qrow, base, pp.r0[0], pp.r0[1], pp.r0[2], pp.r0[3], pp.d0);
+    if (cur.pcnt > 1) m |= piece_bits(qrow, base, pp.r1[0], pp.r1[1], pp.r1[2], pp.r1[3], pp.d1);
     return m & range_bits(0, tail);
 }
 
@@ -257,15 +306,12 @@ __device__ __forceinline__ uint64_t mask_bits(const FwdArgs &a, const Step &cur,
 // block kb from base.
 __device__ __forceinline__ void apply_bits(uint64_t m, f32x16 (&s)[2])
 {
-    const int32_t ninf = __float_as_int(-INFINITY);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const int32_t w = (int32_t)(kb ? (uint32_t)(m >> 32) : (uint32_t)m);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int off = 8 * (r >> 2) + (r & 3);   // < 32 within the block
-            const int32_t keep = (w << (31 - off)) >> 31;
-            s[kb][r] = __int_as_float((keep & __float_as_int(s[kb][r])) | (~keep & ninf));
+            s[kb][r] = masked(s[kb][r], w, 8 * (r >> 2) + (r & 3));
         }
     }
 }
@@ -396,7 +442,7 @@ __device__ __forceinline__ void step_body(char *__restrict__ k_dst, char *__rest
     acc.l += e0 + e1;
 
     // Phase 2 also takes the unmasked tile max of the new scores (block 0 once its
-    // chain has finished, block 1 two products later).
+    // chain has finished, block 1 later).
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float s0 = 0.f, s1 = 0.f, mx0 = 0.f, mx1 = 0.f;
     constexpr int MG = 5, B0 = 2, B1 = NP >= 8 + MG ? 8 : NP;   // B1 == NP: after the loop
@@ -437,6 +483,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
     const int i0 = cload(a.meta.bin_ptr, (int)blockIdx.x), i1 = cload(a.meta.bin_ptr, (int)blockIdx.x + 1);
     const int group = a.hq / a.hkv;
     const float c = a.c;
+    const __amdgpu_buffer_rsrc_t r_ent = rsrc(a.meta.entries, (uint32_t)a.n_entries * 16u);
+    const __amdgpu_buffer_rsrc_t r_pc = rsrc(a.meta.pieces, (uint32_t)a.n_pieces * 32u);
 
     Lane<D> ln;
     {
@@ -492,18 +540,33 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
         const int spe = a.bk_plan / kBkS;     // steps per CSR entry
         const int n = (e1 - e0) * spe;        // steps of this item
         if (n > 0) {
-            // step cursor: entry / sub-step of the next step to load
+            // Step cursor (entry ce, sub-step cs) of the next step to create, and that
+            // entry prefetched into registers.
             int ce = e0, cs = 0;
-            auto next_step = [&]() {
-                const Step st = make_step(a, ce, cs);
+            auto advance = [&]() {
                 if (++cs == spe) {
                     cs = 0;
                     ++ce;
                 }
-                return st;
             };
-            const Step st0 = next_step();
-            const Step st1 = n > 1 ? next_step() : st0;
+            const Step st0 = make_step(a, cload(a.meta.entries, ce), cs);
+            advance();
+            const Step st1 = n > 1 ? make_step(a, cload(a.meta.entries, ce), cs) : st0;
+            if (n > 1) advance();
+            i32x4 en_pf = vload16(r_ent, ce * 16);   // out of range reads as zeros
+            // pieces of the step whose mask is built next (st1 first)
+            PiecePair pp;
+            auto fetch_pieces = [&](const Step &st) {
+                if (st.partial && st.pcnt <= kPfPieces) {
+                    pp.r0 = vload16(r_pc, st.pbeg * 32);
+                    pp.d0 = vload16(r_pc, st.pbeg * 32 + 16)[0];
+                    if (st.pcnt > 1) {
+                        pp.r1 = vload16(r_pc, st.pbeg * 32 + 32);
+                        pp.d1 = vload16(r_pc, st.pbeg * 32 + 48)[0];
+                    }
+                }
+            };
+            fetch_pieces(st1);
             // prologue: K0, V0 and K1 into LDS; S0 and its max
             load_k<D>(a, st0, g, ln, smem + C::K_OFF0, wave);
             load_v<D>(a, st0, g, ln, smem + C::V_OFF0, wave);
@@ -527,7 +590,17 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
                 const bool has1 = j + 1 < n, has2 = j + 2 < n;
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();   // K_{j+1}, V_j in LDS; every wave is done with step j-1
-                const Step sj2 = has2 ? next_step() : sj1;
+                // step j+1's mask from the pieces fetched last step, before they are replaced
+                const bool m1 = has1 && needs_mask(sj1);
+                uint64_t bits = 0;
+                if (m1) bits = sj1.pcnt <= kPfPieces ? mask_bits_pf(sj1, pp, qrow, hh) : mask_bits(a, sj1, qrow, hh);
+                Step sj2 = sj1;
+                if (has2) {
+                    sj2 = make_step(a, uniform_entry(en_pf), cs);
+                    advance();
+                    if (cs == 0 && ce < e1) en_pf = vload16(r_ent, ce * 16);
+                    fetch_pieces(sj2);
+                }
                 const TileSrc kld{(const __bf16 *)a.k + (int64_t)g * a.k_sh + (int64_t)sj2.kv0 * a.k_st, a.k_st,
                                   min(kBkS, sj2.kv_end - sj2.kv0)};
                 const TileSrc vld{(const __bf16 *)a.v + (int64_t)g * a.v_sh + (int64_t)sj1.kv0 * a.v_st, a.v_st,
@@ -536,16 +609,17 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
                 __builtin_amdgcn_sched_barrier(0);
                 // The score products run unconditionally so the block stays straight-line;
                 // on the last step they read a stale (valid) tile and are discarded.
+                // One body for every step (two variants of it would not fit the register
+                // budget): a masked step applies its mask after the body and takes the
+                // max again.
                 float mx_raw;
                 step_body<D>(smem + K_FREE, smem + V_NEXT, smem + K_NEXT, smem + V_CUR, kld, has2, vld, has1, ln,
                              wave, qf, cur, c, acc, nxt, mx_raw);
-                if (has1) {
-                    if (needs_mask(sj1)) {
-                        apply_bits(mask_bits(a, sj1, qrow, hh), nxt);
-                        mx_nxt = tile_max(nxt, c);
-                    } else {
-                        mx_nxt = wave_cross_half_max(mx_raw) * c;
-                    }
+                if (m1) {
+                    apply_bits(bits, nxt);
+                    mx_nxt = tile_max(nxt, c);
+                } else if (has1) {
+                    mx_nxt = wave_cross_half_max(mx_raw) * c;
                 }
                 return sj2;
             };

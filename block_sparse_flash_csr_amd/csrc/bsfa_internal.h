@@ -98,6 +98,7 @@ struct FwdArgs {
     float c;  // scale * log2(e)
     DeviceMeta meta;
     int32_t n_bins;
+    int32_t n_entries, n_pieces;   // sizes of meta.entries / meta.pieces (bounds of vector loads)
 };
 hipError_t launch_attn_fwd(const FwdArgs &a, int d, hipStream_t stream);
 

@@ -464,6 +464,8 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     a.c = scale * 1.4426950408889634f;
     a.meta = p->dev;
     a.n_bins = (int32_t)p->bin_ptr.size() - 1;
+    a.n_entries = (int32_t)p->col.size();
+    a.n_pieces = (int32_t)p->pieces.size();
     if (p->sq == 0) return BSFA_OK;
     const hipStream_t s = (hipStream_t)stream;
     if (s != p->ustream) {
