@@ -133,6 +133,24 @@ void staging_release_now(Staging *st)
     st->busy = false;
 }
 
+// One internal copy stream per device (default priority, non-blocking): metadata
+// copies run there, beside the kernels of earlier steps, and the caller's stream waits
+// for them with an event.
+std::mutex g_cs_mu;
+std::vector<hipStream_t> g_copy_streams;
+
+hipStream_t copy_stream(int dev)
+{
+    std::lock_guard<std::mutex> lk(g_cs_mu);
+    if ((size_t)dev >= g_copy_streams.size()) g_copy_streams.resize((size_t)dev + 1, nullptr);
+    if (!g_copy_streams[(size_t)dev]) {
+        hipStream_t s = nullptr;
+        if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        g_copy_streams[(size_t)dev] = s;
+    }
+    return g_copy_streams[(size_t)dev];
+}
+
 // Device buffers for plan metadata, reused across plans.  A buffer is lent to one
 // plan from its upload to its destruction; destruction records one event per stream
 // the plan was used on, and the buffer is lent again only once all of them have
@@ -319,10 +337,20 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
         return st;
     }
     void *d = slot->ptr;
-    // the pinned image stays reserved until the copy has run on the stream
-    if (hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
-        hipEventRecord(stg->copied, s) != hipSuccess) {
-        dev_release(slot, std::vector<hipStream_t>{s});
+    // The copy runs on the internal copy stream (the buffer is idle, nothing earlier on
+    // s touches it) and s waits for it; the pinned image stays reserved until it has run.
+    hipStream_t cs = nullptr;
+    try {
+        cs = copy_stream(dev);
+    } catch (const std::bad_alloc &) {
+        cs = nullptr;
+    }
+    if (!cs || hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, cs) != hipSuccess ||
+        hipEventRecord(stg->copied, cs) != hipSuccess || hipStreamWaitEvent(s, stg->copied, 0) != hipSuccess) {
+        std::vector<hipStream_t> rel;
+        if (cs) rel.push_back(cs);
+        rel.push_back(s);
+        dev_release(slot, rel);
         staging_release_now(stg);
         return BSFA_ERR_HIP;
     }

@@ -117,8 +117,11 @@ bsfa_status bsfa_plan_from_blocks(const uint8_t *codes, int32_t nbq, int32_t nbk
                                   int32_t hq, int32_t hkv, int32_t d, int32_t bq, int32_t bk,
                                   bsfa_plan **out);
 
-/* Copy the plan's metadata to the current HIP device, enqueued on stream.  The
- * device buffer comes from a per-device pool the library owns: buffers are
+/* Copy the plan's metadata to the current HIP device.  The copy runs on an internal
+ * per-device copy stream (so it overlaps kernels already enqueued on stream) and
+ * stream waits for it: work enqueued on stream afterwards sees the metadata; other
+ * streams must be ordered after stream by the caller.  The device buffer comes from a
+ * per-device pool the library owns: buffers are
  * allocated on first need, reused by later plans and held until process exit, so a
  * steady stream of plans allocates nothing and never synchronises.  Must precede
  * bsfa_attn_fwd.  Errors: BSFA_ERR_ARG, BSFA_ERR_STATE (already uploaded),
