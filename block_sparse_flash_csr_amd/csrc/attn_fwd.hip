@@ -633,13 +633,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
             __syncthreads();   // every wave is done with the LDS tiles before the next item
         }
 
-        // ---- epilogue: O = O^T columns / (sum of bf16 weights), LSE = ln2 * (m + log2 l)
+        // ---- epilogue: O = O^T columns / (sum of bf16 weights), LSE = ln2 * (m + log2 l).
+        // A lane holds 4-value pieces of its query's row; the wave stages its 32 rows in
+        // LDS (the K tiles' space, free after the last step) and writes whole rows, 16 B
+        // per lane.  Staging swizzle (conflict-free writes and reads): 16-byte chunk c of
+        // row q at c ^ ((q >> ESH) mod NCH), its 8-byte halves swapped on rows 16..31.
         const float l_tot = wave_cross_half_sum(acc.l);
         const float lb_tot = wave_cross_half_sum(acc.lb);
-        if (qvalid) {
-            const bool any = l_tot > 0.f;
-            const float inv = any ? 1.0f / lb_tot : 0.f;
-            __bf16 *op = (__bf16 *)a.o + (int64_t)qrow * a.o_st + (int64_t)h * a.o_sh;
+        const bool any = l_tot > 0.f;
+        const float inv = any ? 1.0f / lb_tot : 0.f;
+        {
+            constexpr int ESH = D == 128 ? 0 : 1;
+            constexpr int RPI = 1024 / C::ROWB;   // rows per 16-byte-per-lane read
+            char *stage = smem + wave * 32 * C::ROWB;
+            const int qsw = (l32 >> ESH) & (C::NCH - 1), hsw = hh ^ ((l32 >> 4) & 1);
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -647,11 +654,21 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
                     bf16x4 w;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) w[r] = (__bf16)(acc.o[db][g4 * 4 + r] * inv);
-                    *(bf16x4 *)(op + db * 32 + 8 * g4 + 4 * hh) = w;
+                    *(bf16x4 *)(stage + l32 * C::ROWB + ((4 * db + g4) ^ qsw) * 16 + hsw * 8) = w;
                 }
-            if (hh == 0)
-                a.lse[(int64_t)h * a.lse_sh + qrow] = any ? (acc.m + __log2f(l_tot)) * kLn2 : -INFINITY;
+            const int cc = lane % C::NCH;
+#pragma unroll
+            for (int k = 0; k < 32 / RPI; ++k) {
+                const int row = RPI * k + lane / C::NCH;
+                const u32x4 v = *(const u32x4 *)(stage + row * C::ROWB + (cc ^ ((row >> ESH) & (C::NCH - 1))) * 16);
+                if (qrow0 + row < a.sq)
+                    *(u32x4 *)((__bf16 *)a.o + (int64_t)(qrow0 + row) * a.o_st + (int64_t)h * a.o_sh + cc * 8) =
+                        ((RPI * k) >> 4) & 1 ? u32x4{v[2], v[3], v[0], v[1]} : v;
+            }
+            __syncthreads();   // every wave has read its rows before the next item's loads
         }
+        if (qvalid && hh == 0)
+            a.lse[(int64_t)h * a.lse_sh + qrow] = any ? (acc.m + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
 }
 
