@@ -216,6 +216,17 @@ __device__ __forceinline__ void load_tile(const void *src, int32_t st_elems, int
             r, (lds_ptr)(lds_tile + (wave * C::NLD + i) * 1024), 16, (int)goff[i], 0, 0, 0);
 }
 
+// Buffer resource of one tile load (every operand wave-uniform, so it lives in SGPRs);
+// n = 0 makes every lane out of range: the load then only writes zeros into LDS.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *src, int32_t st_elems, int n)
+{
+    const uint64_t addr = (uint64_t)src;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)max(n, 0) * (uint32_t)st_elems * 2u);
+    return rsrc((const void *)(((uint64_t)hi << 32) | lo), bytes);
+}
+
 template <int D>
 __device__ __forceinline__ void load_k(const FwdArgs &a, const Step &st, int g, const Lane<D> &ln,
                                        char *lds_tile, int wave)
@@ -409,8 +420,12 @@ __device__ __forceinline__ void step_body(char *__restrict__ k_dst, char *__rest
     constexpr int DPG = 16 / NP;    // dot2 sums per PV product
     static_assert(EPG * NS == 32 && DPG * NP == 16 && EPG % 2 == 0, "even split of the vector work");
 
-    if (do_k) load_tile<D>(kld.base, kld.st, kld.n, ln.kg, k_dst, wave);
-    if (do_v) load_tile<D>(vld.base, vld.st, vld.n, ln.vg, v_dst, wave);
+    // The 2*NLD direct loads of K_{j+2} and V_{j+1} go one per score product below (a
+    // burst of them right after the barrier stalls the issue of the products); a tile
+    // that is not needed gets an empty resource.
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kld.base, kld.st, do_k ? kld.n : 0);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vld.base, vld.st, do_v ? vld.n : 0);
+    static_assert(2 * C::NLD <= NS, "one load per score product");
 
     const float nm = -acc.m;
     bf16x8 pb[4];
@@ -424,6 +439,12 @@ __device__ __forceinline__ void step_body(char *__restrict__ k_dst, char *__rest
     for (int i = 0; i < NS; ++i) {
         if (i + 2 < NS) kop[(i + 2) % 3] = k_operand<D>(k_src, ln, i + 2);
         else vop[i + 2 - NS] = v_operand<D>(v_src, ln, i + 2 - NS);
+        if (i < C::NLD)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(k_dst + (wave * C::NLD + i) * 1024), 16,
+                                                     (int)ln.kg[i], 0, 0, 0);
+        else if (i < 2 * C::NLD)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(v_dst + (wave * C::NLD + i - C::NLD) * 1024), 16,
+                                                     (int)ln.vg[i - C::NLD], 0, 0, 0);
         const int kb = i & 1;
         nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i % 3], qf[i >> 1], i < 2 ? f32x16{} : nxt[kb],
                                                           0, 0, 0);
@@ -630,7 +651,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
                 if (j + 1 >= n) break;
                 sj1 = step(std::integral_constant<int, 1>{}, sB, mxB, sA, mxA, sj1, j + 1);
             }
-            __syncthreads();   // every wave is done with the LDS tiles before the next item
+            // the last steps' direct loads (zero fills of unused tiles included) have landed
+            // and every wave is done with the LDS tiles before they are reused
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
         }
 
         // ---- epilogue: O = O^T columns / (sum of bf16 weights), LSE = ln2 * (m + log2 l).
