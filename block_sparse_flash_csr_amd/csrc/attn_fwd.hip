@@ -223,7 +223,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *src, int
     const uint64_t addr = (uint64_t)src;
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
-    const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)max(n, 0) * (uint32_t)st_elems * 2u);
+    // uniform first, so that the clamp and the product stay on the scalar unit
+    const int32_t rows = max(__builtin_amdgcn_readfirstlane(n), 0);
+    const uint32_t bytes = (uint32_t)rows * (uint32_t)__builtin_amdgcn_readfirstlane(st_elems) * 2u;
     return rsrc((const void *)(((uint64_t)hi << 32) | lo), bytes);
 }
 
