@@ -144,6 +144,31 @@ def other_workloads(api, W, reps=10):
         del q, k, v, o, lse
         torch.cuda.empty_cache()
 
+    # Few query rows against a long context (a prefill chunk): 1 query tile x 32 heads is
+    # 32 items for 512 workgroup slots, so the plan splits every row's key range into
+    # parts whose partial results a second kernel merges inside the same call.
+    sq, sk, hq, hkv, d = 128, 65536, 32, 8, 128
+    rng = np.random.default_rng(6)
+    qb, kb, vb = W.random_inputs(rng, sq, sk, hq, hkv, d)
+    q, k, v = api.to_device_bf16(qb), api.to_device_bf16(kb), api.to_device_bf16(vb)
+    plan = api.Plan.from_slices([(0, sq, 0, sk, 1)], sq, sk, hq, hkv, d).upload(stream)
+    info = plan.info()
+    fl = 4.0 * d * info["pairs"] * hq
+    o = torch.empty((sq, hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, sq), dtype=torch.float32, device="cuda")
+    f = lambda: api.attn_fwd(q, k, v, plan, 1.0 / np.sqrt(d), out=o, lse=lse, stream=stream)
+    for _ in range(3):
+        f()
+    ms = float(np.median(event_times(f, reps * 2, stream)))
+    name = f"prefill_chunk_q{sq}_ctx{sk}_gqa{hq}x{hkv}_d{d}"
+    out[name] = {"kernel_ms": ms, "tflops": fl / ms * 1e-9, "frac_of_peak": fl / ms * 1e-9 / PEAK_BF16_TFLOPS,
+                 "pairs_per_head": info["pairs"], "units": info["n_units"], "split_rows": info["n_splits"],
+                 "note": "not a reference workload; shows the in-call KV split (forward + part merge)"}
+    log(f"{name}: {ms:.3f} ms  {fl / ms * 1e-9:.1f} TFLOPS ({info['n_units']} units, {info['n_splits']} split rows)")
+    plan.close()
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
     # KV split: 8 partial forwards over 8192-token KV chunks, then the merge
     w = W.config5()
     c, nc = w.extra["chunk"], w.extra["n_chunks"]

@@ -46,7 +46,9 @@ class PlanInfo(ctypes.Structure):
                 ("nnz", ctypes.c_int64), ("n_full", ctypes.c_int64), ("n_partial", ctypes.c_int64),
                 ("n_pieces", ctypes.c_int64), ("pairs", ctypes.c_int64), ("n_items", ctypes.c_int32),
                 ("n_bins", ctypes.c_int32), ("makespan", ctypes.c_double),
-                ("total_cost", ctypes.c_double), ("uploaded", ctypes.c_int32)]
+                ("total_cost", ctypes.c_double), ("uploaded", ctypes.c_int32),
+                ("n_units", ctypes.c_int32), ("n_splits", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64)]
 
 
 _lib = None
@@ -72,6 +74,7 @@ def library():
     lib.bsfa_plan_get_info.argtypes = [P, ctypes.POINTER(PlanInfo)]
     lib.bsfa_plan_export_csr.argtypes = [P, P, P, P, I64, ctypes.POINTER(I64)]
     lib.bsfa_plan_export_schedule.argtypes = [P, P, P, P]
+    lib.bsfa_plan_export_units.argtypes = [P, P]
     lib.bsfa_tile_cost.argtypes = [I32, ctypes.c_double]
     lib.bsfa_tile_cost.restype = ctypes.c_double
     lib.bsfa_imbalance_bound.argtypes = [ctypes.c_double, I32]
@@ -190,13 +193,22 @@ class Plan:
         return row_ptr, col[:n.value].copy(), tag[:n.value].copy()
 
     def schedule(self):
+        """(bin_ptr [n_bins + 1], unit ids in execution order [n_units], unit cost by unit id).
+        Without split rows, unit id == item id == h * n_qtiles + qtile."""
         inf = self.info()
         bin_ptr = np.zeros(inf["n_bins"] + 1, np.int32)
-        items = np.zeros(max(1, inf["n_items"]), np.int32)
-        cost = np.zeros(max(1, inf["n_items"]), np.float32)
+        units = np.zeros(max(1, inf["n_units"]), np.int32)
+        cost = np.zeros(max(1, inf["n_units"]), np.float32)
         _check("bsfa_plan_export_schedule", library().bsfa_plan_export_schedule(
-            self._h, _ptr(bin_ptr), _ptr(items), _ptr(cost)))
-        return bin_ptr, items[:inf["n_items"]], cost[:inf["n_items"]]
+            self._h, _ptr(bin_ptr), _ptr(units), _ptr(cost)))
+        return bin_ptr, units[:inf["n_units"]], cost[:inf["n_units"]]
+
+    def units(self):
+        """[n_units, 4] int32: item, first entry, end entry (CSR indices), partial slot or -1."""
+        inf = self.info()
+        u = np.zeros((max(1, inf["n_units"]), 4), np.int32)
+        _check("bsfa_plan_export_units", library().bsfa_plan_export_units(self._h, _ptr(u)))
+        return u[:inf["n_units"]]
 
 
 def to_device_bf16(bits: np.ndarray, device="cuda"):

@@ -11,7 +11,11 @@
 //
 // Design (own, for CDNA4; the pages' Hopper/Blackwell kernels are prior art):
 //   * Work item = (query head, 128-query tile); 4 waves, 32 query rows each.  A
-//     persistent workgroup walks the items of its bin (min-heap greedy schedule).
+//     persistent workgroup walks the units of its bin (min-heap greedy schedule); a
+//     unit is an item over a range of its CSR row.  A row too costly for one bin is
+//     split into parts (UltraAttn 3.2: key ranges merge exactly through their
+//     summaries): a part writes its normalised fp32 O and LSE to a workspace slot and a
+//     second kernel merges the parts.
 //   * The CSR row of the query tile lists the non-empty key tiles; each is run in
 //     64-key steps.  Empty tiles never appear (UltraAttn 3.3: skip Empty blocks).
 //   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
@@ -56,6 +60,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -533,7 +538,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
     }
 
     for (int it = i0; it < i1; ++it) {
-        const int item = cload(a.meta.bin_items, it);
+        // unit: (item, entry range of its row, partial slot or -1)
+        const i32x4 un = ((cptr_i32x4)a.meta.units)[cload(a.meta.bin_items, it)];
+        const int item = un[0], slot = un[3];
         const int h = item / a.n_qt, qt = item - h * a.n_qt;
         const int g = h / group;
         const int qrow0 = qt * kKernelBq + wave * 32;
@@ -559,7 +566,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
         acc.l = 0.f;
         acc.lb = 0.f;
 
-        const int e0 = cload(a.meta.row_ptr, qt), e1 = cload(a.meta.row_ptr, qt + 1);
+        const int e0 = un[1], e1 = un[2];
         const int spe = a.bk_plan / kBkS;     // steps per CSR entry
         const int n = (e1 - e0) * spe;        // steps of this item
         if (n > 0) {
@@ -668,6 +675,24 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
         const float lb_tot = wave_cross_half_sum(acc.lb);
         const bool any = l_tot > 0.f;
         const float inv = any ? 1.0f / lb_tot : 0.f;
+        const float lse_v = any ? (acc.m + __log2f(l_tot)) * kLn2 : -INFINITY;
+        if (slot >= 0) {
+            // one part of a split row: normalised fp32 O and its LSE into the workspace
+            // slot (rows past the end included; the merge skips them)
+            float *ws = a.meta.ws + (size_t)slot * (kKernelBq * (D + 1));
+            const int r = wave * 32 + l32;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    f32x4 w;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) w[t] = acc.o[db][g4 * 4 + t] * inv;
+                    *(f32x4 *)(ws + (size_t)r * D + db * 32 + 8 * g4 + 4 * hh) = w;
+                }
+            if (hh == 0) ws[kKernelBq * D + r] = lse_v;
+            continue;
+        }
         {
             constexpr int ESH = D == 128 ? 0 : 1;
             constexpr int RPI = 1024 / C::ROWB;   // rows per 16-byte-per-lane read
@@ -693,8 +718,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
             }
             __syncthreads();   // every wave has read its rows before the next item's loads
         }
-        if (qvalid && hh == 0)
-            a.lse[(int64_t)h * a.lse_sh + qrow] = any ? (acc.m + __log2f(l_tot)) * kLn2 : -INFINITY;
+        if (qvalid && hh == 0) a.lse[(int64_t)h * a.lse_sh + qrow] = lse_v;
     }
 }
 

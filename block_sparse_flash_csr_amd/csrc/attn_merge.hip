@@ -16,6 +16,8 @@ namespace bsfa {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.693147180559945309f;
@@ -87,6 +89,55 @@ __global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a)
 }
 
 }  // namespace
+
+// Rows of the forward launch that were split into parts: the parts' normalised fp32
+// (O_t, LSE_t) in the workspace merge the same way into the caller's O and LSE.  A
+// workgroup takes RPB rows of one split row; a lane owns 4 head dims.
+template <int D>
+__global__ void __launch_bounds__(kThreads) split_merge_kernel(const SplitMergeArgs a)
+{
+    constexpr int TPR = D / 4;               // lanes per row (4 floats each)
+    constexpr int RPB = kThreads / TPR;      // rows per workgroup
+    constexpr size_t kSlot = (size_t)kKernelBq * (D + 1);
+    const int r = (int)blockIdx.y * RPB + (int)threadIdx.x / TPR;   // row within the tile
+    const int c = ((int)threadIdx.x % TPR) * 4;
+    const Split sp = a.splits[blockIdx.x];
+    const int h = sp.item / a.n_qt, qt = sp.item - h * a.n_qt;
+    const int row = qt * kKernelBq + r;
+    if (r >= kKernelBq || row >= a.sq) return;
+    const float *ws = a.ws + (size_t)sp.first * kSlot;
+    float m = -INFINITY;
+    for (int t = 0; t < sp.parts; ++t) m = fmaxf(m, ws[t * kSlot + kKernelBq * D + r]);
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    float lse = -INFINITY;
+    if (m != -INFINITY) {
+        float sum = 0.f;
+        for (int t = 0; t < sp.parts; ++t) {
+            const float w = exp2f((ws[t * kSlot + kKernelBq * D + r] - m) * kLog2e);
+            sum += w;
+            o += w * *(const f32x4 *)(ws + t * kSlot + (size_t)r * D + c);
+        }
+        o *= 1.0f / sum;
+        lse = m + __log2f(sum) * kLn2;
+    }
+    bf16x4 ob;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ob[e] = (__bf16)o[e];
+    *(bf16x4 *)((__bf16 *)a.o + (int64_t)row * a.o_st + (int64_t)h * a.o_sh + c) = ob;
+    if (c == 0) a.lse[(int64_t)h * a.lse_sh + row] = lse;
+}
+
+hipError_t launch_split_merge(const SplitMergeArgs &a, int d, hipStream_t stream)
+{
+    if (a.n_splits <= 0) return hipSuccess;
+    const int rpb = kThreads / (d / 4);
+    dim3 grid(a.n_splits, (kKernelBq + rpb - 1) / rpb);
+    if (d == 128)
+        hipLaunchKernelGGL(split_merge_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(split_merge_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_attn_merge(const MergeArgs &a, int d, hipStream_t stream)
 {

@@ -28,6 +28,20 @@ struct Entry {
 };
 static_assert(sizeof(Entry) == 16, "Entry is one 16-byte word");
 
+// One unit of forward work: item = h * n_qt + qt over the entry range [eb, ee) of the
+// query tile's CSR row.  slot < 0: the unit covers the whole row and writes O / LSE;
+// otherwise it writes partial results into workspace slot `slot` (the row was split).
+struct Unit {
+    int32_t item, eb, ee, slot;
+};
+static_assert(sizeof(Unit) == 16, "Unit is one 16-byte word");
+
+// A split row of one query head: its parts occupy slots first .. first + parts - 1.
+struct Split {
+    int32_t item, first, parts, pad;
+};
+static_assert(sizeof(Split) == 16, "Split is one 16-byte word");
+
 constexpr int32_t kDiagFull = 1 << 30;
 constexpr int kKernelBq = 128;   // query rows per work item (4 waves x 32)
 constexpr int kKernelBk = 64;    // keys per inner step of the forward kernel
@@ -38,6 +52,10 @@ constexpr int kNumCu = 256;
 // A partial tile runs the same matrix work plus the per-element mask; the
 // per-item constant covers the Q load and the O/LSE epilogue.
 constexpr double kCostPartial = 1.15;
+// Rows costlier than the per-bin target (total / bins) are split into parts of about
+// the target, at most kMaxParts; a part is never below kMinPartCost.
+constexpr double kMinPartCost = 16.0;
+constexpr int32_t kMaxParts = 16;
 constexpr double kCostItem = 1.0;
 
 struct DeviceMeta {
@@ -45,7 +63,11 @@ struct DeviceMeta {
     const Entry *entries = nullptr;
     const Piece *pieces = nullptr;
     const int32_t *bin_ptr = nullptr;
-    const int32_t *bin_items = nullptr;
+    const int32_t *bin_items = nullptr;   // unit ids in execution order per bin
+    const Unit *units = nullptr;
+    const Split *splits = nullptr;
+    float *ws = nullptr;                  // partial results of split rows: per slot
+                                          // O [128][d] then LSE [128], fp32
 };
 
 }  // namespace bsfa
@@ -62,8 +84,12 @@ struct bsfa_plan {
     int64_t n_full = 0, n_partial = 0, pairs = 0;
     // schedule
     std::vector<float> item_cost;      // by item id = h * n_qt + qt
+    std::vector<bsfa::Unit> units;     // by unit id; unit id == item id when no row is split
+    std::vector<float> unit_cost;      // by unit id
+    std::vector<bsfa::Split> splits;   // split (head, row) pairs
+    int32_t n_slots = 0;               // partial-result slots of the split rows
     std::vector<int32_t> bin_ptr;      // [n_bins + 1]
-    std::vector<int32_t> bin_items;    // item ids in execution order per bin
+    std::vector<int32_t> bin_items;    // unit ids in execution order per bin
     double makespan = 0.0, total_cost = 0.0;
     // device copy: a pooled buffer, handed back when the plan is destroyed and reused
     // only once the work enqueued on every stream that used it has run
@@ -101,6 +127,17 @@ struct FwdArgs {
     int32_t n_entries, n_pieces;   // sizes of meta.entries / meta.pieces (bounds of vector loads)
 };
 hipError_t launch_attn_fwd(const FwdArgs &a, int d, hipStream_t stream);
+
+// Merge of split rows: partial results in meta.ws -> O (bf16) and LSE.
+struct SplitMergeArgs {
+    const float *ws;
+    const Split *splits;
+    int32_t n_splits, n_qt, sq;
+    void *o;
+    float *lse;
+    int32_t o_st, o_sh, lse_sh;
+};
+hipError_t launch_split_merge(const SplitMergeArgs &a, int d, hipStream_t stream);
 
 struct MergeArgs {
     const void *o_parts[BSFA_MERGE_MAX_PARTS];

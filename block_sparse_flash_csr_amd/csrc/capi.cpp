@@ -67,6 +67,10 @@ bsfa_status build_plan(const bsfa_slice *slices, int32_t n_slices, int32_t sq, i
     return BSFA_OK;
 }
 
+// Partial results of one part: O [kKernelBq][d] then LSE [kKernelBq], fp32.
+size_t slot_floats(int32_t d) { return (size_t)kKernelBq * ((size_t)d + 1); }
+size_t workspace_bytes(const bsfa_plan &p) { return (size_t)p.n_slots * slot_floats(p.d) * sizeof(float); }
+
 template <class T>
 size_t place(size_t &off, size_t count)
 {
@@ -305,7 +309,8 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     if (!p) return BSFA_ERR_ARG;
     if (p->dbuf) return BSFA_ERR_STATE;
     hipStream_t s = (hipStream_t)stream;
-    // one image: row_ptr | entries | pieces | bin_ptr | bin_items
+    // one image: row_ptr | entries | pieces | bin_ptr | bin_items | units | splits, then
+    // the workspace of split rows (device only, not copied)
     size_t off = 0;
     const size_t nnz = p->col.size();
     const size_t o_row = place<int32_t>(off, p->row_ptr.size());
@@ -313,7 +318,10 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     const size_t o_pc = place<Piece>(off, p->pieces.size());
     const size_t o_bp = place<int32_t>(off, p->bin_ptr.size());
     const size_t o_bi = place<int32_t>(off, p->bin_items.size());
+    const size_t o_un = place<Unit>(off, p->units.size());
+    const size_t o_sp = place<Split>(off, p->splits.size());
     const size_t bytes = (off + 255) & ~size_t(255);
+    const size_t ws_bytes = workspace_bytes(*p);
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return BSFA_ERR_HIP;
@@ -329,9 +337,11 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     std::memcpy(h + o_bp, p->bin_ptr.data(), p->bin_ptr.size() * sizeof(int32_t));
     if (!p->bin_items.empty())
         std::memcpy(h + o_bi, p->bin_items.data(), p->bin_items.size() * sizeof(int32_t));
+    if (!p->units.empty()) std::memcpy(h + o_un, p->units.data(), p->units.size() * sizeof(Unit));
+    if (!p->splits.empty()) std::memcpy(h + o_sp, p->splits.data(), p->splits.size() * sizeof(Split));
 
     DevSlot *slot = nullptr;
-    st = dev_acquire(dev, bytes, &slot);
+    st = dev_acquire(dev, bytes + ws_bytes, &slot);
     if (st != BSFA_OK) {
         staging_release_now(stg);
         return st;
@@ -360,6 +370,9 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     p->dev.pieces = (const Piece *)(base + o_pc);
     p->dev.bin_ptr = (const int32_t *)(base + o_bp);
     p->dev.bin_items = (const int32_t *)(base + o_bi);
+    p->dev.units = (const Unit *)(base + o_un);
+    p->dev.splits = (const Split *)(base + o_sp);
+    p->dev.ws = ws_bytes ? (float *)(base + bytes) : nullptr;
     p->dbuf = d;
     p->slot = slot;
     p->device = dev;
@@ -410,6 +423,9 @@ bsfa_status bsfa_plan_get_info(const bsfa_plan *p, bsfa_plan_info *info)
     info->makespan = p->makespan;
     info->total_cost = p->total_cost;
     info->uploaded = p->dbuf ? 1 : 0;
+    info->n_units = (int32_t)p->units.size();
+    info->n_splits = (int32_t)p->splits.size();
+    info->workspace_bytes = (int64_t)workspace_bytes(*p);
     return BSFA_OK;
 }
 
@@ -428,15 +444,22 @@ bsfa_status bsfa_plan_export_csr(const bsfa_plan *p, int32_t *row_ptr, int32_t *
     return BSFA_OK;
 }
 
-bsfa_status bsfa_plan_export_schedule(const bsfa_plan *p, int32_t *bin_ptr, int32_t *items,
-                                      float *item_cost)
+bsfa_status bsfa_plan_export_schedule(const bsfa_plan *p, int32_t *bin_ptr, int32_t *units,
+                                      float *unit_cost)
 {
     if (!p) return BSFA_ERR_ARG;
     if (bin_ptr) std::memcpy(bin_ptr, p->bin_ptr.data(), p->bin_ptr.size() * sizeof(int32_t));
-    if (items && !p->bin_items.empty())
-        std::memcpy(items, p->bin_items.data(), p->bin_items.size() * sizeof(int32_t));
-    if (item_cost && !p->item_cost.empty())
-        std::memcpy(item_cost, p->item_cost.data(), p->item_cost.size() * sizeof(float));
+    if (units && !p->bin_items.empty())
+        std::memcpy(units, p->bin_items.data(), p->bin_items.size() * sizeof(int32_t));
+    if (unit_cost && !p->unit_cost.empty())
+        std::memcpy(unit_cost, p->unit_cost.data(), p->unit_cost.size() * sizeof(float));
+    return BSFA_OK;
+}
+
+bsfa_status bsfa_plan_export_units(const bsfa_plan *p, int32_t *units)
+{
+    if (!p || !units) return BSFA_ERR_ARG;
+    if (!p->units.empty()) std::memcpy(units, p->units.data(), p->units.size() * sizeof(Unit));
     return BSFA_OK;
 }
 
@@ -508,6 +531,20 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
         }
     }
     if (launch_attn_fwd(a, p->d, s) != hipSuccess) return BSFA_ERR_HIP;
+    if (!p->splits.empty()) {
+        SplitMergeArgs m;
+        m.ws = p->dev.ws;
+        m.splits = p->dev.splits;
+        m.n_splits = (int32_t)p->splits.size();
+        m.n_qt = p->n_qt;
+        m.sq = p->sq;
+        m.o = o->ptr;
+        m.lse = lse;
+        m.o_st = a.o_st;
+        m.o_sh = a.o_sh;
+        m.lse_sh = a.lse_sh;
+        if (launch_split_merge(m, p->d, s) != hipSuccess) return BSFA_ERR_HIP;
+    }
     return BSFA_OK;
 }
 

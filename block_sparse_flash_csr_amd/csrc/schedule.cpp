@@ -61,19 +61,23 @@ void lpt(const std::vector<int32_t> &items, const std::vector<float> &cost,
 void build_schedule(bsfa_plan &p, int n_bins_max)
 {
     const int32_t n_items = p.hq * p.n_qt;
-    p.item_cost.assign((size_t)n_items, 0.f);
-    // cost of one query tile row (same for every head): inner 64-key steps weighted by tag
+    const size_t nnz = p.col.size();
+    // cost of each entry: its 64-key steps weighted by tag; of a row: the per-item
+    // constant plus its entries (the same for every head)
+    std::vector<double> ecost(nnz);
+    for (size_t e = 0; e < nnz; ++e) {
+        const int64_t c0 = (int64_t)p.col[e] * p.bk;
+        const int64_t keys = std::min<int64_t>(c0 + p.bk, p.sk) - c0;
+        const double steps = (double)((keys + kKernelBk - 1) / kKernelBk);
+        ecost[e] = steps * bsfa_tile_cost(p.tag[e], kCostPartial);
+    }
     std::vector<double> row_cost((size_t)p.n_qt, 0.0);
     for (int32_t qt = 0; qt < p.n_qt; ++qt) {
         double c = kCostItem;
-        for (int32_t e = p.row_ptr[qt]; e < p.row_ptr[(size_t)qt + 1]; ++e) {
-            const int64_t c0 = (int64_t)p.col[e] * p.bk;
-            const int64_t keys = std::min<int64_t>(c0 + p.bk, p.sk) - c0;
-            const double steps = (double)((keys + kKernelBk - 1) / kKernelBk);
-            c += steps * bsfa_tile_cost(p.tag[e], kCostPartial);
-        }
+        for (int32_t e = p.row_ptr[qt]; e < p.row_ptr[(size_t)qt + 1]; ++e) c += ecost[e];
         row_cost[qt] = c;
     }
+    p.item_cost.assign((size_t)n_items, 0.f);
     double total = 0.0;
     for (int32_t h = 0; h < p.hq; ++h)
         for (int32_t qt = 0; qt < p.n_qt; ++qt) {
@@ -82,25 +86,91 @@ void build_schedule(bsfa_plan &p, int n_bins_max)
         }
     p.total_cost = total;
 
-    const int32_t n_bins = std::max(1, std::min(n_items, n_bins_max));
-    std::vector<std::pair<int32_t, int32_t>> assign;   // (bin, item) in assignment order
-    assign.reserve((size_t)n_items);
+    // Rows costlier than the per-bin target are split (UltraAttn 3.2: a row's key range
+    // may be cut anywhere, the parts' summaries merge exactly): parts of contiguous
+    // entries with about equal cost, each of at least kMinPartCost.
+    const double target = std::max(total / std::max(1, n_bins_max), kMinPartCost);
+    std::vector<int32_t> parts((size_t)p.n_qt, 1);
+    std::vector<int32_t> cut_ptr((size_t)p.n_qt + 1, 0);   // into cuts
+    std::vector<int32_t> cuts;                               // entry boundaries per row
+    std::vector<double> part_cost;                           // per (row, part)
+    for (int32_t qt = 0; qt < p.n_qt; ++qt) {
+        const int32_t e0 = p.row_ptr[qt], e1 = p.row_ptr[(size_t)qt + 1];
+        int32_t np = 1;
+        if (row_cost[qt] > target && e1 - e0 >= 2)
+            np = (int32_t)std::min<double>({(double)kMaxParts, (double)(e1 - e0), std::ceil(row_cost[qt] / target)});
+        parts[qt] = np;
+        cut_ptr[(size_t)qt + 1] = cut_ptr[qt] + np;
+        cuts.push_back(e0);
+        const double work = row_cost[qt] - kCostItem;
+        double acc = 0.0;
+        int32_t e = e0;
+        for (int32_t k = 1; k < np; ++k) {
+            // end of part k-1: first entry where the running cost reaches k/np of the
+            // row, leaving at least one entry for each later part
+            const double goal = work * k / np;
+            while (e < e1 - (np - k) && acc + ecost[e] * 0.5 < goal) acc += ecost[e++];
+            if (e == cuts.back()) acc += ecost[e++];
+            cuts.push_back(e);
+        }
+        cuts.push_back(e1);
+    }
+    // cuts holds, per row, np + 1 boundaries: rebase cut_ptr onto that layout
+    {
+        int32_t at = 0;
+        for (int32_t qt = 0; qt < p.n_qt; ++qt) {
+            cut_ptr[qt] = at;
+            at += parts[qt] + 1;
+        }
+        cut_ptr[(size_t)p.n_qt] = at;
+    }
+
+    // units: id = h * units_per_head + row_base[qt] + k; partial slots likewise over the
+    // split rows only
+    std::vector<int32_t> row_base((size_t)p.n_qt + 1, 0), slot_base((size_t)p.n_qt + 1, 0);
+    for (int32_t qt = 0; qt < p.n_qt; ++qt) {
+        row_base[(size_t)qt + 1] = row_base[qt] + parts[qt];
+        slot_base[(size_t)qt + 1] = slot_base[qt] + (parts[qt] > 1 ? parts[qt] : 0);
+    }
+    const int32_t upr = row_base[(size_t)p.n_qt], spr = slot_base[(size_t)p.n_qt];
+    const int32_t n_units = p.hq * upr;
+    p.n_slots = p.hq * spr;
+    p.units.assign((size_t)n_units, Unit{0, 0, 0, -1});
+    p.unit_cost.assign((size_t)n_units, 0.f);
+    p.splits.clear();
+    std::vector<float> rk_cost((size_t)upr);   // cost of (row, part) = of its unit in any head
+    for (int32_t qt = 0; qt < p.n_qt; ++qt)
+        for (int32_t k = 0; k < parts[qt]; ++k) {
+            const int32_t eb = cuts[(size_t)cut_ptr[qt] + k], ee = cuts[(size_t)cut_ptr[qt] + k + 1];
+            double c = kCostItem;
+            for (int32_t e = eb; e < ee; ++e) c += ecost[e];
+            rk_cost[(size_t)row_base[qt] + k] = (float)c;
+        }
+    for (int32_t h = 0; h < p.hq; ++h)
+        for (int32_t qt = 0; qt < p.n_qt; ++qt) {
+            const int32_t item = h * p.n_qt + qt;
+            const int32_t first = parts[qt] > 1 ? h * spr + slot_base[qt] : -1;
+            if (parts[qt] > 1) p.splits.push_back(Split{item, first, parts[qt], 0});
+            for (int32_t k = 0; k < parts[qt]; ++k) {
+                const int32_t u = h * upr + row_base[qt] + k;
+                p.units[(size_t)u] = Unit{item, cuts[(size_t)cut_ptr[qt] + k], cuts[(size_t)cut_ptr[qt] + k + 1],
+                                          first < 0 ? -1 : first + k};
+                p.unit_cost[(size_t)u] = rk_cost[(size_t)row_base[qt] + k];
+            }
+        }
+
+    const int32_t n_bins = std::max(1, std::min(n_units, n_bins_max));
+    std::vector<std::pair<int32_t, int32_t>> assign;   // (bin, unit) in assignment order
+    assign.reserve((size_t)n_units);
     std::vector<double> load((size_t)n_bins, 0.0);
 
     bool placed = false;
     const int32_t group = p.hq / p.hkv;  // query heads per key/value head
     if (n_bins % kNumXcd == 0 && p.hkv >= kNumXcd) {
         // level 1: key/value heads onto XCDs (LPT on head totals)
-        std::vector<double> head_cost((size_t)p.hkv, 0.0);
-        for (int32_t g = 0; g < p.hkv; ++g)
-            for (int32_t h = g * group; h < (g + 1) * group; ++h)
-                for (int32_t qt = 0; qt < p.n_qt; ++qt) head_cost[g] += row_cost[qt];
+        std::vector<double> head_cost((size_t)p.hkv, (double)group * (total / std::max(1, p.hq)));
         std::vector<int32_t> gorder((size_t)p.hkv);
         for (int32_t g = 0; g < p.hkv; ++g) gorder[g] = g;
-        std::sort(gorder.begin(), gorder.end(), [&](int32_t a, int32_t b) {
-            if (head_cost[a] != head_cost[b]) return head_cost[a] > head_cost[b];
-            return a < b;
-        });
         std::vector<double> xload(kNumXcd, 0.0);
         std::vector<std::vector<int32_t>> xheads(kNumXcd);
         for (int32_t g : gorder) {
@@ -114,12 +184,12 @@ void build_schedule(bsfa_plan &p, int n_bins_max)
         const double xavg = total / kNumXcd;
         if (xavg > 0 && xmax / xavg - 1.0 <= 0.03) {
             // level 2: within each XCD, LPT over the bins that XCD runs.  Every head has
-            // the same per-tile costs, so the query tiles are sorted once: items go in
-            // order of decreasing cost, ties by query tile, then head.
-            std::vector<int32_t> qorder((size_t)p.n_qt);
-            for (int32_t qt = 0; qt < p.n_qt; ++qt) qorder[qt] = qt;
-            std::stable_sort(qorder.begin(), qorder.end(),
-                             [&](int32_t x, int32_t y) { return row_cost[x] > row_cost[y]; });
+            // the same (row, part) costs, so those are sorted once: units go in order of
+            // decreasing cost, ties by row and part, then head.
+            std::vector<int32_t> order((size_t)upr);
+            for (int32_t i = 0; i < upr; ++i) order[i] = i;
+            std::stable_sort(order.begin(), order.end(),
+                             [&](int32_t x, int32_t y) { return rk_cost[x] > rk_cost[y]; });
             std::vector<int32_t> items, bins;
             for (int32_t x = 0; x < kNumXcd; ++x) {
                 items.clear();
@@ -128,32 +198,35 @@ void build_schedule(bsfa_plan &p, int n_bins_max)
                 for (int32_t g : xheads[x])
                     for (int32_t h = g * group; h < (g + 1) * group; ++h) heads.push_back(h);
                 std::sort(heads.begin(), heads.end());
-                for (int32_t qt : qorder)
-                    for (int32_t h : heads) items.push_back(h * p.n_qt + qt);
+                for (int32_t r : order)
+                    for (int32_t h : heads) items.push_back(h * upr + r);
                 for (int32_t b = x; b < n_bins; b += kNumXcd) bins.push_back(b);
-                lpt_sorted(items, p.item_cost, bins, assign, load);
+                lpt_sorted(items, p.unit_cost, bins, assign, load);
             }
             placed = true;
         }
     }
     if (!placed) {
-        std::vector<int32_t> items((size_t)n_items), bins((size_t)n_bins);
-        for (int32_t i = 0; i < n_items; ++i) items[i] = i;
+        std::vector<int32_t> items((size_t)n_units), bins((size_t)n_bins);
+        for (int32_t i = 0; i < n_units; ++i) items[i] = i;
         for (int32_t b = 0; b < n_bins; ++b) bins[b] = b;
-        lpt(items, p.item_cost, bins, assign, load);
+        lpt(items, p.unit_cost, bins, assign, load);
     }
 
     // per-bin lists in assignment order (counting sort by bin)
     p.bin_ptr.assign((size_t)n_bins + 1, 0);
     for (const auto &ba : assign) ++p.bin_ptr[(size_t)ba.first + 1];
     for (int32_t b = 0; b < n_bins; ++b) p.bin_ptr[(size_t)b + 1] += p.bin_ptr[b];
-    p.bin_items.assign((size_t)n_items, 0);
+    p.bin_items.assign((size_t)n_units, 0);
     {
         std::vector<int32_t> fill(p.bin_ptr.begin(), p.bin_ptr.end() - 1);
         for (const auto &ba : assign) p.bin_items[(size_t)fill[ba.first]++] = ba.second;
     }
     p.makespan = 0.0;
     for (int32_t b = 0; b < n_bins; ++b) p.makespan = std::max(p.makespan, load[b]);
+    // the cost of split rows includes one per-item constant per part
+    p.total_cost = 0.0;
+    for (float c : p.unit_cost) p.total_cost += c;
 }
 
 }  // namespace bsfa

@@ -80,8 +80,11 @@ typedef struct {
     int32_t n_items;      /* work items = (query head, query tile) */
     int32_t n_bins;       /* persistent workgroups of the forward launch */
     double makespan;      /* largest bin cost of the schedule (cost units) */
-    double total_cost;    /* sum of item costs */
+    double total_cost;    /* sum of unit costs */
     int32_t uploaded;     /* 1 once bsfa_plan_upload has run */
+    int32_t n_units;      /* scheduled units: n_items plus one per extra part of a split row */
+    int32_t n_splits;     /* (query head, query tile) rows split into parts */
+    int64_t workspace_bytes;  /* device bytes for the parts' partial results (0 if no split) */
 } bsfa_plan_info;
 
 /* ---- plans: mask compiler + scheduler (host) --------------------------------
@@ -143,11 +146,20 @@ bsfa_status bsfa_plan_get_info(const bsfa_plan *plan, bsfa_plan_info *info);
 bsfa_status bsfa_plan_export_csr(const bsfa_plan *plan, int32_t *row_ptr, int32_t *col,
                                  uint8_t *tag, int64_t cap, int64_t *nnz);
 
-/* Copy out the schedule: bin_ptr [n_bins + 1], items [n_items] (item = h * n_qtiles
- * + qtile, in execution order within a bin) and item_cost [n_items] (indexed by item
- * id), host memory.  Any pointer may be NULL to skip it. */
-bsfa_status bsfa_plan_export_schedule(const bsfa_plan *plan, int32_t *bin_ptr, int32_t *items,
-                                      float *item_cost);
+/* Copy out the schedule: bin_ptr [n_bins + 1], units [n_units] (unit ids in execution
+ * order within a bin) and unit_cost [n_units] (indexed by unit id), host memory.  Any
+ * pointer may be NULL to skip it.  When no row is split, unit id == item id =
+ * h * n_qtiles + qtile and the unit costs are the item costs. */
+bsfa_status bsfa_plan_export_schedule(const bsfa_plan *plan, int32_t *bin_ptr, int32_t *units,
+                                      float *unit_cost);
+
+/* Copy out the units ([UA] 3.2: a query tile's key range split into parts whose
+ * summaries merge exactly): units [n_units][4] = {item, entry_begin, entry_end, slot}
+ * where [entry_begin, entry_end) indexes the tile CSR's col/tag arrays and slot is -1
+ * for a whole row or the partial-result slot of a part.  A row is split when its cost
+ * exceeds both the per-bin target (total cost / resident workgroups) and 16 steps: into
+ * at most 16 parts of contiguous entries with about equal cost. */
+bsfa_status bsfa_plan_export_units(const bsfa_plan *plan, int32_t *units);
 
 /* Cost of one tile under the scheduler's model ([UA] 4.1: full = 1, causal/partial =
  * w_partial, empty = 0) and the page's imbalance bound ceil(avg)/avg - 1 for a total
@@ -173,6 +185,10 @@ double bsfa_lpt_assign(const float *cost, int32_t n_items, int32_t n_bins, int32
  * Shapes come from the plan, which must be uploaded to the current device.
  * No allocation, no synchronisation; deterministic (no atomics).  The stream is
  * remembered so that bsfa_plan_destroy releases the plan's buffer behind it.
+ * A plan with split rows (info.n_splits > 0) runs a second kernel on the same stream
+ * that merges the parts; their partial results live in a workspace inside the plan's
+ * device buffer, so launches of such a plan must not overlap (order them on one
+ * stream).
  * Errors: BSFA_ERR_ARG, BSFA_ERR_ALIGN, BSFA_ERR_UNSUPPORTED (d not 64/128, bq != 128,
  * bk % 64 != 0), BSFA_ERR_STATE (plan not on this device), BSFA_ERR_HIP. */
 bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,

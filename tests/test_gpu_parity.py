@@ -272,3 +272,30 @@ def test_plan_churn_reuses_buffers_safely():
     torch.cuda.synchronize()
     for i, (m, o, l) in enumerate(outs):
         assert torch.equal(o, ref[m][0]) and torch.equal(l, ref[m][1]), f"plan {i} (mask {m}) differs"
+
+
+# ---------------------------------------------------------------------------
+# rows split into parts inside one call (partials merged by a second kernel)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed,sq,sk,hq,hkv,d,kind", [
+    (31, 256, 12000, 2, 1, 128, "full"),
+    (32, 200, 9000, 2, 2, 64, "causal"),
+    (33, 130, 20000, 1, 1, 128, "gappy"),
+])
+def test_split_rows_full(seed, sq, sk, hq, hkv, d, kind):
+    rng = np.random.default_rng(seed)
+    if kind == "full":
+        slices = [(0, sq, 0, sk, 0)]
+    elif kind == "causal":
+        slices = [(0, sq, 0, sk, 1)]
+    else:
+        # rows 0..64 see only early keys, 70..129 only late keys (causal), 65..69 none:
+        # some parts hold no key of a row, and some rows have no key at all
+        slices = [(0, 65, 0, 3000, 0), (70, 130, 15000, sk, 1)]
+    qb, kb, vb = W.random_inputs(rng, sq, sk, hq, hkv, d)
+    plan = api.Plan.from_slices(slices, sq, sk, hq, hkv, d)
+    inf = plan.info()
+    assert inf["n_splits"] > 0, inf
+    say(f"split rows {kind}: units={inf['n_units']} splits={inf['n_splits']}")
+    plan.close()
+    full_check(qb, kb, vb, slices, 1.0 / np.sqrt(d), f"split rows {kind}")

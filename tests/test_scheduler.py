@@ -51,9 +51,9 @@ def test_lpt_is_deterministic_and_follows_the_greedy_rule():
 def _check_plan_schedule(plan):
     inf = plan.info()
     bin_ptr, items, cost = plan.schedule()
-    assert bin_ptr[0] == 0 and bin_ptr[-1] == inf["n_items"]
+    assert bin_ptr[0] == 0 and bin_ptr[-1] == inf["n_units"]
     assert np.all(np.diff(bin_ptr) >= 0)
-    assert sorted(items.tolist()) == list(range(inf["n_items"]))
+    assert sorted(items.tolist()) == list(range(inf["n_units"]))
     loads = np.array([cost[items[bin_ptr[b]:bin_ptr[b + 1]]].astype(np.float64).sum()
                       for b in range(inf["n_bins"])])
     assert abs(loads.sum() - inf["total_cost"]) < 1e-3 * max(1.0, inf["total_cost"])
@@ -68,6 +68,7 @@ def test_workload_schedules(cfg):
     w = W.CONFIGS[cfg](with_inputs=False)
     plan = api.plan_from_workload(w, upload=False)
     inf, loads = _check_plan_schedule(plan)
+    assert inf["n_splits"] == 0 and inf["n_units"] == inf["n_items"]   # no row needs splitting
     assert inf["n_bins"] == min(inf["n_items"], 512)
     # repeat build: identical schedule
     plan2 = api.plan_from_workload(w, upload=False)
@@ -100,3 +101,63 @@ def test_pages_block_weights_and_imbalance_table():
         assert total / g["n_gpus"] == row["avg"]
         assert int(np.ceil(total / g["n_gpus"])) == row["max"]
         assert round(lib.bsfa_imbalance_bound(total, g["n_gpus"]), 2) == row["imbalance"]
+
+
+# ---------------------------------------------------------------------------
+# in-call KV split: rows costlier than the per-bin target are cut into parts
+# ---------------------------------------------------------------------------
+def _check_units(plan):
+    inf = plan.info()
+    row_ptr, col, tag = plan.csr()
+    units = plan.units()
+    n_qt, hq = inf["n_qtiles"], inf["hq"]
+    assert units.shape == (inf["n_units"], 4)
+    # per item, the parts tile the CSR row in order, each part non-empty
+    by_item = {}
+    for u, (item, eb, ee, slot) in enumerate(units):
+        by_item.setdefault(int(item), []).append((int(eb), int(ee), int(slot)))
+    assert sorted(by_item) == list(range(hq * n_qt))
+    slots = []
+    for item, parts in by_item.items():
+        qt = item % n_qt
+        assert parts[0][0] == row_ptr[qt] and parts[-1][1] == row_ptr[qt + 1]
+        for (a0, a1, _), (b0, _, _) in zip(parts, parts[1:]):
+            assert a1 == b0
+        if len(parts) == 1:
+            assert parts[0][2] == -1
+        else:
+            assert all(p[0] < p[1] for p in parts)
+            assert len(parts) <= 16
+            first = parts[0][2]
+            assert [p[2] for p in parts] == list(range(first, first + len(parts)))
+            slots += [p[2] for p in parts]
+    assert sorted(slots) == list(range(len(slots)))
+    assert inf["n_splits"] == sum(1 for p in by_item.values() if len(p) > 1)
+    assert inf["workspace_bytes"] == len(slots) * 128 * (inf["d"] + 1) * 4
+    return units
+
+
+@pytest.mark.parametrize("sq,sk,hq,causal", [(256, 16384, 2, False), (200, 20000, 1, True),
+                                              (1024, 65536, 8, False)])
+def test_long_rows_are_split_into_balanced_parts(sq, sk, hq, causal):
+    slices = [(0, sq, 0, sk, 1 if causal else 0)]
+    plan = api.Plan.from_slices(slices, sq, sk, hq, hq, 128)
+    inf, loads = _check_plan_schedule(plan)
+    units = _check_units(plan)
+    assert inf["n_splits"] > 0
+    # parts of one row cost about the same (within one entry of 2 steps plus rounding)
+    _, _, cost = plan.schedule()
+    for item in set(units[:, 0].tolist()):
+        c = cost[units[:, 0] == item]
+        if len(c) > 1:
+            assert c.max() - c.min() <= 2 * 1.15 + 1e-4
+    # the split leaves the makespan close to the mean load
+    assert inf["makespan"] <= inf["total_cost"] / inf["n_bins"] + cost.max() + 1e-3
+
+
+def test_short_rows_are_not_split():
+    # every row is below the 16-step floor: no split however few the items
+    plan = api.Plan.from_slices([(0, 256, 0, 256, 1)], 256, 256, 1, 1, 128)
+    inf = plan.info()
+    assert inf["n_splits"] == 0 and inf["workspace_bytes"] == 0
+    _check_units(plan)
