@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for masked attention, the KV-split merge and tile classification.
+"""fp64 CPU oracle for masked attention (forward and gradients), the KV-split merge and
+tile classification.
 
 TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU-baseline
 leg of ``bench.py`` are the only callers.  The product path never imports this
@@ -53,6 +54,13 @@ def _load():
         lib.oracle_attn_fwd.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32,
                                         ctypes.c_double, P, ctypes.c_int64, P, P, ctypes.c_int32]
+        I32, D = ctypes.c_int32, ctypes.c_double
+        lib.oracle_attn_fwd_f64.restype = I32
+        lib.oracle_attn_fwd_f64.argtypes = [P, P, P, I32, I32, I32, I32, I32, P, I32, D, P, P, I32]
+        lib.oracle_attn_bwd.restype = I32
+        lib.oracle_attn_bwd.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P, I32, D, P, P, P, I32]
+        lib.oracle_attn_bwd_f64.restype = I32
+        lib.oracle_attn_bwd_f64.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P, I32, D, P, P, P]
         lib.oracle_merge.restype = None
         lib.oracle_merge.argtypes = [P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P, P]
         _lib = lib
@@ -130,6 +138,57 @@ def attn_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, slices,
     if rc != 0:
         raise ValueError("oracle_attn_fwd: bad head counts")
     return o, lse
+
+
+def attn_fwd_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, slices, scale: float, n_threads: int = 1):
+    """The same fp64 forward on fp64 inputs q [sq, hq, d], k/v [sk, hkv, d] -> (O, LSE [hq, sq])."""
+    q, k, v = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v))
+    sq, hq, d = q.shape
+    sk, hkv, _ = k.shape
+    o = np.zeros((sq, hq, d), np.float64)
+    lse = np.zeros((hq, sq), np.float64)
+    rc = _load().oracle_attn_fwd_f64(_ptr(q), _ptr(k), _ptr(v), sq, sk, hq, hkv, d, _slices(slices),
+                                     len(slices), float(scale), _ptr(o), _ptr(lse), int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_attn_fwd_f64: bad head counts")
+    return o, lse
+
+
+def attn_bwd(q_bits, k_bits, v_bits, do_bits, slices, scale: float, n_threads: int | None = None):
+    """fp64 gradients (dQ [sq, hq, d], dK [sk, hkv, d], dV [sk, hkv, d]) of the forward for
+    an upstream gradient dO [sq, hq, d]; all inputs bf16 bit patterns (uint16)."""
+    q_bits, k_bits, v_bits, do_bits = (np.ascontiguousarray(x, dtype=np.uint16)
+                                       for x in (q_bits, k_bits, v_bits, do_bits))
+    sq, hq, d = q_bits.shape
+    sk, hkv, _ = k_bits.shape
+    assert do_bits.shape == q_bits.shape and v_bits.shape == k_bits.shape
+    dq = np.zeros((sq, hq, d), np.float64)
+    dk = np.zeros((sk, hkv, d), np.float64)
+    dv = np.zeros((sk, hkv, d), np.float64)
+    if n_threads is None:
+        n_threads = os.cpu_count() or 1
+    rc = _load().oracle_attn_bwd(_ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(do_bits), sq, sk, hq, hkv,
+                                 d, _slices(slices), len(slices), float(scale), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_attn_bwd: bad head counts")
+    return dq, dk, dv
+
+
+def attn_bwd_f64(q, k, v, do, slices, scale: float):
+    """attn_bwd on fp64 inputs (for finite-difference checks)."""
+    q, k, v, do = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, do))
+    sq, hq, d = q.shape
+    sk, hkv, _ = k.shape
+    dq = np.zeros((sq, hq, d), np.float64)
+    dk = np.zeros((sk, hkv, d), np.float64)
+    dv = np.zeros((sk, hkv, d), np.float64)
+    rc = _load().oracle_attn_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(do), sq, sk, hq, hkv, d,
+                                     _slices(slices), len(slices), float(scale), _ptr(dq), _ptr(dk),
+                                     _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle_attn_bwd_f64: bad head counts")
+    return dq, dk, dv
 
 
 def merge(o_parts: np.ndarray, lse_parts: np.ndarray):

@@ -1,6 +1,6 @@
 /*
- * oracle.c -- plain fp64 CPU reference for masked attention, the KV-split merge
- * and the tile classification of a mask.
+ * oracle.c -- plain fp64 CPU reference for masked attention (forward and its
+ * gradients), the KV-split merge and the tile classification of a mask.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
  * leg of the benchmark may load this library.  It shares no source with the GPU
@@ -17,6 +17,9 @@
  *   [FT]  FlashAttention-T post, FlashAttention lineage paragraph (tiling with an
  *         incremental softmax gives the exact softmax, so the plain two-pass
  *         softmax below is the definition the tiled kernel must reproduce).
+ *   [MA2] MagiAttention v1.1.0 news: the kernels cover the forward and the backward
+ *         pass of the same masked attention; the backward below is the plain
+ *         derivative of the forward written out (chain rule through the softmax).
  *
  * Readings taken where the pages are silent (each is listed in the design notes):
  *   - overlapping slices: the mask is the union of the slices' pair sets;
@@ -38,6 +41,13 @@
 typedef struct {
     int32_t q0, q1, k0, k1, type; /* type 0 = full, 1 = causal */
 } oracle_slice;
+
+/* Input element idx of an array that holds bf16 bit patterns (bf16 != 0) or doubles. */
+static double bf16_to_double(uint16_t b);
+static inline double ld(const void *p, size_t idx, int bf16)
+{
+    return bf16 ? bf16_to_double(((const uint16_t *)p)[idx]) : ((const double *)p)[idx];
+}
 
 /* bf16 -> fp64, exact: a bf16 is the top half of an IEEE binary32. */
 static double bf16_to_double(uint16_t b)
@@ -190,7 +200,8 @@ int32_t oracle_tile_csr(const oracle_slice *s, int32_t n_slices, int32_t sq, int
  * [n_rows, d] and lse [n_rows].
  * --------------------------------------------------------------------------- */
 typedef struct {
-    const uint16_t *q, *k, *v;
+    const void *q, *k, *v;
+    int bf16;   /* inputs are bf16 bit patterns (else doubles) */
     int32_t sq, sk, hq, hkv, d;
     const oracle_slice *s;
     int32_t n_slices;
@@ -217,16 +228,16 @@ static void attn_one_row(const attn_job *J, int64_t h, int64_t i, double *o_row,
         *lse_out = -INFINITY;
         return;
     }
-    const uint16_t *qi = J->q + ((size_t)i * J->hq + (size_t)h) * d;
+    const size_t qi = ((size_t)i * J->hq + (size_t)h) * d;
     /* pass 1: scores and their maximum */
     double mx = -INFINITY;
     int64_t c = 0;
     for (int t = 0; t < m; ++t) {
         int64_t lo = ivs[t].lo < 0 ? 0 : ivs[t].lo, hi = ivs[t].hi > J->sk ? J->sk : ivs[t].hi;
         for (int64_t j = lo; j < hi; ++j) {
-            const uint16_t *kj = J->k + ((size_t)j * J->hkv + (size_t)g) * d;
+            const size_t kj = ((size_t)j * J->hkv + (size_t)g) * d;
             double acc = 0.0;
-            for (int e = 0; e < d; ++e) acc += bf16_to_double(qi[e]) * bf16_to_double(kj[e]);
+            for (int e = 0; e < d; ++e) acc += ld(J->q, qi + e, J->bf16) * ld(J->k, kj + e, J->bf16);
             scores[c] = J->scale * acc;
             if (scores[c] > mx) mx = scores[c];
             ++c;
@@ -241,8 +252,8 @@ static void attn_one_row(const attn_job *J, int64_t h, int64_t i, double *o_row,
         int64_t lo = ivs[t].lo < 0 ? 0 : ivs[t].lo, hi = ivs[t].hi > J->sk ? J->sk : ivs[t].hi;
         for (int64_t j = lo; j < hi; ++j) {
             const double p = exp(scores[c] - lse);
-            const uint16_t *vj = J->v + ((size_t)j * J->hkv + (size_t)g) * d;
-            for (int e = 0; e < d; ++e) o_row[e] += p * bf16_to_double(vj[e]);
+            const size_t vj = ((size_t)j * J->hkv + (size_t)g) * d;
+            for (int e = 0; e < d; ++e) o_row[e] += p * ld(J->v, vj + e, J->bf16);
             ++c;
         }
     }
@@ -276,10 +287,10 @@ static void *attn_worker(void *arg)
     return NULL;
 }
 
-int32_t oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int32_t sq,
-                        int32_t sk, int32_t hq, int32_t hkv, int32_t d, const oracle_slice *slices,
-                        int32_t n_slices, double scale, const int64_t *rows, int64_t n_rows,
-                        double *o, double *lse, int32_t n_threads)
+static int32_t attn_fwd_any(const void *q, const void *k, const void *v, int bf16, int32_t sq, int32_t sk,
+                            int32_t hq, int32_t hkv, int32_t d, const oracle_slice *slices, int32_t n_slices,
+                            double scale, const int64_t *rows, int64_t n_rows, double *o, double *lse,
+                            int32_t n_threads)
 {
     if (hkv <= 0 || hq % hkv != 0 || d <= 0) return -1;
     if (n_threads < 1) n_threads = 1;
@@ -287,7 +298,7 @@ int32_t oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     pthread_t th[256];
     attn_job jobs[256];
     for (int t = 0; t < n_threads; ++t) {
-        attn_job J = {q, k, v, sq, sk, hq, hkv, d, slices, n_slices, scale, rows, n_rows, o, lse,
+        attn_job J = {q, k, v, bf16, sq, sk, hq, hkv, d, slices, n_slices, scale, rows, n_rows, o, lse,
                       n_threads, t};
         jobs[t] = J;
     }
@@ -295,6 +306,148 @@ int32_t oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     attn_worker(&jobs[0]);
     for (int t = 1; t < n_threads; ++t) pthread_join(th[t], NULL);
     return 0;
+}
+
+/* Inputs as bf16 bit patterns (the kernels' inputs, decoded exactly). */
+int32_t oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, int32_t sq,
+                        int32_t sk, int32_t hq, int32_t hkv, int32_t d, const oracle_slice *slices,
+                        int32_t n_slices, double scale, const int64_t *rows, int64_t n_rows,
+                        double *o, double *lse, int32_t n_threads)
+{
+    return attn_fwd_any(q, k, v, 1, sq, sk, hq, hkv, d, slices, n_slices, scale, rows, n_rows, o, lse,
+                        n_threads);
+}
+
+/* Inputs as doubles (finite-difference checks of the backward perturb them). */
+int32_t oracle_attn_fwd_f64(const double *q, const double *k, const double *v, int32_t sq, int32_t sk,
+                            int32_t hq, int32_t hkv, int32_t d, const oracle_slice *slices,
+                            int32_t n_slices, double scale, double *o, double *lse, int32_t n_threads)
+{
+    return attn_fwd_any(q, k, v, 0, sq, sk, hq, hkv, d, slices, n_slices, scale, NULL, 0, o, lse,
+                        n_threads);
+}
+
+/* ---------------------------------------------------------------------------
+ * Attention backward ([MA2]: gradients of the same masked attention), plain
+ * fp64: the derivative of the forward above, term by term.  With
+ * P_ij = exp(s_ij - LSE_i) for j in U(i) (0 elsewhere) and O_i = sum_j P_ij v_j,
+ * an upstream gradient dO gives
+ *   D_i   = sum_t dO_it O_it                  (= sum_j P_ij dP_ij)
+ *   dP_ij = dO_i . v_j
+ *   dS_ij = P_ij (dP_ij - D_i)                 (softmax Jacobian)
+ *   dQ_i  = scale sum_j dS_ij k_j
+ *   dK_j  = scale sum_(h in group) sum_i dS_ij q_i
+ *   dV_j  = sum_(h in group) sum_i P_ij dO_i
+ * where O and LSE are recomputed here in fp64 (not taken from a kernel).
+ * Layouts as the forward; dq [sq, hq, d], dk and dv [sk, hkv, d] fp64, zeroed
+ * here.  Threads take key/value head groups, so dk/dv rows have one writer.
+ * --------------------------------------------------------------------------- */
+typedef struct {
+    const void *q, *k, *v, *dout;
+    int bf16;
+    int32_t sq, sk, hq, hkv, d;
+    const oracle_slice *s;
+    int32_t n_slices;
+    double scale;
+    double *dq, *dk, *dv;
+    int32_t n_threads, tid;
+} bwd_job;
+
+static void *bwd_worker(void *arg)
+{
+    const bwd_job *J = (const bwd_job *)arg;
+    const int d = J->d, group = J->hq / J->hkv;
+    interval *ivs = (interval *)malloc(sizeof(interval) * (size_t)(J->n_slices > 0 ? J->n_slices : 1));
+    double *scores = (double *)malloc(sizeof(double) * (size_t)(J->sk > 0 ? J->sk : 1));
+    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)(J->sk > 0 ? J->sk : 1));
+    double *o_row = (double *)malloc(sizeof(double) * (size_t)d);
+    for (int64_t g = J->tid; g < J->hkv; g += J->n_threads) {
+        for (int64_t h = g * group; h < (g + 1) * group; ++h) {
+            for (int64_t i = 0; i < J->sq; ++i) {
+                const int m = row_key_set(J->s, J->n_slices, i, ivs);
+                int64_t n_keys = 0;
+                for (int t = 0; t < m; ++t) {
+                    int64_t lo = ivs[t].lo < 0 ? 0 : ivs[t].lo, hi = ivs[t].hi > J->sk ? J->sk : ivs[t].hi;
+                    for (int64_t j = lo; j < hi; ++j) keys[n_keys++] = j;
+                }
+                if (n_keys == 0) continue;   /* no admitted key: every gradient term is 0 */
+                const size_t qi = ((size_t)i * J->hq + (size_t)h) * d;
+                double mx = -INFINITY;
+                for (int64_t c = 0; c < n_keys; ++c) {
+                    const size_t kj = ((size_t)keys[c] * J->hkv + (size_t)g) * d;
+                    double acc = 0.0;
+                    for (int e = 0; e < d; ++e) acc += ld(J->q, qi + e, J->bf16) * ld(J->k, kj + e, J->bf16);
+                    scores[c] = J->scale * acc;
+                    if (scores[c] > mx) mx = scores[c];
+                }
+                double sum = 0.0;
+                for (int64_t c = 0; c < n_keys; ++c) sum += exp(scores[c] - mx);
+                const double lse = mx + log(sum);
+                /* P (in place of the scores), O and D */
+                for (int e = 0; e < d; ++e) o_row[e] = 0.0;
+                for (int64_t c = 0; c < n_keys; ++c) {
+                    scores[c] = exp(scores[c] - lse);
+                    const size_t vj = ((size_t)keys[c] * J->hkv + (size_t)g) * d;
+                    for (int e = 0; e < d; ++e) o_row[e] += scores[c] * ld(J->v, vj + e, J->bf16);
+                }
+                double D = 0.0;
+                for (int e = 0; e < d; ++e) D += ld(J->dout, qi + e, J->bf16) * o_row[e];
+                for (int64_t c = 0; c < n_keys; ++c) {
+                    const size_t kv = ((size_t)keys[c] * J->hkv + (size_t)g) * d;
+                    double dp = 0.0;
+                    for (int e = 0; e < d; ++e) dp += ld(J->dout, qi + e, J->bf16) * ld(J->v, kv + e, J->bf16);
+                    const double p = scores[c], ds = p * (dp - D);
+                    for (int e = 0; e < d; ++e) {
+                        J->dq[qi + e] += J->scale * ds * ld(J->k, kv + e, J->bf16);
+                        J->dk[kv + e] += J->scale * ds * ld(J->q, qi + e, J->bf16);
+                        J->dv[kv + e] += p * ld(J->dout, qi + e, J->bf16);
+                    }
+                }
+            }
+        }
+    }
+    free(o_row);
+    free(keys);
+    free(scores);
+    free(ivs);
+    return NULL;
+}
+
+static int32_t attn_bwd_any(const void *q, const void *k, const void *v, const void *dout, int bf16, int32_t sq,
+                            int32_t sk, int32_t hq, int32_t hkv, int32_t d, const oracle_slice *slices,
+                            int32_t n_slices, double scale, double *dq, double *dk, double *dv, int32_t n_threads)
+{
+    if (hkv <= 0 || hq % hkv != 0 || d <= 0) return -1;
+    memset(dq, 0, sizeof(double) * (size_t)sq * hq * d);
+    memset(dk, 0, sizeof(double) * (size_t)sk * hkv * d);
+    memset(dv, 0, sizeof(double) * (size_t)sk * hkv * d);
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > hkv) n_threads = hkv;
+    if (n_threads > 256) n_threads = 256;
+    pthread_t th[256];
+    bwd_job jobs[256];
+    for (int t = 0; t < n_threads; ++t) {
+        bwd_job J = {q, k, v, dout, bf16, sq, sk, hq, hkv, d, slices, n_slices, scale, dq, dk, dv, n_threads, t};
+        jobs[t] = J;
+    }
+    for (int t = 1; t < n_threads; ++t) pthread_create(&th[t], NULL, bwd_worker, &jobs[t]);
+    bwd_worker(&jobs[0]);
+    for (int t = 1; t < n_threads; ++t) pthread_join(th[t], NULL);
+    return 0;
+}
+
+int32_t oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                        int32_t sq, int32_t sk, int32_t hq, int32_t hkv, int32_t d, const oracle_slice *slices,
+                        int32_t n_slices, double scale, double *dq, double *dk, double *dv, int32_t n_threads)
+{
+    return attn_bwd_any(q, k, v, dout, 1, sq, sk, hq, hkv, d, slices, n_slices, scale, dq, dk, dv, n_threads);
+}
+
+int32_t oracle_attn_bwd_f64(const double *q, const double *k, const double *v, const double *dout, int32_t sq,
+                            int32_t sk, int32_t hq, int32_t hkv, int32_t d, const oracle_slice *slices,
+                            int32_t n_slices, double scale, double *dq, double *dk, double *dv)
+{
+    return attn_bwd_any(q, k, v, dout, 0, sq, sk, hq, hkv, d, slices, n_slices, scale, dq, dk, dv, 1);
 }
 
 /* ---------------------------------------------------------------------------
