@@ -85,11 +85,14 @@ def library():
                                                                  ctypes.POINTER(Tensor), P, I64, P]
     lib.bsfa_attn_merge.argtypes = [P, P, I32, I64, I64, I64, I32, I32, I32,
                                     ctypes.POINTER(Tensor), P, P]
+    lib.bsfa_attn_bwd.argtypes = [ctypes.POINTER(Tensor)] * 5 + [P, I64, P, ctypes.c_float,
+                                                                 P, P, P, P, P]
     lib.bsfa_status_str.argtypes = [I32]
     lib.bsfa_status_str.restype = ctypes.c_char_p
     for name in ("bsfa_plan_create", "bsfa_plan_from_varlen", "bsfa_plan_from_blocks",
                  "bsfa_plan_upload", "bsfa_plan_get_info", "bsfa_plan_export_csr",
-                 "bsfa_plan_export_schedule", "bsfa_attn_fwd", "bsfa_attn_merge"):
+                 "bsfa_plan_export_schedule", "bsfa_plan_export_units", "bsfa_attn_fwd",
+                 "bsfa_attn_merge", "bsfa_attn_bwd"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -249,6 +252,46 @@ def attn_fwd(q, k, v, plan: Plan, scale: float, out=None, lse=None, stream=None)
         ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), plan.handle, float(scale),
         ctypes.byref(to), ctypes.c_void_p(lse.data_ptr()), lse.stride(0), _stream_handle(stream)))
     return out, lse
+
+
+def attn_bwd(q, k, v, out, dout, lse, plan: Plan, scale: float, dq=None, dk=None, dv=None,
+             delta=None, stream=None):
+    """Gradients of the plan's masked attention.  q/out/dout [sq, hq, d], k/v [sk, hkv, d]
+    bf16; lse [hq, >= sq] fp32 from the forward.
+
+    Returns (dQ [sq, hq, d], dK [sk, hkv, d], dV [sk, hkv, d]) fp32; delta (rowsum of
+    dout * out, shaped like lse) is scratch the call fills."""
+    import torch
+    sq, hq, d = q.shape
+    psq, psk, phq, phkv, pd = plan.shapes()
+    if (sq, hq, d) != (psq, phq, pd):
+        raise ValueError(f"q shape {tuple(q.shape)} does not match the plan ({psq}, {phq}, {pd})")
+    for name, t, shp in (("k", k, (psk, phkv, pd)), ("v", v, (psk, phkv, pd)),
+                         ("out", out, (psq, phq, pd)), ("dout", dout, (psq, phq, pd))):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} shape {tuple(t.shape)} does not match the plan {shp}")
+        assert t.dtype == torch.bfloat16, f"{name} must be bf16"
+    assert q.dtype == torch.bfloat16
+    assert lse.dtype == torch.float32 and lse.stride(1) == 1 and lse.shape[0] == hq
+    dev = q.device
+    if dq is None:
+        dq = torch.empty((sq, hq, d), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty((psk, phkv, d), dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty((psk, phkv, d), dtype=torch.float32, device=dev)
+    if delta is None:
+        delta = torch.empty_like(lse)
+    for name, t, shp in (("dq", dq, (sq, hq, d)), ("dk", dk, (psk, phkv, d)), ("dv", dv, (psk, phkv, d))):
+        assert t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shp, name
+    assert delta.dtype == torch.float32 and delta.stride() == lse.stride() and delta.shape == lse.shape
+    tq, tk, tv, to, tg = _tview(q), _tview(k), _tview(v), _tview(out), _tview(dout)
+    _check("bsfa_attn_bwd", library().bsfa_attn_bwd(
+        ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(to), ctypes.byref(tg),
+        ctypes.c_void_p(lse.data_ptr()), lse.stride(0), plan.handle, float(scale),
+        ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()),
+        ctypes.c_void_p(delta.data_ptr()), _stream_handle(stream)))
+    return dq, dk, dv
 
 
 def attn_merge(o_parts, lse_parts, out=None, lse=None, stream=None):

@@ -68,6 +68,8 @@ struct DeviceMeta {
     const Split *splits = nullptr;
     float *ws = nullptr;                  // partial results of split rows: per slot
                                           // O [128][d] then LSE [128], fp32
+    const int32_t *t_ptr = nullptr;       // transposed CSR: per key tile [n_kt + 1]
+    const int32_t *t_list = nullptr;      // (query tile, entry) pairs, ascending query tile
 };
 
 }  // namespace bsfa
@@ -82,6 +84,9 @@ struct bsfa_plan {
     std::vector<int32_t> piece_ptr;    // [nnz + 1]; empty range for full tiles
     std::vector<bsfa::Piece> pieces;
     int64_t n_full = 0, n_partial = 0, pairs = 0;
+    // the same CSR by key-tile column: t_ptr [n_kt + 1], t_list [2 * nnz] = (qt, entry)
+    std::vector<int32_t> t_ptr;
+    std::vector<int32_t> t_list;
     // schedule
     std::vector<float> item_cost;      // by item id = h * n_qt + qt
     std::vector<bsfa::Unit> units;     // by unit id; unit id == item id when no row is split
@@ -106,6 +111,8 @@ namespace bsfa {
 
 // Mask compiler: validated slices -> tile CSR with pieces and the pair count.
 bsfa_status compile_mask(const bsfa_slice *slices, int32_t n_slices, bsfa_plan &p);
+// Column view of the tile CSR (for the key/value gradients).
+void build_transpose(bsfa_plan &p);
 // Scheduler: items, costs and the per-bin lists.
 void build_schedule(bsfa_plan &p, int n_bins_max);
 // Min-heap greedy (LPT) of the given items onto the given bins; appends (bin, item)
@@ -138,6 +145,21 @@ struct SplitMergeArgs {
     int32_t o_st, o_sh, lse_sh;
 };
 hipError_t launch_split_merge(const SplitMergeArgs &a, int d, hipStream_t stream);
+
+// Backward: delta = rowsum(dO * O); dQ per query tile over its CSR row; dK, dV per
+// key tile over its CSR column and the query heads of its key/value head.
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    float *delta;
+    float *dq, *dk, *dv;                 // fp32, contiguous [tokens, heads, d]
+    int32_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh, do_st, do_sh, lse_sh;
+    int32_t sq, sk, hq, hkv, n_qt, n_kt, bk_plan;
+    float scale, c;                      // c = scale * log2(e)
+    DeviceMeta meta;
+    int32_t n_entries, n_pieces;
+};
+hipError_t launch_attn_bwd(const BwdArgs &a, int d, hipStream_t stream);
 
 struct MergeArgs {
     const void *o_parts[BSFA_MERGE_MAX_PARTS];

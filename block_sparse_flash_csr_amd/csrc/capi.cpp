@@ -54,6 +54,7 @@ bsfa_status build_plan(const bsfa_slice *slices, int32_t n_slices, int32_t sq, i
     st = compile_mask(slices, n_slices, *p);
     if (st == BSFA_OK) {
         try {
+            build_transpose(*p);
             build_schedule(*p, kNumCu * kBinsPerCu);
         } catch (const std::bad_alloc &) {
             st = BSFA_ERR_OOM;
@@ -320,6 +321,8 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     const size_t o_bi = place<int32_t>(off, p->bin_items.size());
     const size_t o_un = place<Unit>(off, p->units.size());
     const size_t o_sp = place<Split>(off, p->splits.size());
+    const size_t o_tp = place<int32_t>(off, p->t_ptr.size());
+    const size_t o_tl = place<int32_t>(off, p->t_list.size());
     const size_t bytes = (off + 255) & ~size_t(255);
     const size_t ws_bytes = workspace_bytes(*p);
 
@@ -339,6 +342,8 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
         std::memcpy(h + o_bi, p->bin_items.data(), p->bin_items.size() * sizeof(int32_t));
     if (!p->units.empty()) std::memcpy(h + o_un, p->units.data(), p->units.size() * sizeof(Unit));
     if (!p->splits.empty()) std::memcpy(h + o_sp, p->splits.data(), p->splits.size() * sizeof(Split));
+    std::memcpy(h + o_tp, p->t_ptr.data(), p->t_ptr.size() * sizeof(int32_t));
+    if (!p->t_list.empty()) std::memcpy(h + o_tl, p->t_list.data(), p->t_list.size() * sizeof(int32_t));
 
     DevSlot *slot = nullptr;
     st = dev_acquire(dev, bytes + ws_bytes, &slot);
@@ -373,6 +378,8 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     p->dev.units = (const Unit *)(base + o_un);
     p->dev.splits = (const Split *)(base + o_sp);
     p->dev.ws = ws_bytes ? (float *)(base + bytes) : nullptr;
+    p->dev.t_ptr = (const int32_t *)(base + o_tp);
+    p->dev.t_list = (const int32_t *)(base + o_tl);
     p->dbuf = d;
     p->slot = slot;
     p->device = dev;
@@ -545,6 +552,82 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
         m.lse_sh = a.lse_sh;
         if (launch_split_merge(m, p->d, s) != hipSuccess) return BSFA_ERR_HIP;
     }
+    return BSFA_OK;
+}
+
+bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
+                          const bsfa_tensor *o, const bsfa_tensor *dout, const float *lse,
+                          int64_t lse_stride_head, const bsfa_plan *p, float scale, float *dq, float *dk,
+                          float *dv, float *delta, void *stream)
+{
+    if (!q || !k || !v || !o || !dout || !p || !lse || !delta) return BSFA_ERR_ARG;
+    if (!(scale > 0.f) || !std::isfinite(scale)) return BSFA_ERR_ARG;
+    if (p->d != 64 && p->d != 128) return BSFA_ERR_UNSUPPORTED;
+    if (p->bq != kKernelBq || p->bk != 2 * kKernelBk) return BSFA_ERR_UNSUPPORTED;
+    if (!p->dbuf) return BSFA_ERR_STATE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BSFA_ERR_HIP;
+    if (dev != p->device) return BSFA_ERR_STATE;
+    if (lse_stride_head < p->sq || lse_stride_head > INT32_MAX) return BSFA_ERR_ARG;
+    if ((p->sq > 0 && !dq) || (p->sk > 0 && (!dk || !dv))) return BSFA_ERR_ARG;
+    const int32_t n_tok[5] = {p->sq, p->sk, p->sk, p->sq, p->sq};
+    const int32_t n_head[5] = {p->hq, p->hkv, p->hkv, p->hq, p->hq};
+    const bsfa_tensor *ts[5] = {q, k, v, o, dout};
+    for (int t = 0; t < 5; ++t) {
+        if (n_tok[t] > 0 && !ts[t]->ptr) return BSFA_ERR_ARG;
+        if (ts[t]->ptr && !aligned16(ts[t]->ptr)) return BSFA_ERR_ALIGN;
+        if (!stride_ok(ts[t]->stride_tok) || !stride_ok(ts[t]->stride_head)) return BSFA_ERR_ALIGN;
+        if (n_tok[t] > 1 && ts[t]->stride_tok < p->d) return BSFA_ERR_SHAPE;
+        if (n_head[t] > 1 && ts[t]->stride_head < p->d) return BSFA_ERR_SHAPE;
+        if (ts[t]->stride_tok > (1 << 24) || ts[t]->stride_head > INT32_MAX) return BSFA_ERR_UNSUPPORTED;
+    }
+    if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(delta)) return BSFA_ERR_ALIGN;
+    BwdArgs a{};
+    a.q = q->ptr;
+    a.k = k->ptr;
+    a.v = v->ptr;
+    a.o = o->ptr;
+    a.dout = dout->ptr;
+    a.lse = lse;
+    a.delta = delta;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.q_st = (int32_t)q->stride_tok;
+    a.q_sh = (int32_t)q->stride_head;
+    a.k_st = (int32_t)k->stride_tok;
+    a.k_sh = (int32_t)k->stride_head;
+    a.v_st = (int32_t)v->stride_tok;
+    a.v_sh = (int32_t)v->stride_head;
+    a.o_st = (int32_t)o->stride_tok;
+    a.o_sh = (int32_t)o->stride_head;
+    a.do_st = (int32_t)dout->stride_tok;
+    a.do_sh = (int32_t)dout->stride_head;
+    a.lse_sh = (int32_t)lse_stride_head;
+    a.sq = p->sq;
+    a.sk = p->sk;
+    a.hq = p->hq;
+    a.hkv = p->hkv;
+    a.n_qt = p->n_qt;
+    a.n_kt = p->n_kt;
+    a.bk_plan = p->bk;
+    a.scale = scale;
+    a.c = scale * 1.4426950408889634f;
+    a.meta = p->dev;
+    a.n_entries = (int32_t)p->col.size();
+    a.n_pieces = (int32_t)p->pieces.size();
+    const hipStream_t s = (hipStream_t)stream;
+    if (s != p->ustream) {
+        std::lock_guard<std::mutex> lk(p->streams_mu);
+        if (std::find(p->used_streams.begin(), p->used_streams.end(), s) == p->used_streams.end()) {
+            try {
+                p->used_streams.push_back(s);
+            } catch (const std::bad_alloc &) {
+                return BSFA_ERR_OOM;
+            }
+        }
+    }
+    if (launch_attn_bwd(a, p->d, s) != hipSuccess) return BSFA_ERR_HIP;
     return BSFA_OK;
 }
 

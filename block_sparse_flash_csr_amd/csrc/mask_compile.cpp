@@ -198,4 +198,21 @@ bsfa_status compile_mask(const bsfa_slice *slices, int32_t n_slices, bsfa_plan &
     return BSFA_OK;
 }
 
+void build_transpose(bsfa_plan &p)
+{
+    // counting sort of the entries by column; rows are visited in order, so every
+    // column's list comes out by ascending query tile
+    p.t_ptr.assign((size_t)p.n_kt + 1, 0);
+    for (int32_t c : p.col) ++p.t_ptr[(size_t)c + 1];
+    for (int32_t kt = 0; kt < p.n_kt; ++kt) p.t_ptr[(size_t)kt + 1] += p.t_ptr[kt];
+    p.t_list.assign(2 * p.col.size(), 0);
+    std::vector<int32_t> fill(p.t_ptr.begin(), p.t_ptr.end() - 1);
+    for (int32_t qt = 0; qt < p.n_qt; ++qt)
+        for (int32_t e = p.row_ptr[qt]; e < p.row_ptr[(size_t)qt + 1]; ++e) {
+            const int32_t at = fill[p.col[e]]++;
+            p.t_list[2 * (size_t)at] = qt;
+            p.t_list[2 * (size_t)at + 1] = e;
+        }
+}
+
 }  // namespace bsfa

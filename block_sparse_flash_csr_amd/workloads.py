@@ -228,3 +228,8 @@ def random_slices(rng, sq: int, sk: int, n: int, allow_empty: bool = True) -> li
 
 def random_inputs(rng, sq: int, sk: int, hq: int, hkv: int, d: int):
     return _draw_qkv(rng, sq, sk, hq, hkv, d)
+
+
+def random_grad(rng, sq: int, hq: int, d: int):
+    """Upstream gradient dO [sq, hq, d]: standard normal, as bf16 bit patterns."""
+    return bf16_bits(rng.standard_normal((sq, hq, d), dtype=np.float32))

@@ -195,6 +195,27 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
                           const bsfa_plan *plan, float scale, bsfa_tensor *o, float *lse,
                           int64_t lse_stride_head, void *stream);
 
+/* ---- backward ([MA] the same masked attention, forward and backward) ----------
+ * Gradients of the forward above for an upstream gradient dO:
+ *   P_ij = exp(scale q_i.k_j - LSE_i) on the plan's admitted pairs (0 elsewhere),
+ *   D_i = sum_e dO_ie O_ie,  dS_ij = P_ij (dO_i.v_j - D_i),
+ *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_(h,i) dS_ij q_i,
+ *   dV_j = sum_(h,i) P_ij dO_i  (h over the query heads of j's key/value head).
+ * q, o, dout: bf16 [sq, hq, d]; k, v: bf16 [sk, hkv, d] (strides as bsfa_attn_fwd);
+ * lse: the forward's fp32 LSE [hq, lse_stride_head].  dq [sq, hq, d], dk and dv
+ * [sk, hkv, d]: fp32, contiguous, 16-byte aligned, fully written (rows no key reaches
+ * get zeros).  delta: caller scratch of LSE's shape (fp32 [hq, lse_stride_head]),
+ * overwritten with D.  The plan must have bq = 128 and bk = 128 and be uploaded to the
+ * current device.  Three kernels on stream: D, dQ (by query tile), dK/dV (by key tile
+ * over the query heads of its key/value head: no atomics, deterministic).  No
+ * allocation, no synchronisation.
+ * Errors: BSFA_ERR_ARG, BSFA_ERR_ALIGN, BSFA_ERR_SHAPE, BSFA_ERR_UNSUPPORTED (d not 64/
+ * 128, tiles not 128 x 128), BSFA_ERR_STATE, BSFA_ERR_HIP. */
+bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
+                          const bsfa_tensor *o, const bsfa_tensor *dout, const float *lse,
+                          int64_t lse_stride_head, const bsfa_plan *plan, float scale, float *dq,
+                          float *dk, float *dv, float *delta, void *stream);
+
 /* ---- merge of KV-split partials ([UA] 3.2) -----------------------------------
  * For n partial results (O_t, LSE_t) of the same queries over disjoint key sets:
  *   M = max_t LSE_t, LSE = M + ln sum_t exp(LSE_t - M), O = sum_t exp(LSE_t - LSE) O_t;

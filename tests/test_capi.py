@@ -125,3 +125,24 @@ def test_merge_rejects_bad_arguments():
                                ctypes.c_void_p(16), None) == 3
     assert lib.bsfa_attn_merge(ptrs, lptr, 2, 1024, 128, 10, 64, 8, 128, ctypes.byref(t),
                                ctypes.c_void_p(16), None) == 1
+
+
+def test_backward_rejects_bad_arguments():
+    """Checks of the gradient entry that fail before any HIP call."""
+    lib = api.library()
+    t = api.Tensor(ctypes.c_void_p(16), 8, 8)
+    buf = ctypes.c_void_p(16)
+    tp = [ctypes.byref(t)] * 5
+
+    def call(plan, scale=0.1, lse=buf, dq=buf, delta=buf):
+        return lib.bsfa_attn_bwd(*tp, lse, 64, plan.handle, scale, dq, buf, buf, delta, None)
+
+    p = api.Plan.from_slices([(0, 64, 0, 64, 1)], 64, 64, 1, 1, 128, bq=64, bk=64)
+    assert call(p) == 4                # tiles other than 128 x 128
+    p = api.Plan.from_slices([(0, 64, 0, 64, 1)], 64, 64, 1, 1, 96)
+    assert call(p) == 4                # d = 96
+    p = api.Plan.from_slices([(0, 64, 0, 64, 1)], 64, 64, 1, 1, 128)
+    assert call(p, scale=0.0) == 1     # non-positive scale
+    assert call(p, lse=None) == 1      # no LSE
+    assert call(p, delta=None) == 1    # no delta scratch
+    assert call(p) == 8                # not uploaded
