@@ -144,6 +144,35 @@ def other_workloads(api, W, reps=10):
         del q, k, v, o, lse
         torch.cuda.empty_cache()
 
+    # Backward at the varlen causal workload: one call runs delta = rowsum(dO*O), the dQ
+    # kernel (by query tile) and the dK/dV kernel (by key tile).  Algorithmic work is 5
+    # products of 2*d flops per admitted pair (S, dP, dV, dK, dQ); the kernels execute 7
+    # (S and dP are recomputed by both gradient kernels instead of using atomics).
+    w = W.config2()
+    q, k, v = api.to_device_bf16(w.q), api.to_device_bf16(w.k), api.to_device_bf16(w.v)
+    g = api.to_device_bf16(W.random_grad(np.random.default_rng(2002), w.sq, w.hq, w.d))
+    plan = api.plan_from_workload(w, stream=stream)
+    info = plan.info()
+    fl = 10.0 * w.d * info["pairs"] * w.hq
+    o, lse = api.attn_fwd(q, k, v, plan, w.scale, stream=stream)
+    dq = torch.empty((w.sq, w.hq, w.d), dtype=torch.float32, device="cuda")
+    dk = torch.empty((w.sk, w.hkv, w.d), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    delta = torch.empty_like(lse)
+    f = lambda: api.attn_bwd(q, k, v, o, g, lse, plan, w.scale, dq=dq, dk=dk, dv=dv, delta=delta,
+                             stream=stream)
+    for _ in range(3):
+        f()
+    ms = float(np.median(event_times(f, reps * 2, stream)))
+    name = w.name + "_backward"
+    out[name] = {"kernel_ms": ms, "tflops": fl / ms * 1e-9, "frac_of_peak": fl / ms * 1e-9 / PEAK_BF16_TFLOPS,
+                 "flops_per_pair": 10 * w.d, "pairs_per_head": info["pairs"],
+                 "note": "dQ, dK, dV (fp32) from O, LSE and dO; algorithmic flops = 2.5x the forward's"}
+    log(f"{name}: {ms:.3f} ms  {fl / ms * 1e-9:.1f} TFLOPS (algorithmic)")
+    plan.close()
+    del q, k, v, g, o, lse, dq, dk, dv, delta
+    torch.cuda.empty_cache()
+
     # Few query rows against a long context (a prefill chunk): 1 query tile x 32 heads is
     # 32 items for 512 workgroup slots, so the plan splits every row's key range into
     # parts whose partial results a second kernel merges inside the same call.

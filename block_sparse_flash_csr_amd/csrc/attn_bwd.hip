@@ -58,13 +58,24 @@ struct BCfg {
     static constexpr int KS = D / 16;           // k-steps over the head dim
     static constexpr int DB = D / 32;           // 32-row blocks over the head dim
     static constexpr int NBLK = TILE_B / 1024;  // 1 KB direct-load blocks per tile
+    static_assert(NBLK % 4 == 0, "the 4 waves share a tile's blocks evenly");
 };
+
+// 16-byte chunk c of tile row r sits at chunk c ^ swz(r).  The pattern serves both reads
+// of a tile: row reads (32 rows, one chunk each) see 16 (d 128) or 8 per row parity
+// (d 64) different chunk positions, and transpose reads (rows 4 m .. 4 m + 3, a 4-chunk
+// group each) put the 4 rows in 4 different 4-chunk groups of banks.
+template <int D>
+__device__ __forceinline__ int swz(int r)
+{
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
 
 // Byte offset of 16-byte chunk c of row r in a swizzled tile.
 template <int D>
 __device__ __forceinline__ uint32_t toff(int r, int c)
 {
-    return (uint32_t)(r * BCfg<D>::ROWB + ((c ^ (r & (BCfg<D>::NCH - 1))) << 4));
+    return (uint32_t)(r * BCfg<D>::ROWB + ((c ^ swz<D>(r)) << 4));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -86,17 +97,18 @@ __device__ __forceinline__ uint32_t extent(int n, int32_t st)
 
 __device__ __forceinline__ int32_t cload(const int32_t *p, int i) { return ((cptr_i32)p)[i]; }
 
-// 64 rows of a [tokens, heads, D] bf16 tensor (row stride st elements, n rows in range)
-// into an LDS tile; the waves share the 1 KB blocks, rows past n land as zeros.
+// 64 rows of a [tokens, heads, D] bf16 tensor (row stride st elements) from the
+// buffer range r into an LDS tile; the waves share the 1 KB blocks, rows outside the
+// range land as zeros.
 template <int D>
-__device__ __forceinline__ void load_rows(const void *base, int32_t st, int n, char *tile, int wave)
+__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t r, int32_t st, char *tile, int wave, int lane)
 {
     using C = BCfg<D>;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, extent<D>(n, st));
-    const int lane = threadIdx.x & 63;
-    for (int b = wave; b < C::NBLK; b += kThreads / 64) {
+#pragma unroll
+    for (int i = 0; i < C::NBLK / 4; ++i) {
+        const int b = wave + 4 * i;
         const int p = 64 * b + lane, row = p / C::NCH, phys = p % C::NCH;
-        const uint32_t goff = (uint32_t)(row * st * 2 + ((phys ^ (row & (C::NCH - 1))) << 4));
+        const uint32_t goff = (uint32_t)(row * st * 2 + ((phys ^ swz<D>(row)) << 4));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(tile + b * 1024), 16, (int)goff, 0, 0, 0);
     }
 }
@@ -114,24 +126,51 @@ __device__ __forceinline__ void load_frag(const void *row_base, int32_t st, int 
                                                r, (int)(l32 * st * 2 + 32 * ks + 16 * hh), 0, 0));
 }
 
-// A operand read along a tile row: row r, chunk c (8 elements).
+// Per-lane LDS offsets of the two tile reads, fixed for the whole kernel:
+//   row[ks]    : chunk 2 ks + hh of tile row l32 (block b adds 32 b rows: the swizzle
+//                depends on the row's low 4 bits only, so it is an immediate offset);
+//   tr[db][j]  : the transpose read of head dims 32 db .. + 31, rows 4 hh + r + 8 j of
+//                k-step 0 (k-step ks adds 16 ks rows, again an immediate).
 template <int D>
-__device__ __forceinline__ bf16x8 rd_row(const char *tile, int r, int c)
+struct Addr {
+    uint32_t row[BCfg<D>::KS];
+    uint32_t tr[BCfg<D>::DB][2];
+};
+
+template <int D>
+__device__ __forceinline__ Addr<D> make_addr(int lane)
 {
-    return *(const bf16x8 *)(tile + toff<D>(r, c));
+    using C = BCfg<D>;
+    Addr<D> a;
+    const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) a.row[ks] = toff<D>(l32, 2 * ks + hh);
+    const int grp = lane >> 4, i16 = lane & 15, r = i16 >> 2, c4 = i16 & 3;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+        const int chunk = 4 * db + 2 * (grp & 1) + (c4 >> 1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) a.tr[db][j] = toff<D>(4 * hh + r + 8 * j, chunk) + (c4 & 1) * 8;
+    }
+    return a;
+}
+
+// A operand read along a tile row: rows 32 b + l32, chunk 2 ks + hh.
+template <int D>
+__device__ __forceinline__ bf16x8 rd_row(const char *tile, const Addr<D> &ad, int b, int ks)
+{
+    return *(const bf16x8 *)(tile + ad.row[ks] + 32 * b * BCfg<D>::ROWB);
 }
 
 // A operand of X^T for a 64-row tile X: head dims 32 db .. + 31 (the A rows) against
 // tile rows 16 ks .. + 15 (the k index), element e of lane (l32, hh) <-> tile row
 // 16 ks + 8 (e >> 2) + 4 hh + (e & 3): two transpose reads of 4 rows each.
 template <int D>
-__device__ __forceinline__ bf16x8 rd_tr(const char *tile, int db, int ks, int lane)
+__device__ __forceinline__ bf16x8 rd_tr(const char *tile, const Addr<D> &ad, int db, int ks)
 {
-    const int grp = lane >> 4, i16 = lane & 15, r = i16 >> 2, c4 = i16 & 3, hh = lane >> 5;
-    const int chunk = 4 * db + 2 * (grp & 1) + (c4 >> 1);
-    const int row0 = 16 * ks + 4 * hh + r, row1 = row0 + 8;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(tile + toff<D>(row0, chunk) + (c4 & 1) * 8));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(tile + toff<D>(row1, chunk) + (c4 & 1) * 8));
+    const char *p = tile + 16 * ks * BCfg<D>::ROWB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(p + ad.tr[db][0]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(p + ad.tr[db][1]));
     const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
     return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
 }
@@ -197,20 +236,115 @@ __global__ void __launch_bounds__(kThreads) bwd_delta_kernel(const BwdArgs a)
     if (i < a.sq && (threadIdx.x % TPR) == 0) a.delta[(int64_t)h * a.lse_sh + i] = s;
 }
 
+// Operands are read this many products ahead of their MFMA: 3 where the kernel runs
+// one wave per SIMD, 2 where two waves share the SIMD (and the register file).
+constexpr int kAheadKv = 3, kAheadQ = 2;
+
+// S = X Y^T and dP = Z W^T over one 64-row LDS tile pair (x_t, z_t) against the register
+// fragments yf, wf (one 32-row block per wave): product i -> S (i even) or dP (i odd),
+// row block (i >> 1) & 1, k-step i >> 2, so four independent accumulator chains rotate.
+// The tile reads run kAhead products ahead; `tail` runs once the last read is issued.
+template <int D, int AH, typename Tail>
+__device__ __forceinline__ void score_products(const char *x_t, const char *z_t, const bf16x8 (&yf)[BCfg<D>::KS],
+                                               const bf16x8 (&wf)[BCfg<D>::KS], const Addr<D> &ad, f32x16 (&s)[2],
+                                               f32x16 (&dp)[2], Tail tail)
+{
+    constexpr int N1 = 4 * BCfg<D>::KS;
+    auto rd1 = [&](int i) { return rd_row<D>((i & 1) ? z_t : x_t, ad, (i >> 1) & 1, i >> 2); };
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        s[b] = f32x16{};
+        dp[b] = f32x16{};
+    }
+    bf16x8 op[AH + 1];
+#pragma unroll
+    for (int i = 0; i < AH; ++i) op[i] = rd1(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < N1; ++i) {
+        if (i + AH < N1) op[(i + AH) % (AH + 1)] = rd1(i + AH);
+        if (i + AH == N1) tail();
+        const int b = (i >> 1) & 1, ks = i >> 2;
+        if (i & 1) dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (AH + 1)], wf[ks], dp[b], 0, 0, 0);
+        else s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (AH + 1)], yf[ks], s[b], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int D, int AH>
+__device__ __forceinline__ void score_products(const char *x_t, const char *z_t, const bf16x8 (&yf)[BCfg<D>::KS],
+                                               const bf16x8 (&wf)[BCfg<D>::KS], const Addr<D> &ad, f32x16 (&s)[2],
+                                               f32x16 (&dp)[2])
+{
+    score_products<D, AH>(x_t, z_t, yf, wf, ad, s, dp, []() {});
+}
+
 // ---------------------------------------------------------------------------
-// kernel 2: dQ by query tile (grid n_qt x hq), 64-key steps over the CSR row
+// kernel 2: dQ by query tile (grid n_qt x hq), 64-key steps over the CSR row; the K and
+// V tiles of step j + 1 load (LDS double buffer) while step j computes
 // ---------------------------------------------------------------------------
+template <int D>
+struct DqTiles {
+    static constexpr int K0 = 0, V0 = BCfg<D>::TILE_B, BUF = 2 * BCfg<D>::TILE_B, BYTES = 2 * BUF;
+};
+
+// One dQ step: issue the next step's K/V loads into (kd, vd) when `issue`, then
+// S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D_i), dQ^T += K^T dS^T on (kt, vt).
+// The restrict qualifiers tell the compiler that the loads in flight do not write the
+// tiles this step reads.
+template <int D>
+__device__ __forceinline__ void dq_step(char *__restrict__ kd, char *__restrict__ vd, const char *__restrict__ kt,
+                                        const char *__restrict__ vt, bool issue, __amdgpu_buffer_rsrc_t rk,
+                                        __amdgpu_buffer_rsrc_t rv, int32_t k_st, int32_t v_st, int wave, int lane,
+                                        const Addr<D> &ad, const bf16x8 (&qf)[BCfg<D>::KS], const bf16x8 (&gf)[BCfg<D>::KS], uint64_t m,
+                                        bool masked_step, float c, float nl, float dlt, f32x16 (&acc)[BCfg<D>::DB])
+{
+    using C = BCfg<D>;
+    const int l32 = lane & 31, hh = lane >> 5;
+    if (issue) {
+        tile_dma<D>(rk, k_st, kd, wave, lane);
+        tile_dma<D>(rv, v_st, vd, wave, lane);
+    }
+    f32x16 s[2], dp[2];
+    score_products<D, kAheadQ>(kt, vt, qf, gf, ad, s, dp);
+    if (masked_step) mask_scores(m, s);
+    f32x16 ds[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, nl));
+            ds[b][r] = p * (dp[b][r] - dlt);
+        }
+    bf16x8 dsb[4];
+    to_bf16_operands(ds, dsb);
+    // dQ^T += K^T dS^T: product i -> head-dim block i % DB, k-step i / DB
+    constexpr int N2 = 4 * C::DB;
+    bf16x8 op[kAheadQ + 1];
+#pragma unroll
+    for (int i = 0; i < kAheadQ; ++i) op[i] = rd_tr<D>(kt, ad, i % C::DB, i / C::DB);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < N2; ++i) {
+        if (i + kAheadQ < N2) op[(i + kAheadQ) % (kAheadQ + 1)] = rd_tr<D>(kt, ad, (i + kAheadQ) % C::DB, (i + kAheadQ) / C::DB);
+        acc[i % C::DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (kAheadQ + 1)], dsb[i / C::DB], acc[i % C::DB], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int D>
 __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
 {
     using C = BCfg<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * C::TILE_B];
-    char *Kt = smem, *Vt = smem + C::TILE_B;
+    using L = DqTiles<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
     const int qt = blockIdx.x, h = blockIdx.y, g = h / (a.hq / a.hkv);
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qrow0 = qt * kKernelBq + wave * 32, qrow = qrow0 + l32;
     const bool qvalid = qrow < a.sq;
+    const int nsub = a.bk_plan / kStep;
+    const Addr<D> ad = make_addr<D>(lane);
 
     bf16x8 qf[C::KS], gf[C::KS];
     load_frag<D>((const __bf16 *)a.q + (int64_t)qrow0 * a.q_st + (int64_t)h * a.q_sh, a.q_st, a.sq - qrow0, l32, hh,
@@ -224,68 +358,67 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
+    const __bf16 *kh = (const __bf16 *)a.k + (int64_t)g * a.k_sh;
+    const __bf16 *vh = (const __bf16 *)a.v + (int64_t)g * a.v_sh;
     const int e0 = cload(a.meta.row_ptr, qt), e1 = cload(a.meta.row_ptr, qt + 1);
-    for (int e = e0; e < e1; ++e) {
-        const i32x4 en = ((cptr_i32x4)a.meta.entries)[e];   // col, piece_begin, piece_count, tag
-        for (int sub = 0; sub < a.bk_plan / kStep; ++sub) {
-            const int kv0 = en[0] * a.bk_plan + sub * kStep;
-            const int kv_end = min(en[0] * a.bk_plan + a.bk_plan, a.sk);
-            const int nk = min(kStep, kv_end - kv0);
-            if (nk <= 0) continue;
-            load_rows<D>((const __bf16 *)a.k + (int64_t)kv0 * a.k_st + (int64_t)g * a.k_sh, a.k_st, nk, Kt, wave);
-            load_rows<D>((const __bf16 *)a.v + (int64_t)kv0 * a.v_st + (int64_t)g * a.v_sh, a.v_st, nk, Vt, wave);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            // S^T = K Q^T and dP^T = V dO^T (keys x queries, two 32-key blocks)
-            f32x16 s[2], dp[2];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                s[b] = f32x16{};
-                dp[b] = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < C::KS; ++ks) {
-                    s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_row<D>(Kt, 32 * b + l32, 2 * ks + hh), qf[ks],
-                                                                   s[b], 0, 0, 0);
-                    dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_row<D>(Vt, 32 * b + l32, 2 * ks + hh), gf[ks],
-                                                                    dp[b], 0, 0, 0);
-                }
-            }
-            // mask (partial tiles and key tails): this lane's query row over the keys
-            const int base = kv0 + 4 * hh;
-            if (en[3] == BSFA_TILE_PARTIAL || nk < kStep) {
-                uint64_t m = range_bits(0, kv0 + nk - base);
-                if (en[3] == BSFA_TILE_PARTIAL) {
-                    uint64_t u = 0;
-                    for (int pi = 0; pi < en[2]; ++pi) {
-                        const i32x4 pc = ((cptr_i32x4)a.meta.pieces)[2 * (en[1] + pi)];
-                        const int diag = ((cptr_i32)a.meta.pieces)[8 * (en[1] + pi) + 4];
-                        if (qrow < pc[0] || qrow >= pc[1]) continue;
-                        u |= range_bits(pc[2] - base, min(pc[3], qrow + diag + 1) - base);
-                    }
-                    m &= u;
-                }
-                mask_scores(m, s);
-            }
-            // dS^T = P^T (dP^T - D_i), P^T = 2^(c s - LSE_i log2 e)
-            f32x16 ds[2];
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], a.c, nl));
-                    ds[b][r] = p * (dp[b][r] - dlt);
-                }
-            bf16x8 dsb[4];
-            to_bf16_operands(ds, dsb);
-            // dQ^T += K^T dS^T
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_tr<D>(Kt, db, ks, lane), dsb[ks], acc[db], 0, 0,
-                                                                      0);
-            __syncthreads();   // every wave is done with the tiles before the next loads
+    // steps (entry e, 64-key part sub); a part that starts past the last key is skipped
+    auto kv_start = [&](int e, int sub) { return cload((const int32_t *)a.meta.entries, 4 * e) * a.bk_plan + sub * kStep; };
+    auto advance = [&](int &e, int &sub) {
+        ++sub;
+        if (sub == nsub || kv_start(e, sub) >= a.sk) {
+            ++e;
+            sub = 0;
         }
+    };
+    auto rsrc_of = [&](const __bf16 *base, int32_t st, int kv0, int kend) {
+        return make_rsrc(base + (int64_t)kv0 * st, extent<D>(min(kStep, kend - kv0), st));
+    };
+    int e = e0, sub = 0, buf = 0;
+    if (e < e1) {
+        const int kv0 = kv_start(e, 0);
+        const int kend = min(kv0 + a.bk_plan, a.sk);
+        tile_dma<D>(rsrc_of(kh, a.k_st, kv0, kend), a.k_st, smem + L::K0, wave, lane);
+        tile_dma<D>(rsrc_of(vh, a.v_st, kv0, kend), a.v_st, smem + L::V0, wave, lane);
+    }
+    while (e < e1) {
+        const i32x4 en = ((cptr_i32x4)a.meta.entries)[e];   // col, piece_begin, piece_count, tag
+        const int kv0 = en[0] * a.bk_plan + sub * kStep;
+        const int nk = min(kStep, min(en[0] * a.bk_plan + a.bk_plan, a.sk) - kv0);
+        int ne = e, ns = sub;
+        advance(ne, ns);
+        const bool more = ne < e1;
+        __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, 0u), rv = make_rsrc(vh, 0u);
+        if (more) {
+            const int nkv0 = kv_start(ne, ns);
+            const int nkend = min(cload((const int32_t *)a.meta.entries, 4 * ne) * a.bk_plan + a.bk_plan, a.sk);
+            rk = rsrc_of(kh, a.k_st, nkv0, nkend);
+            rv = rsrc_of(vh, a.v_st, nkv0, nkend);
+        }
+        // mask (partial tiles and key tails): this lane's query row over the keys
+        const int base = kv0 + 4 * hh;
+        const bool masked_step = en[3] == BSFA_TILE_PARTIAL || nk < kStep;
+        uint64_t m = ~0ull;
+        if (masked_step) {
+            m = range_bits(0, kv0 + nk - base);
+            if (en[3] == BSFA_TILE_PARTIAL) {
+                uint64_t u = 0;
+                for (int pi = 0; pi < en[2]; ++pi) {
+                    const i32x4 pc = ((cptr_i32x4)a.meta.pieces)[2 * (en[1] + pi)];
+                    const int diag = ((cptr_i32)a.meta.pieces)[8 * (en[1] + pi) + 4];
+                    if (qrow < pc[0] || qrow >= pc[1]) continue;
+                    u |= range_bits(pc[2] - base, min(pc[3], qrow + diag + 1) - base);
+                }
+                m &= u;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // this step's tiles are in LDS (own loads) ...
+        __syncthreads();                 // ... for every wave, and the other buffer is free
+        char *cur = smem + buf * L::BUF, *nxt = smem + (buf ^ 1) * L::BUF;
+        dq_step<D>(nxt + L::K0, nxt + L::V0, cur + L::K0, cur + L::V0, more, rk, rv, a.k_st, a.v_st, wave, lane,
+                   ad, qf, gf, m, masked_step, a.c, nl, dlt, acc);
+        e = ne;
+        sub = ns;
+        buf ^= 1;
     }
     // lane (query l32, half hh) holds dims 32 db + 8 g4 + 4 hh + 0..3 of its query
     if (qvalid) {
@@ -304,19 +437,105 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
 
 // ---------------------------------------------------------------------------
 // kernel 3: dK, dV by key tile (grid n_kt x hkv); a wave owns 32 keys; 64-query
-// steps over the CSR column, for every query head of the key/value head
+// steps over the CSR column, for every query head of the key/value head; the Q, dO,
+// LSE and D of step j + 1 load (LDS double buffer) while step j computes
 // ---------------------------------------------------------------------------
+template <int D>
+struct KvTiles {
+    static constexpr int Q0 = 0, G0 = BCfg<D>::TILE_B, L0 = 2 * BCfg<D>::TILE_B, D0 = L0 + 4 * kStep;
+    static constexpr int BUF = 2 * BCfg<D>::TILE_B + 1024, BYTES = 2 * BUF;
+};
+
+struct RowSrc {
+    __amdgpu_buffer_rsrc_t q, g, l, d;
+};
+
+template <int D>
+__device__ __forceinline__ void kv_issue(char *__restrict__ dst, const RowSrc &r, int32_t q_st, int32_t do_st,
+                                         int wave, int lane)
+{
+    using L = KvTiles<D>;
+    tile_dma<D>(r.q, q_st, dst + L::Q0, wave, lane);
+    tile_dma<D>(r.g, do_st, dst + L::G0, wave, lane);
+    if (wave == 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(r.l, (lds_ptr)(dst + L::L0), 4, lane * 4, 0, 0, 0);
+    if (wave == 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(r.d, (lds_ptr)(dst + L::D0), 4, lane * 4, 0, 0, 0);
+}
+
+// One dK/dV step on the 64 query rows in `cur`: S = Q K^T, dP = dO V^T,
+// P = 2^(c S - LSE log2 e), dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.  Query rows
+// past the end arrive as zero rows with LSE = D = 0, so they add nothing.
+template <int D>
+__device__ __forceinline__ void kv_step(char *__restrict__ nxt, const char *__restrict__ cur, bool issue,
+                                        const RowSrc &src, int32_t q_st, int32_t do_st, int wave, int lane,
+                                        const Addr<D> &ad, const bf16x8 (&kf)[BCfg<D>::KS], const bf16x8 (&vf)[BCfg<D>::KS], uint64_t m,
+                                        bool masked_step, float c, f32x16 (&dk)[BCfg<D>::DB],
+                                        f32x16 (&dv)[BCfg<D>::DB])
+{
+    using C = BCfg<D>;
+    using L = KvTiles<D>;
+    const int l32 = lane & 31, hh = lane >> 5;
+    if (issue) kv_issue<D>(nxt, src, q_st, do_st, wave, lane);
+    const char *qt_ = cur + L::Q0, *gt = cur + L::G0;
+    const float *lse_s = (const float *)(cur + L::L0), *dlt_s = (const float *)(cur + L::D0);
+    // rows of the lane's registers: 32 b + 8 g4 + 4 hh + t
+    f32x4 l4[2][4], d4[2][4];
+    f32x16 s[2], dp[2];
+    score_products<D, kAheadKv>(qt_, gt, kf, vf, ad, s, dp, [&]() {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                l4[b][g4] = *(const f32x4 *)(lse_s + 32 * b + 8 * g4 + 4 * hh);
+                d4[b][g4] = *(const f32x4 *)(dlt_s + 32 * b + 8 * g4 + 4 * hh);
+            }
+    });
+    // the first operands of the gradient products load during the exponentials
+    constexpr int N2 = 8 * C::DB;   // product i: dV (i even) or dK (i odd), block (i / 2) % DB, k-step i / (2 DB)
+    auto rd2 = [&](int i) { return rd_tr<D>((i & 1) ? qt_ : gt, ad, (i >> 1) % C::DB, (i >> 1) / C::DB); };
+    bf16x8 op[kAheadKv + 1];
+#pragma unroll
+    for (int i = 0; i < kAheadKv; ++i) op[i] = rd2(i);
+    __builtin_amdgcn_sched_barrier(0);
+    if (masked_step) mask_scores(m, s);
+    f32x16 p[2], ds[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float lv = l4[b][g4][t];
+                const float nl = lv == -INFINITY ? -INFINITY : -lv * kLog2e;
+                const int r = 4 * g4 + t;
+                p[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, nl));
+                ds[b][r] = p[b][r] * (dp[b][r] - d4[b][g4][t]);
+            }
+    bf16x8 pb[4], dsb[4];
+    to_bf16_operands(p, pb);
+    to_bf16_operands(ds, dsb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < N2; ++i) {
+        if (i + kAheadKv < N2) op[(i + kAheadKv) % (kAheadKv + 1)] = rd2(i + kAheadKv);
+        const int db = (i >> 1) % C::DB, ks = (i >> 1) / C::DB;
+        if (i & 1) dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (kAheadKv + 1)], dsb[ks], dk[db], 0, 0, 0);
+        else dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (kAheadKv + 1)], pb[ks], dv[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int D>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(const BwdArgs a)
 {
     using C = BCfg<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * C::TILE_B + 2 * kStep * 4];
-    char *Qt = smem, *Gt = smem + C::TILE_B;
-    float *lse_s = (float *)(smem + 2 * C::TILE_B), *dlt_s = lse_s + kStep;
+    using L = KvTiles<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
     const int kt = blockIdx.x, g = blockIdx.y, group = a.hq / a.hkv;
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int key0 = kt * a.bk_plan + wave * 32, key = key0 + l32;
+    const int nsub = kKernelBq / kStep;
+    const Addr<D> ad = make_addr<D>(lane);
 
     bf16x8 kf[C::KS], vf[C::KS];
     load_frag<D>((const __bf16 *)a.k + (int64_t)key0 * a.k_st + (int64_t)g * a.k_sh, a.k_st, a.sk - key0, l32, hh, kf);
@@ -329,84 +548,64 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(const BwdArgs a)
     }
 
     const int t0 = cload(a.meta.t_ptr, kt), t1 = cload(a.meta.t_ptr, kt + 1);
-    for (int h = g * group; h < (g + 1) * group; ++h)
-        for (int t = t0; t < t1; ++t) {
-            const int qt = cload(a.meta.t_list, 2 * t), e = cload(a.meta.t_list, 2 * t + 1);
-            const i32x4 en = ((cptr_i32x4)a.meta.entries)[e];
-            for (int sub = 0; sub < kKernelBq / kStep; ++sub) {
-                const int q0 = qt * kKernelBq + sub * kStep;
-                const int nq = min(kStep, a.sq - q0);
-                if (nq <= 0) continue;
-                load_rows<D>((const __bf16 *)a.q + (int64_t)q0 * a.q_st + (int64_t)h * a.q_sh, a.q_st, nq, Qt, wave);
-                load_rows<D>((const __bf16 *)a.dout + (int64_t)q0 * a.do_st + (int64_t)h * a.do_sh, a.do_st, nq, Gt,
-                             wave);
-                if (tid < kStep) {
-                    const int i = q0 + tid;
-                    lse_s[tid] = i < a.sq ? a.lse[(int64_t)h * a.lse_sh + i] : -INFINITY;
-                    dlt_s[tid] = i < a.sq ? a.delta[(int64_t)h * a.lse_sh + i] : 0.f;
-                }
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();
-                // S = Q K^T and dP = dO V^T (queries x keys, two 32-query blocks)
-                f32x16 s[2], dp[2];
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    s[b] = f32x16{};
-                    dp[b] = f32x16{};
-#pragma unroll
-                    for (int ks = 0; ks < C::KS; ++ks) {
-                        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_row<D>(Qt, 32 * b + l32, 2 * ks + hh), kf[ks],
-                                                                       s[b], 0, 0, 0);
-                        dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_row<D>(Gt, 32 * b + l32, 2 * ks + hh),
-                                                                        vf[ks], dp[b], 0, 0, 0);
-                    }
-                }
-                // mask of partial tiles: this lane's key over the 64 query rows
-                if (en[3] == BSFA_TILE_PARTIAL) {
-                    const int base = q0 + 4 * hh;
-                    uint64_t m = 0;
-                    for (int pi = 0; pi < en[2]; ++pi) {
-                        const i32x4 pc = ((cptr_i32x4)a.meta.pieces)[2 * (en[1] + pi)];
-                        const int diag = ((cptr_i32)a.meta.pieces)[8 * (en[1] + pi) + 4];
-                        if (key < pc[2] || key >= pc[3]) continue;
-                        // rows i of the piece with key <= i + diag
-                        m |= range_bits(max(pc[0], key - diag) - base, pc[1] - base);
-                    }
-                    mask_scores(m, s);
-                }
-                // P = 2^(c s - LSE_i log2 e), dS = P (dP - D_i); rows of the lane's
-                // registers: 32 b + 8 g4 + 4 hh + t
-                f32x16 p[2], ds[2];
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const f32x4 l4 = *(const f32x4 *)(lse_s + 32 * b + 8 * g4 + 4 * hh);
-                        const f32x4 d4 = *(const f32x4 *)(dlt_s + 32 * b + 8 * g4 + 4 * hh);
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            const float nl = l4[t] == -INFINITY ? -INFINITY : -l4[t] * kLog2e;
-                            const int r = 4 * g4 + t;
-                            p[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], a.c, nl));
-                            ds[b][r] = p[b][r] * (dp[b][r] - d4[t]);
-                        }
-                    }
-                bf16x8 pb[4], dsb[4];
-                to_bf16_operands(p, pb);
-                to_bf16_operands(ds, dsb);
-                // dV^T += dO^T P, dK^T += Q^T dS
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                    for (int db = 0; db < C::DB; ++db) {
-                        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_tr<D>(Gt, db, ks, lane), pb[ks], dv[db], 0,
-                                                                         0, 0);
-                        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_tr<D>(Qt, db, ks, lane), dsb[ks], dk[db],
-                                                                         0, 0, 0);
-                    }
-                __syncthreads();   // every wave is done with the tiles before the next loads
+    const int h_end = (g + 1) * group;
+    // steps (head h, column entry t, 64-query part sub); a part past the last query is skipped
+    auto q_start = [&](int t, int sub) { return cload(a.meta.t_list, 2 * t) * kKernelBq + sub * kStep; };
+    auto advance = [&](int &h, int &t, int &sub) {
+        ++sub;
+        if (sub == nsub || q_start(t, sub) >= a.sq) {
+            sub = 0;
+            if (++t == t1) {
+                t = t0;
+                ++h;
             }
         }
+    };
+    auto sources = [&](int h, int q0) {
+        const int nq = min(kStep, a.sq - q0);
+        RowSrc r;
+        r.q = make_rsrc((const __bf16 *)a.q + (int64_t)q0 * a.q_st + (int64_t)h * a.q_sh, extent<D>(nq, a.q_st));
+        r.g = make_rsrc((const __bf16 *)a.dout + (int64_t)q0 * a.do_st + (int64_t)h * a.do_sh,
+                        extent<D>(nq, a.do_st));
+        r.l = make_rsrc(a.lse + (int64_t)h * a.lse_sh + q0, (uint32_t)nq * 4u);
+        r.d = make_rsrc(a.delta + (int64_t)h * a.lse_sh + q0, (uint32_t)nq * 4u);
+        return r;
+    };
+    int h = g * group, t = t0, sub = 0, buf = 0;
+    if (t0 < t1) kv_issue<D>(smem, sources(h, q_start(t, 0)), a.q_st, a.do_st, wave, lane);
+    else h = h_end;
+    while (h < h_end) {
+        const int e = cload(a.meta.t_list, 2 * t + 1);
+        const i32x4 en = ((cptr_i32x4)a.meta.entries)[e];
+        const int q0 = q_start(t, sub);
+        int nh = h, ntt = t, ns = sub;
+        advance(nh, ntt, ns);
+        const bool more = nh < h_end;
+        RowSrc src = sources(h, q0);   // placeholder when there is no next step
+        if (more) src = sources(nh, q_start(ntt, ns));
+        // mask of partial tiles: this lane's key over the 64 query rows
+        const bool masked_step = en[3] == BSFA_TILE_PARTIAL;
+        uint64_t m = ~0ull;
+        if (masked_step) {
+            const int base = q0 + 4 * hh;
+            m = 0;
+            for (int pi = 0; pi < en[2]; ++pi) {
+                const i32x4 pc = ((cptr_i32x4)a.meta.pieces)[2 * (en[1] + pi)];
+                const int diag = ((cptr_i32)a.meta.pieces)[8 * (en[1] + pi) + 4];
+                if (key < pc[2] || key >= pc[3]) continue;
+                // rows i of the piece with key <= i + diag
+                m |= range_bits(max(pc[0], key - diag) - base, pc[1] - base);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // this step's rows are in LDS (own loads) ...
+        __syncthreads();                 // ... for every wave, and the other buffer is free
+        kv_step<D>(smem + (buf ^ 1) * L::BUF, smem + buf * L::BUF, more, src, a.q_st, a.do_st, wave, lane, ad, kf, vf, m,
+                   masked_step, a.c, dk, dv);
+        h = nh;
+        t = ntt;
+        sub = ns;
+        buf ^= 1;
+    }
     // lane (key l32, half hh) holds dims 32 db + 8 g4 + 4 hh + 0..3 of its key
     if (key < a.sk) {
         float *ok = a.dk + ((int64_t)key * a.hkv + g) * D, *ov = a.dv + ((int64_t)key * a.hkv + g) * D;
@@ -416,9 +615,9 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(const BwdArgs a)
             for (int g4 = 0; g4 < 4; ++g4) {
                 f32x4 wk, wv;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    wk[t] = a.scale * dk[db][4 * g4 + t];
-                    wv[t] = dv[db][4 * g4 + t];
+                for (int t4 = 0; t4 < 4; ++t4) {
+                    wk[t4] = a.scale * dk[db][4 * g4 + t4];
+                    wv[t4] = dv[db][4 * g4 + t4];
                 }
                 *(f32x4 *)(ok + 32 * db + 8 * g4 + 4 * hh) = wk;
                 *(f32x4 *)(ov + 32 * db + 8 * g4 + 4 * hh) = wv;

@@ -61,6 +61,9 @@ def _load():
         lib.oracle_attn_bwd.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P, I32, D, P, P, P, I32]
         lib.oracle_attn_bwd_f64.restype = I32
         lib.oracle_attn_bwd_f64.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P, I32, D, P, P, P]
+        lib.oracle_attn_bwd_sampled.restype = I32
+        lib.oracle_attn_bwd_sampled.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P, I32, D, P,
+                                                ctypes.c_int64, P, P, ctypes.c_int64, P, P, I32]
         lib.oracle_merge.restype = None
         lib.oracle_merge.argtypes = [P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P, P]
         _lib = lib
@@ -172,6 +175,30 @@ def attn_bwd(q_bits, k_bits, v_bits, do_bits, slices, scale: float, n_threads: i
                                  _ptr(dv), int(n_threads))
     if rc != 0:
         raise ValueError("oracle_attn_bwd: bad head counts")
+    return dq, dk, dv
+
+
+def attn_bwd_sampled(q_bits, k_bits, v_bits, do_bits, slices, scale: float, rows=(), keys=(),
+                     n_threads: int | None = None):
+    """fp64 gradients at sampled outputs: dQ at (h, i) pairs `rows` -> [n_rows, d];
+    dK, dV at (g, j) pairs `keys` (g a key/value head) -> [n_keys, d] each."""
+    q_bits, k_bits, v_bits, do_bits = (np.ascontiguousarray(x, dtype=np.uint16)
+                                       for x in (q_bits, k_bits, v_bits, do_bits))
+    sq, hq, d = q_bits.shape
+    sk, hkv, _ = k_bits.shape
+    rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
+    keys_arr = np.ascontiguousarray(np.asarray(keys, dtype=np.int64).reshape(-1, 2))
+    dq = np.zeros((rows_arr.shape[0], d), np.float64)
+    dk = np.zeros((keys_arr.shape[0], d), np.float64)
+    dv = np.zeros((keys_arr.shape[0], d), np.float64)
+    if n_threads is None:
+        n_threads = os.cpu_count() or 1
+    rc = _load().oracle_attn_bwd_sampled(
+        _ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(do_bits), sq, sk, hq, hkv, d, _slices(slices),
+        len(slices), float(scale), _ptr(rows_arr), rows_arr.shape[0], _ptr(dq), _ptr(keys_arr),
+        keys_arr.shape[0], _ptr(dk), _ptr(dv), int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_attn_bwd_sampled: bad head counts")
     return dq, dk, dv
 
 

@@ -353,54 +353,77 @@ typedef struct {
     int32_t n_threads, tid;
 } bwd_job;
 
+/* One row (h, i): its admitted keys (keys[0 .. n)), P_ij in p[], and D_i.  Returns n;
+ * 0 when U(i) is empty (then every gradient term of the row is 0). */
+static int64_t bwd_row(const bwd_job *J, int64_t h, int64_t i, interval *ivs, int64_t *keys, double *p,
+                       double *o_row, double *D_out)
+{
+    const int d = J->d;
+    const int64_t g = h / (J->hq / J->hkv);
+    const int m = row_key_set(J->s, J->n_slices, i, ivs);
+    int64_t n_keys = 0;
+    for (int t = 0; t < m; ++t) {
+        int64_t lo = ivs[t].lo < 0 ? 0 : ivs[t].lo, hi = ivs[t].hi > J->sk ? J->sk : ivs[t].hi;
+        for (int64_t j = lo; j < hi; ++j) keys[n_keys++] = j;
+    }
+    if (n_keys == 0) return 0;
+    const size_t qi = ((size_t)i * J->hq + (size_t)h) * d;
+    double mx = -INFINITY;
+    for (int64_t c = 0; c < n_keys; ++c) {
+        const size_t kj = ((size_t)keys[c] * J->hkv + (size_t)g) * d;
+        double acc = 0.0;
+        for (int e = 0; e < d; ++e) acc += ld(J->q, qi + e, J->bf16) * ld(J->k, kj + e, J->bf16);
+        p[c] = J->scale * acc;
+        if (p[c] > mx) mx = p[c];
+    }
+    double sum = 0.0;
+    for (int64_t c = 0; c < n_keys; ++c) sum += exp(p[c] - mx);
+    const double lse = mx + log(sum);
+    /* P (in place of the scores), O and D */
+    for (int e = 0; e < d; ++e) o_row[e] = 0.0;
+    for (int64_t c = 0; c < n_keys; ++c) {
+        p[c] = exp(p[c] - lse);
+        const size_t vj = ((size_t)keys[c] * J->hkv + (size_t)g) * d;
+        for (int e = 0; e < d; ++e) o_row[e] += p[c] * ld(J->v, vj + e, J->bf16);
+    }
+    double D = 0.0;
+    for (int e = 0; e < d; ++e) D += ld(J->dout, qi + e, J->bf16) * o_row[e];
+    *D_out = D;
+    return n_keys;
+}
+
+/* dS_ij = P_ij (dO_i . v_j - D_i) for row (h, i) and key j. */
+static double bwd_ds(const bwd_job *J, int64_t h, int64_t i, int64_t j, double p, double D)
+{
+    const int d = J->d;
+    const int64_t g = h / (J->hq / J->hkv);
+    const size_t qi = ((size_t)i * J->hq + (size_t)h) * d, kv = ((size_t)j * J->hkv + (size_t)g) * d;
+    double dp = 0.0;
+    for (int e = 0; e < d; ++e) dp += ld(J->dout, qi + e, J->bf16) * ld(J->v, kv + e, J->bf16);
+    return p * (dp - D);
+}
+
 static void *bwd_worker(void *arg)
 {
     const bwd_job *J = (const bwd_job *)arg;
     const int d = J->d, group = J->hq / J->hkv;
     interval *ivs = (interval *)malloc(sizeof(interval) * (size_t)(J->n_slices > 0 ? J->n_slices : 1));
-    double *scores = (double *)malloc(sizeof(double) * (size_t)(J->sk > 0 ? J->sk : 1));
+    double *p = (double *)malloc(sizeof(double) * (size_t)(J->sk > 0 ? J->sk : 1));
     int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)(J->sk > 0 ? J->sk : 1));
     double *o_row = (double *)malloc(sizeof(double) * (size_t)d);
     for (int64_t g = J->tid; g < J->hkv; g += J->n_threads) {
         for (int64_t h = g * group; h < (g + 1) * group; ++h) {
             for (int64_t i = 0; i < J->sq; ++i) {
-                const int m = row_key_set(J->s, J->n_slices, i, ivs);
-                int64_t n_keys = 0;
-                for (int t = 0; t < m; ++t) {
-                    int64_t lo = ivs[t].lo < 0 ? 0 : ivs[t].lo, hi = ivs[t].hi > J->sk ? J->sk : ivs[t].hi;
-                    for (int64_t j = lo; j < hi; ++j) keys[n_keys++] = j;
-                }
-                if (n_keys == 0) continue;   /* no admitted key: every gradient term is 0 */
-                const size_t qi = ((size_t)i * J->hq + (size_t)h) * d;
-                double mx = -INFINITY;
-                for (int64_t c = 0; c < n_keys; ++c) {
-                    const size_t kj = ((size_t)keys[c] * J->hkv + (size_t)g) * d;
-                    double acc = 0.0;
-                    for (int e = 0; e < d; ++e) acc += ld(J->q, qi + e, J->bf16) * ld(J->k, kj + e, J->bf16);
-                    scores[c] = J->scale * acc;
-                    if (scores[c] > mx) mx = scores[c];
-                }
-                double sum = 0.0;
-                for (int64_t c = 0; c < n_keys; ++c) sum += exp(scores[c] - mx);
-                const double lse = mx + log(sum);
-                /* P (in place of the scores), O and D */
-                for (int e = 0; e < d; ++e) o_row[e] = 0.0;
-                for (int64_t c = 0; c < n_keys; ++c) {
-                    scores[c] = exp(scores[c] - lse);
-                    const size_t vj = ((size_t)keys[c] * J->hkv + (size_t)g) * d;
-                    for (int e = 0; e < d; ++e) o_row[e] += scores[c] * ld(J->v, vj + e, J->bf16);
-                }
                 double D = 0.0;
-                for (int e = 0; e < d; ++e) D += ld(J->dout, qi + e, J->bf16) * o_row[e];
+                const int64_t n_keys = bwd_row(J, h, i, ivs, keys, p, o_row, &D);
+                const size_t qi = ((size_t)i * J->hq + (size_t)h) * d;
                 for (int64_t c = 0; c < n_keys; ++c) {
                     const size_t kv = ((size_t)keys[c] * J->hkv + (size_t)g) * d;
-                    double dp = 0.0;
-                    for (int e = 0; e < d; ++e) dp += ld(J->dout, qi + e, J->bf16) * ld(J->v, kv + e, J->bf16);
-                    const double p = scores[c], ds = p * (dp - D);
+                    const double ds = bwd_ds(J, h, i, keys[c], p[c], D);
                     for (int e = 0; e < d; ++e) {
                         J->dq[qi + e] += J->scale * ds * ld(J->k, kv + e, J->bf16);
                         J->dk[kv + e] += J->scale * ds * ld(J->q, qi + e, J->bf16);
-                        J->dv[kv + e] += p * ld(J->dout, qi + e, J->bf16);
+                        J->dv[kv + e] += p[c] * ld(J->dout, qi + e, J->bf16);
                     }
                 }
             }
@@ -408,7 +431,7 @@ static void *bwd_worker(void *arg)
     }
     free(o_row);
     free(keys);
-    free(scores);
+    free(p);
     free(ivs);
     return NULL;
 }
@@ -448,6 +471,95 @@ int32_t oracle_attn_bwd_f64(const double *q, const double *k, const double *v, c
                             int32_t n_slices, double scale, double *dq, double *dk, double *dv)
 {
     return attn_bwd_any(q, k, v, dout, 0, sq, sk, hq, hkv, d, slices, n_slices, scale, dq, dk, dv, 1);
+}
+
+/* ---------------------------------------------------------------------------
+ * The same gradients at sampled outputs, for problems too large for the full
+ * pass: dQ rows at (h, i) pairs rows[2r], rows[2r+1] -> dq_rows [n_rows, d], and
+ * dK, dV rows at (g, j) pairs keys[2t], keys[2t+1] -> dk_rows, dv_rows [n_keys, d].
+ * A sampled key visits every row i of every head of its group whose key set holds
+ * j, recomputing that row's P and D; the terms are summed in the full pass's order.
+ * --------------------------------------------------------------------------- */
+typedef struct {
+    bwd_job base;
+    const int64_t *rows, *keys;
+    int64_t n_rows, n_keys;
+    double *dq_rows, *dk_rows, *dv_rows;
+} bwd_sample_job;
+
+static void *bwd_sample_worker(void *arg)
+{
+    const bwd_sample_job *S = (const bwd_sample_job *)arg;
+    const bwd_job *J = &S->base;
+    const int d = J->d, group = J->hq / J->hkv;
+    interval *ivs = (interval *)malloc(sizeof(interval) * (size_t)(J->n_slices > 0 ? J->n_slices : 1));
+    double *p = (double *)malloc(sizeof(double) * (size_t)(J->sk > 0 ? J->sk : 1));
+    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)(J->sk > 0 ? J->sk : 1));
+    double *o_row = (double *)malloc(sizeof(double) * (size_t)d);
+    for (int64_t r = J->tid; r < S->n_rows + S->n_keys; r += J->n_threads) {
+        if (r < S->n_rows) {
+            const int64_t h = S->rows[2 * r], i = S->rows[2 * r + 1], g = h / group;
+            double *out = S->dq_rows + (size_t)r * d;
+            for (int e = 0; e < d; ++e) out[e] = 0.0;
+            double D = 0.0;
+            const int64_t n = bwd_row(J, h, i, ivs, keys, p, o_row, &D);
+            for (int64_t c = 0; c < n; ++c) {
+                const size_t kv = ((size_t)keys[c] * J->hkv + (size_t)g) * d;
+                const double ds = bwd_ds(J, h, i, keys[c], p[c], D);
+                for (int e = 0; e < d; ++e) out[e] += J->scale * ds * ld(J->k, kv + e, J->bf16);
+            }
+        } else {
+            const int64_t t = r - S->n_rows, g = S->keys[2 * t], j = S->keys[2 * t + 1];
+            double *ok = S->dk_rows + (size_t)t * d, *ov = S->dv_rows + (size_t)t * d;
+            for (int e = 0; e < d; ++e) ok[e] = ov[e] = 0.0;
+            for (int64_t h = g * group; h < (g + 1) * group; ++h)
+                for (int64_t i = 0; i < J->sq; ++i) {
+                    /* is j in U(i)? */
+                    const int m = row_key_set(J->s, J->n_slices, i, ivs);
+                    int in = 0;
+                    for (int u = 0; u < m && !in; ++u) in = j >= ivs[u].lo && j < ivs[u].hi;
+                    if (!in) continue;
+                    double D = 0.0;
+                    const int64_t n = bwd_row(J, h, i, ivs, keys, p, o_row, &D);
+                    int64_t c = 0;
+                    while (c < n && keys[c] != j) ++c;
+                    if (c == n) continue;
+                    const size_t qi = ((size_t)i * J->hq + (size_t)h) * d;
+                    const double ds = bwd_ds(J, h, i, j, p[c], D);
+                    for (int e = 0; e < d; ++e) {
+                        ok[e] += J->scale * ds * ld(J->q, qi + e, J->bf16);
+                        ov[e] += p[c] * ld(J->dout, qi + e, J->bf16);
+                    }
+                }
+        }
+    }
+    free(o_row);
+    free(keys);
+    free(p);
+    free(ivs);
+    return NULL;
+}
+
+int32_t oracle_attn_bwd_sampled(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                                int32_t sq, int32_t sk, int32_t hq, int32_t hkv, int32_t d,
+                                const oracle_slice *slices, int32_t n_slices, double scale, const int64_t *rows,
+                                int64_t n_rows, double *dq_rows, const int64_t *keys, int64_t n_keys,
+                                double *dk_rows, double *dv_rows, int32_t n_threads)
+{
+    if (hkv <= 0 || hq % hkv != 0 || d <= 0) return -1;
+    if (n_threads < 1) n_threads = 1;
+    if (n_threads > 256) n_threads = 256;
+    pthread_t th[256];
+    bwd_sample_job jobs[256];
+    for (int t = 0; t < n_threads; ++t) {
+        bwd_job J = {q, k, v, dout, 1, sq, sk, hq, hkv, d, slices, n_slices, scale, NULL, NULL, NULL, n_threads, t};
+        bwd_sample_job S = {J, rows, keys, n_rows, n_keys, dq_rows, dk_rows, dv_rows};
+        jobs[t] = S;
+    }
+    for (int t = 1; t < n_threads; ++t) pthread_create(&th[t], NULL, bwd_sample_worker, &jobs[t]);
+    bwd_sample_worker(&jobs[0]);
+    for (int t = 1; t < n_threads; ++t) pthread_join(th[t], NULL);
+    return 0;
 }
 
 /* ---------------------------------------------------------------------------

@@ -2,9 +2,16 @@
 through the C-ABI library, on the forward kernel's own O and LSE.
 
 Tolerance (derived from the arithmetic): the kernels round P and dS to bf16 (unit
-roundoff 2^-9) before the products that accumulate the gradients, and D = rowsum(dO*O)
-takes O as the forward's bf16 output; every other step is fp32.  Per tensor the bar is
-max|diff| <= GRAD_TOL * max(1, max|reference|)."""
+roundoff u = 2^-8) before the products that accumulate the gradients, and
+D = rowsum(dO*O) takes O as the forward's bf16 output; every other step is fp32.  A
+gradient element is a sum of such rounded terms, so its error is a few u times the
+magnitude of the terms; per tensor the bar is max|diff| <= GRAD_TOL * max(1, max|ref|)
+with GRAD_TOL = 1e-2 (about 2.5 u).
+
+At the full workload sizes the oracle computes sampled rows (dQ) and keys (dK, dV),
+and one identity that holds at any size is checked on every key/value head: the
+weights of an admitted row sum to 1, so sum_j dV_j = sum over the group's rows with
+keys of dO_i, within u * sum |dO_i| (bf16 rounding of P)."""
 import numpy as np
 import pytest
 
@@ -12,7 +19,7 @@ import oracle
 from block_sparse_flash_csr_amd import api
 from block_sparse_flash_csr_amd import workloads as W
 
-from gpu_helpers import dev_bf16, say
+from gpu_helpers import dev_bf16, sample_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -137,3 +144,90 @@ def test_bwd_deterministic():
     b = run_bwd(qb, kb, vb, gb, slices, 0.09)
     for x, y in zip(a, b):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# full workload sizes, in the forward's launch configuration: sampled outputs
+# ---------------------------------------------------------------------------
+U_BF16 = 2.0 ** -8
+
+
+def full_size_run(w, plan, seed):
+    import torch
+    q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    gb = W.random_grad(np.random.default_rng(seed), w.sq, w.hq, w.d)
+    g = dev_bf16(gb)
+    say(f"{w.name}: forward + backward")
+    o, lse = api.attn_fwd(q, k, v, plan, w.scale)
+    dq, dk, dv = api.attn_bwd(q, k, v, o, g, lse, plan, w.scale)
+    torch.cuda.synchronize()
+    for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert torch.isfinite(t).all().item(), f"non-finite {name}"
+    return gb, lse, dq, dk, dv
+
+
+def check_dv_sum_identity(w, gb, lse, dv, what):
+    """sum_j dV[j, g] == sum over h in g, rows i with keys, of dO[i, h]."""
+    import torch
+    group = w.hq // w.hkv
+    has_keys = torch.isfinite(lse).cpu().numpy()          # [hq, sq]
+    do = W.bf16_to_f32(gb).astype(np.float64)             # [sq, hq, d]
+    lhs = dv.double().sum(dim=0).cpu().numpy()            # [hkv, d]
+    worst = 0.0
+    for gi in range(w.hkv):
+        rhs = np.zeros(w.d)
+        bound = np.zeros(w.d)
+        for h in range(gi * group, (gi + 1) * group):
+            m = has_keys[h]
+            rhs += do[m, h].sum(axis=0)
+            bound += np.abs(do[m, h]).sum(axis=0)
+        err = np.abs(lhs[gi] - rhs)
+        worst = max(worst, float(np.max(err / (U_BF16 * bound + 1e-6))))
+        assert np.all(err <= U_BF16 * bound + 1e-6), f"{what}: sum_j dV off for kv head {gi}"
+    say(f"{what}: sum_j dV identity holds, worst error {worst:.3f} of the bound")
+
+
+def test_config2_bwd_sampled():
+    import torch
+    w = W.config2()
+    plan = api.plan_from_workload(w)
+    gb, lse, dq, dk, dv = full_size_run(w, plan, 2002)
+    cu = [int(x) for x in w.cu_seqlens]
+    extra = cu[:-1] + [c + 1 for c in cu[:-1]] + [c - 1 for c in cu[1:]]
+    rows = sample_rows(w, 40, 22, extra)
+    rng = np.random.default_rng(23)
+    lens = np.diff(cu)
+    short = [cu[t] for t in np.argsort(lens)[:2]]                 # first keys of the shortest documents
+    kj = sorted(set([c - 1 for c in cu[1:]] + short + [c + 5 for c in short]
+                    + [int(x) for x in rng.integers(0, w.sk, 4)]))
+    keys = [(int(rng.integers(0, w.hkv)), j) for j in kj]
+    say(f"config2 backward: oracle on {len(rows)} rows and {len(keys)} keys")
+    rq, rk, rv = oracle.attn_bwd_sampled(w.q, w.k, w.v, gb, w.slices, w.scale, rows=rows, keys=keys)
+    r = np.array(rows, np.int64)
+    gq = dq[torch.from_numpy(r[:, 1]).cuda(), torch.from_numpy(r[:, 0]).cuda()].cpu().numpy()
+    kk = np.array(keys, np.int64)
+    ki, kg = torch.from_numpy(kk[:, 1]).cuda(), torch.from_numpy(kk[:, 0]).cuda()
+    gk, gv = dk[ki, kg].cpu().numpy(), dv[ki, kg].cpu().numpy()
+    check_grads((gq, gk, gv), (rq, rk, rv), "config2 backward sampled")
+    check_dv_sum_identity(w, gb, lse, dv, "config2 backward")
+    plan.close()
+
+
+def test_config4_bwd_rows_and_identity():
+    """GQA 32/8 at 65536 tokens: sampled dQ rows and the dV identity on every kv head
+    (a sampled key there would cost the oracle tens of seconds)."""
+    import torch
+    w = W.config4()
+    plan = api.plan_from_workload(w)
+    gb, lse, dq, dk, dv = full_size_run(w, plan, 2004)
+    extra = [s[0] for s in w.slices[16:30]] + [s[1] - 1 for s in w.slices[16:30]]
+    rows = sample_rows(w, 24, 44, extra)
+    rq, _, _ = oracle.attn_bwd_sampled(w.q, w.k, w.v, gb, w.slices, w.scale, rows=rows)
+    r = np.array(rows, np.int64)
+    gq = dq[torch.from_numpy(r[:, 1]).cuda(), torch.from_numpy(r[:, 0]).cuda()].cpu().numpy()
+    err = float(np.max(np.abs(gq - rq)))
+    mag = float(np.max(np.abs(rq)))
+    say(f"config4 backward sampled: max|ddQ| = {err:.3e} (max|ref| {mag:.2e})")
+    assert err <= GRAD_TOL * max(1.0, mag)
+    check_dv_sum_identity(w, gb, lse, dv, "config4 backward")
+    plan.close()

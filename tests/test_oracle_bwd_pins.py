@@ -86,3 +86,20 @@ def test_bf16_entry_equals_f64_entry():
     b = oracle.attn_bwd_f64(*f, slices, 0.3)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("seed,sq,sk,hq,hkv,d,n", [(41, 37, 29, 4, 2, 16, 4), (42, 50, 50, 3, 1, 8, 3)])
+def test_sampled_backward_equals_full_pass(seed, sq, sk, hq, hkv, d, n):
+    """The sampled gradients add the same terms in the same order as the full pass,
+    so they agree with it exactly (rows without keys and unreached keys included)."""
+    rng = np.random.default_rng(seed)
+    slices = W.random_slices(rng, sq, sk, n) + [(5, 9, 0, 0, 0)]
+    qb, kb, vb = W.random_inputs(rng, sq, sk, hq, hkv, d)
+    gb = W.random_grad(rng, sq, hq, d)
+    dq, dk, dv = oracle.attn_bwd(qb, kb, vb, gb, slices, 0.3)
+    rows = [(h, i) for h in range(hq) for i in range(sq)]
+    keys = [(g, j) for g in range(hkv) for j in range(sk)]
+    sq_, sk_, sv_ = oracle.attn_bwd_sampled(qb, kb, vb, gb, slices, 0.3, rows=rows, keys=keys)
+    assert np.array_equal(sq_, np.stack([dq[i, h] for h, i in rows]))
+    assert np.array_equal(sk_, np.stack([dk[j, g] for g, j in keys]))
+    assert np.array_equal(sv_, np.stack([dv[j, g] for g, j in keys]))
