@@ -4,7 +4,7 @@ from __future__ import annotations
 
 
 def __getattr__(name):
-    if name in ("Plan", "attn_fwd", "attn_bwd", "attn_merge", "BsfaError", "library", "plan_from_workload"):
+    if name in ("Plan", "DeviceCsr", "attn_fwd", "attn_bwd", "attn_merge", "BsfaError", "library", "plan_from_workload"):
         from . import api
         return getattr(api, name)
     raise AttributeError(name)

@@ -87,12 +87,19 @@ def library():
                                     ctypes.POINTER(Tensor), P, P]
     lib.bsfa_attn_bwd.argtypes = [ctypes.POINTER(Tensor)] * 5 + [P, I64, P, ctypes.c_float,
                                                                  P, P, P, P, P]
+    lib.bsfa_plan_export_pieces.argtypes = [P, P, P, I64]
+    lib.bsfa_dcsr_build.argtypes = [P, I32, I32, I32, I32, I32, P, PP]
+    lib.bsfa_dcsr_view_get.argtypes = [P, ctypes.POINTER(DcsrView)]
+    lib.bsfa_dcsr_export.argtypes = [P, P, P, P, P, P, I64, I64]
+    lib.bsfa_dcsr_destroy.argtypes = [P]
+    lib.bsfa_dcsr_destroy.restype = None
     lib.bsfa_status_str.argtypes = [I32]
     lib.bsfa_status_str.restype = ctypes.c_char_p
     for name in ("bsfa_plan_create", "bsfa_plan_from_varlen", "bsfa_plan_from_blocks",
                  "bsfa_plan_upload", "bsfa_plan_get_info", "bsfa_plan_export_csr",
                  "bsfa_plan_export_schedule", "bsfa_plan_export_units", "bsfa_attn_fwd",
-                 "bsfa_attn_merge", "bsfa_attn_bwd"):
+                 "bsfa_attn_merge", "bsfa_attn_bwd", "bsfa_plan_export_pieces", "bsfa_dcsr_build",
+                 "bsfa_dcsr_view_get", "bsfa_dcsr_export"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -111,6 +118,56 @@ def _stream_handle(stream=None):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+class DcsrView(ctypes.Structure):
+    _fields_ = [("row_ptr", ctypes.c_void_p), ("col", ctypes.c_void_p), ("tag", ctypes.c_void_p),
+                ("piece_ptr", ctypes.c_void_p), ("pieces", ctypes.c_void_p),
+                ("n_qtiles", ctypes.c_int32), ("n_ktiles", ctypes.c_int32),
+                ("nnz", ctypes.c_int64), ("n_full", ctypes.c_int64), ("n_partial", ctypes.c_int64),
+                ("n_pieces", ctypes.c_int64), ("pairs", ctypes.c_int64), ("touches", ctypes.c_int64)]
+
+
+class DeviceCsr:
+    """Tile CSR compiled on the GPU (bsfa_dcsr_build); `view()` waits for it."""
+
+    def __init__(self, slices, sq, sk, bq=128, bk=128, stream=None):
+        arr = (Slice * max(1, len(slices)))()
+        for t, sl in enumerate(slices):
+            arr[t] = Slice(*[int(x) for x in sl])
+        h = ctypes.c_void_p()
+        _check("bsfa_dcsr_build", library().bsfa_dcsr_build(arr, len(slices), sq, sk, bq, bk,
+                                                             _stream_handle(stream), ctypes.byref(h)))
+        self._h = h
+
+    def view(self) -> dict:
+        v = DcsrView()
+        _check("bsfa_dcsr_view_get", library().bsfa_dcsr_view_get(self._h, ctypes.byref(v)))
+        return {f: getattr(v, f) for f, _ in DcsrView._fields_}
+
+    def export(self):
+        """(row_ptr, col, tag, piece_ptr, pieces [n, 5]) as numpy arrays."""
+        v = self.view()
+        row_ptr = np.zeros(v["n_qtiles"] + 1, np.int32)
+        col = np.zeros(max(1, v["nnz"]), np.int32)
+        tag = np.zeros(max(1, v["nnz"]), np.uint8)
+        piece_ptr = np.zeros(v["nnz"] + 1, np.int32)
+        pieces = np.zeros((max(1, v["n_pieces"]), 5), np.int32)
+        _check("bsfa_dcsr_export", library().bsfa_dcsr_export(
+            self._h, _ptr(row_ptr), _ptr(col), _ptr(tag), _ptr(piece_ptr), _ptr(pieces),
+            v["nnz"], v["n_pieces"]))
+        return row_ptr, col[:v["nnz"]], tag[:v["nnz"]], piece_ptr, pieces[:v["n_pieces"]]
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            library().bsfa_dcsr_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class Plan:
@@ -183,6 +240,15 @@ class Plan:
             self.info()
         i = self._info
         return i["sq"], i["sk"], i["hq"], i["hkv"], i["d"]
+
+    def pieces(self):
+        """(piece_ptr [nnz + 1], pieces [n_pieces, 5]) of the host compiler."""
+        inf = self.info()
+        piece_ptr = np.zeros(inf["nnz"] + 1, np.int32)
+        pieces = np.zeros((max(1, inf["n_pieces"]), 5), np.int32)
+        _check("bsfa_plan_export_pieces", library().bsfa_plan_export_pieces(
+            self._h, _ptr(piece_ptr), _ptr(pieces), inf["n_pieces"]))
+        return piece_ptr, pieces[:inf["n_pieces"]]
 
     def csr(self):
         inf = self.info()

@@ -107,6 +107,23 @@ struct bsfa_plan {
     bsfa::DeviceMeta dev;
 };
 
+// A tile CSR compiled on the device (see bsfa_dcsr_build).
+struct bsfa_dcsr {
+    int device = -1;
+    int32_t n_qt = 0, n_kt = 0;
+    int64_t n_touch = 0;
+    std::vector<bsfa_slice> slices;      // host copies kept until destruction (their
+    std::vector<int32_t> pair_info;      // uploads are enqueued on the build stream)
+    std::vector<int64_t> pair_off;
+    void *buf = nullptr;
+    hipEvent_t done = nullptr;
+    const int32_t *row_ptr = nullptr, *col = nullptr, *piece_ptr = nullptr, *pieces = nullptr;
+    const uint8_t *tag = nullptr;
+    unsigned long long *totals_dev = nullptr;
+    unsigned long long totals[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    bool have_totals = false;
+};
+
 namespace bsfa {
 
 // Mask compiler: validated slices -> tile CSR with pieces and the pair count.
@@ -160,6 +177,30 @@ struct BwdArgs {
     int32_t n_entries, n_pieces;
 };
 hipError_t launch_attn_bwd(const BwdArgs &a, int d, hipStream_t stream);
+
+// Device mask compiler (same CSR as compile_mask, built on the GPU).  Keys are
+// (tile << sbits) | slice with tile = qt * n_kt + kt; the work arrays hold n_touch
+// elements (every (tile, slice) incidence), an upper bound of nnz and of n_pieces.
+struct DcsrArgs {
+    int32_t sq, sk, bq, bk, n_qt, n_kt, sbits, end_bit;
+    int64_t n_touch, n_pairs;
+    const bsfa_slice *slices;      // [n_slices]
+    const int32_t *pair_info;      // [n_pairs][4]: slice, qt, kt_lo, kt_hi
+    const int64_t *pair_off;       // [n_pairs]: first key of the pair
+    uint64_t *keys_in, *keys;      // [n_touch] unsorted / sorted
+    int32_t *flag, *seg, *e_first, *e_n, *e_pieces, *p_off;   // [n_touch]
+    uint8_t *e_full;               // [n_touch]
+    void *temp;                    // sort / scan scratch
+    size_t temp_bytes;
+    int32_t *row_ptr;              // [n_qt + 1]
+    int32_t *col;                  // [n_touch]
+    uint8_t *tag;                  // [n_touch]
+    int32_t *piece_ptr;            // [n_touch + 1]
+    Piece *pieces;                 // [n_touch]
+    unsigned long long *totals;    // [8]: nnz, n_full, n_partial, n_pieces, pairs
+};
+size_t dcsr_sort_temp_bytes(int64_t n, int32_t end_bit);
+hipError_t launch_dcsr(const DcsrArgs &a, hipStream_t stream);
 
 struct MergeArgs {
     const void *o_parts[BSFA_MERGE_MAX_PARTS];

@@ -451,6 +451,24 @@ bsfa_status bsfa_plan_export_csr(const bsfa_plan *p, int32_t *row_ptr, int32_t *
     return BSFA_OK;
 }
 
+bsfa_status bsfa_plan_export_pieces(const bsfa_plan *p, int32_t *piece_ptr, int32_t *pieces, int64_t cap)
+{
+    if (!p || !piece_ptr) return BSFA_ERR_ARG;
+    const int64_t n = (int64_t)p->pieces.size();
+    if (cap < n || (n > 0 && !pieces)) return BSFA_ERR_ARG;
+    std::memcpy(piece_ptr, p->piece_ptr.data(), p->piece_ptr.size() * sizeof(int32_t));
+    for (int64_t t = 0; t < n; ++t) {
+        const Piece &pc = p->pieces[(size_t)t];
+        int32_t *o = pieces + 5 * t;
+        o[0] = pc.q_lo;
+        o[1] = pc.q_hi;
+        o[2] = pc.k_lo;
+        o[3] = pc.k_hi;
+        o[4] = pc.diag;
+    }
+    return BSFA_OK;
+}
+
 bsfa_status bsfa_plan_export_schedule(const bsfa_plan *p, int32_t *bin_ptr, int32_t *units,
                                       float *unit_cost)
 {
@@ -665,6 +683,213 @@ bsfa_status bsfa_attn_merge(const void *const *o_parts, const float *const *lse_
     a.o_sh = o->stride_head;
     if (launch_attn_merge(a, d, (hipStream_t)stream) != hipSuccess) return BSFA_ERR_HIP;
     return BSFA_OK;
+}
+
+bsfa_status bsfa_dcsr_build(const bsfa_slice *slices, int32_t n_slices, int32_t sq, int32_t sk, int32_t bq,
+                            int32_t bk, void *stream, bsfa_dcsr **out)
+{
+    if (!out) return BSFA_ERR_ARG;
+    *out = nullptr;
+    if (n_slices < 0 || (n_slices > 0 && !slices)) return BSFA_ERR_ARG;
+    if (sq < 0 || sk < 0 || bq <= 0 || bk <= 0 || sq >= (1 << 30) || sk >= (1 << 30)) return BSFA_ERR_ARG;
+    bsfa_status st = check_slices(slices, n_slices, sq, sk);
+    if (st != BSFA_OK) return st;
+    if (bk > 256 || n_slices >= (1 << 24)) return BSFA_ERR_UNSUPPORTED;
+    const int32_t n_qt = (int32_t)(((int64_t)sq + bq - 1) / bq), n_kt = (int32_t)(((int64_t)sk + bk - 1) / bk);
+    int32_t sbits = 1;
+    while (sbits < 24 && (1 << sbits) < n_slices) ++sbits;
+    int32_t tbits = 1;
+    const uint64_t n_tiles = (uint64_t)n_qt * (uint64_t)n_kt;
+    while (tbits < 63 && (1ull << tbits) < n_tiles) ++tbits;
+    if (tbits + sbits > 64) return BSFA_ERR_UNSUPPORTED;
+    bsfa_dcsr *c = new (std::nothrow) bsfa_dcsr;
+    if (!c) return BSFA_ERR_OOM;
+    c->n_qt = n_qt;
+    c->n_kt = n_kt;
+    // (slice, query tile) pairs and the key tiles each reaches: the host compiler's walk
+    try {
+        c->slices.assign(slices, slices + n_slices);
+        int64_t total = 0;
+        for (int32_t s = 0; s < n_slices; ++s) {
+            const bsfa_slice &sl = slices[s];
+            if (sl.q0 >= sl.q1 || sl.k0 >= sl.k1) continue;
+            const int64_t diag = sl.type == BSFA_CAUSAL ? (int64_t)sl.k1 - sl.q1 : kDiagFull;
+            for (int64_t qt = sl.q0 / bq; qt * bq < sl.q1; ++qt) {
+                const int64_t r1 = std::min<int64_t>(qt * bq + bq, sq);
+                const int64_t b = std::min<int64_t>(sl.q1, r1);
+                const int64_t j_lo = sl.k0, j_hi = std::min<int64_t>(b - 1 + diag + 1, sl.k1);
+                if (j_lo >= j_hi) continue;
+                const int64_t kt_lo = j_lo / bk, kt_hi = (j_hi + bk - 1) / bk;
+                c->pair_info.insert(c->pair_info.end(), {s, (int32_t)qt, (int32_t)kt_lo, (int32_t)kt_hi});
+                c->pair_off.push_back(total);
+                total += kt_hi - kt_lo;
+            }
+        }
+        c->n_touch = total;
+    } catch (const std::bad_alloc &) {
+        delete c;
+        return BSFA_ERR_OOM;
+    }
+    if (c->n_touch >= INT32_MAX) {
+        delete c;
+        return BSFA_ERR_UNSUPPORTED;
+    }
+    const int64_t n = c->n_touch, n_pairs = (int64_t)c->pair_off.size();
+    const size_t temp = n > 0 ? dcsr_sort_temp_bytes(n, tbits + sbits) : 0;
+    // one device buffer, 256-byte aligned sections
+    size_t off = 0;
+    auto place = [&](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return at;
+    };
+    const size_t nn = (size_t)std::max<int64_t>(n, 1);
+    const size_t o_tot = place(8 * sizeof(unsigned long long));
+    const size_t o_row = place(((size_t)n_qt + 1) * 4), o_col = place(nn * 4), o_tag = place(nn);
+    const size_t o_pp = place((nn + 1) * 4), o_pc = place(nn * sizeof(Piece));
+    const size_t o_sl = place((size_t)std::max(n_slices, 1) * sizeof(bsfa_slice));
+    const size_t o_pi = place((size_t)std::max<int64_t>(n_pairs, 1) * 16), o_po = place((size_t)std::max<int64_t>(n_pairs, 1) * 8);
+    const size_t o_k0 = place(nn * 8), o_k1 = place(nn * 8);
+    const size_t o_fl = place(nn * 4), o_sg = place(nn * 4), o_ef = place(nn * 4), o_en = place(nn * 4);
+    const size_t o_ep = place(nn * 4), o_po2 = place(nn * 4), o_eu = place(nn), o_tmp = place(std::max<size_t>(temp, 1));
+    if (hipGetDevice(&c->device) != hipSuccess) {
+        delete c;
+        return BSFA_ERR_HIP;
+    }
+    void *buf = nullptr;
+    if (hipMalloc(&buf, off) != hipSuccess) {
+        (void)hipGetLastError();
+        delete c;
+        return BSFA_ERR_OOM;
+    }
+    c->buf = buf;
+    char *b = (char *)buf;
+    if (hipEventCreateWithFlags(&c->done, hipEventDisableTiming) != hipSuccess) {
+        bsfa_dcsr_destroy(c);
+        return BSFA_ERR_HIP;
+    }
+    const hipStream_t s = (hipStream_t)stream;
+    DcsrArgs a{};
+    a.sq = sq;
+    a.sk = sk;
+    a.bq = bq;
+    a.bk = bk;
+    a.n_qt = n_qt;
+    a.n_kt = n_kt;
+    a.sbits = sbits;
+    a.end_bit = tbits + sbits;
+    a.n_touch = n;
+    a.n_pairs = n_pairs;
+    a.slices = (const bsfa_slice *)(b + o_sl);
+    a.pair_info = (const int32_t *)(b + o_pi);
+    a.pair_off = (const int64_t *)(b + o_po);
+    a.keys_in = (uint64_t *)(b + o_k0);
+    a.keys = (uint64_t *)(b + o_k1);
+    a.flag = (int32_t *)(b + o_fl);
+    a.seg = (int32_t *)(b + o_sg);
+    a.e_first = (int32_t *)(b + o_ef);
+    a.e_n = (int32_t *)(b + o_en);
+    a.e_pieces = (int32_t *)(b + o_ep);
+    a.p_off = (int32_t *)(b + o_po2);
+    a.e_full = (uint8_t *)(b + o_eu);
+    a.temp = b + o_tmp;
+    a.temp_bytes = temp;
+    a.row_ptr = (int32_t *)(b + o_row);
+    a.col = (int32_t *)(b + o_col);
+    a.tag = (uint8_t *)(b + o_tag);
+    a.piece_ptr = (int32_t *)(b + o_pp);
+    a.pieces = (Piece *)(b + o_pc);
+    a.totals = (unsigned long long *)(b + o_tot);
+    c->row_ptr = a.row_ptr;
+    c->col = a.col;
+    c->tag = a.tag;
+    c->piece_ptr = a.piece_ptr;
+    c->pieces = (const int32_t *)a.pieces;
+    c->totals_dev = a.totals;
+    bool ok = true;
+    if (n_slices > 0)
+        ok = ok && hipMemcpyAsync((void *)a.slices, c->slices.data(), (size_t)n_slices * sizeof(bsfa_slice),
+                                  hipMemcpyHostToDevice, s) == hipSuccess;
+    if (n_pairs > 0) {
+        ok = ok && hipMemcpyAsync((void *)a.pair_info, c->pair_info.data(), (size_t)n_pairs * 16,
+                                  hipMemcpyHostToDevice, s) == hipSuccess;
+        ok = ok && hipMemcpyAsync((void *)a.pair_off, c->pair_off.data(), (size_t)n_pairs * 8,
+                                  hipMemcpyHostToDevice, s) == hipSuccess;
+    }
+    ok = ok && launch_dcsr(a, s) == hipSuccess;
+    ok = ok && hipEventRecord(c->done, s) == hipSuccess;
+    if (!ok) {
+        (void)hipGetLastError();
+        bsfa_dcsr_destroy(c);
+        return BSFA_ERR_HIP;
+    }
+    *out = c;
+    return BSFA_OK;
+}
+
+bsfa_status bsfa_dcsr_view_get(bsfa_dcsr *c, bsfa_dcsr_view *v)
+{
+    if (!c || !v) return BSFA_ERR_ARG;
+    if (!c->have_totals) {
+        if (hipEventSynchronize(c->done) != hipSuccess) return BSFA_ERR_HIP;
+        if (hipMemcpy(c->totals, c->totals_dev, sizeof(c->totals), hipMemcpyDeviceToHost) != hipSuccess)
+            return BSFA_ERR_HIP;
+        c->have_totals = true;
+    }
+    v->row_ptr = c->row_ptr;
+    v->col = c->col;
+    v->tag = c->tag;
+    v->piece_ptr = c->piece_ptr;
+    v->pieces = c->pieces;
+    v->n_qtiles = c->n_qt;
+    v->n_ktiles = c->n_kt;
+    v->nnz = (int64_t)c->totals[0];
+    v->n_full = (int64_t)c->totals[1];
+    v->n_partial = (int64_t)c->totals[2];
+    v->n_pieces = (int64_t)c->totals[3];
+    v->pairs = (int64_t)c->totals[4];
+    v->touches = c->n_touch;
+    return BSFA_OK;
+}
+
+bsfa_status bsfa_dcsr_export(bsfa_dcsr *c, int32_t *row_ptr, int32_t *col, uint8_t *tag, int32_t *piece_ptr,
+                             int32_t *pieces, int64_t cap_nnz, int64_t cap_pieces)
+{
+    bsfa_dcsr_view v;
+    const bsfa_status st = bsfa_dcsr_view_get(c, &v);
+    if (st != BSFA_OK) return st;
+    if (!row_ptr || !piece_ptr || cap_nnz < v.nnz || cap_pieces < v.n_pieces) return BSFA_ERR_ARG;
+    if (v.nnz > 0 && (!col || !tag)) return BSFA_ERR_ARG;
+    if (v.n_pieces > 0 && !pieces) return BSFA_ERR_ARG;
+    bool ok = hipMemcpy(row_ptr, v.row_ptr, ((size_t)v.n_qtiles + 1) * 4, hipMemcpyDeviceToHost) == hipSuccess;
+    ok = ok && hipMemcpy(piece_ptr, v.piece_ptr, ((size_t)v.nnz + 1) * 4, hipMemcpyDeviceToHost) == hipSuccess;
+    if (v.nnz > 0) {
+        ok = ok && hipMemcpy(col, v.col, (size_t)v.nnz * 4, hipMemcpyDeviceToHost) == hipSuccess;
+        ok = ok && hipMemcpy(tag, v.tag, (size_t)v.nnz, hipMemcpyDeviceToHost) == hipSuccess;
+    }
+    if (v.n_pieces > 0) {
+        std::vector<int32_t> raw;
+        try {
+            raw.resize((size_t)v.n_pieces * 8);
+        } catch (const std::bad_alloc &) {
+            return BSFA_ERR_OOM;
+        }
+        ok = ok && hipMemcpy(raw.data(), v.pieces, raw.size() * 4, hipMemcpyDeviceToHost) == hipSuccess;
+        for (int64_t t = 0; ok && t < v.n_pieces; ++t)
+            for (int f = 0; f < 5; ++f) pieces[5 * t + f] = raw[(size_t)(8 * t + f)];
+    }
+    return ok ? BSFA_OK : BSFA_ERR_HIP;
+}
+
+void bsfa_dcsr_destroy(bsfa_dcsr *c)
+{
+    if (!c) return;
+    if (c->done) {
+        (void)hipEventSynchronize(c->done);
+        (void)hipEventDestroy(c->done);
+    }
+    if (c->buf) (void)hipFree(c->buf);
+    delete c;
 }
 
 const char *bsfa_status_str(bsfa_status s)

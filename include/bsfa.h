@@ -161,6 +161,15 @@ bsfa_status bsfa_plan_export_schedule(const bsfa_plan *plan, int32_t *bin_ptr, i
  * at most 16 parts of contiguous entries with about equal cost. */
 bsfa_status bsfa_plan_export_units(const bsfa_plan *plan, int32_t *units);
 
+/* Copy out the pieces of the partial tiles: piece_ptr [nnz + 1] (pieces of entry e are
+ * piece_ptr[e] .. piece_ptr[e + 1] - 1; a full tile has none) and pieces
+ * [n_pieces][5] = {q_lo, q_hi, k_lo, k_hi, diag}: the piece admits (i, j) iff
+ * q_lo <= i < q_hi, k_lo <= j < k_hi and j <= i + diag (a full slice stores
+ * diag = 2^30).  Host memory; cap is the capacity of pieces in pieces.  Returns
+ * BSFA_ERR_ARG if cap < n_pieces or a pointer is NULL. */
+bsfa_status bsfa_plan_export_pieces(const bsfa_plan *plan, int32_t *piece_ptr, int32_t *pieces,
+                                    int64_t cap);
+
 /* Cost of one tile under the scheduler's model ([UA] 4.1: full = 1, causal/partial =
  * w_partial, empty = 0) and the page's imbalance bound ceil(avg)/avg - 1 for a total
  * cost split over n_bins units of integral capacity. */
@@ -231,6 +240,54 @@ bsfa_status bsfa_attn_merge(const void *const *o_parts, const float *const *lse_
                             int64_t part_stride_tok, int64_t part_stride_head,
                             int64_t lse_stride_head, int32_t n_tok, int32_t n_head, int32_t d,
                             bsfa_tensor *o, float *lse, void *stream);
+
+/* ---- device mask compiler ------------------------------------------------------
+ * The tile CSR of a slice mask built on the GPU ([MA] "Blackwell adaptation": block-
+ * sparse mask generation without instantiating a dense mask, CSR mask metadata; [UA] 3
+ * block classes, 3.3 skip Empty blocks).  Its arrays equal, entry for entry, those of a
+ * plan made from the same slices and tile sizes (bsfa_plan_export_csr /
+ * bsfa_plan_export_pieces): per query tile the non-empty key tiles in ascending order,
+ * tagged full when one slice or the union of the slices admits every in-range pair of
+ * the tile, else partial with the tile's clipped slices in ascending slice order.
+ *
+ * bsfa_dcsr_build validates the slices on the host (as bsfa_plan_create), lists every
+ * (slice, query tile) pair with the key tiles it reaches (host work proportional to the
+ * number of such pairs), allocates one device buffer on the current device and enqueues
+ * the compile on `stream` (a hipStream_t, NULL = the default stream); it does not wait
+ * for the GPU.  The work is proportional to the (tile, slice) incidences ("touches").
+ * Limits: bk <= 256, n_slices < 2^24, touches < 2^31, and the key
+ * (query tile * n_ktiles + key tile) * 2^ceil(log2 n_slices) must fit in 64 bits
+ * (else BSFA_ERR_UNSUPPORTED).  Errors: BSFA_ERR_ARG, BSFA_ERR_MASK as
+ * bsfa_plan_create; BSFA_ERR_OOM; BSFA_ERR_HIP for a failed allocation, copy or launch.
+ *
+ * bsfa_dcsr_view_get waits for the compile and fills `view` with device pointers into
+ * the object's buffer and the totals (one small device-to-host copy the first time).
+ * bsfa_dcsr_destroy waits for the compile and frees the buffer; views die with it. */
+typedef struct bsfa_dcsr bsfa_dcsr;
+
+typedef struct {
+    const int32_t *row_ptr;    /* [n_qtiles + 1], device */
+    const int32_t *col;        /* [nnz], device */
+    const uint8_t *tag;        /* [nnz], device: BSFA_TILE_FULL / BSFA_TILE_PARTIAL */
+    const int32_t *piece_ptr;  /* [nnz + 1], device */
+    const int32_t *pieces;     /* [n_pieces][8], device: q_lo, q_hi, k_lo, k_hi, diag, 0, 0, 0 */
+    int32_t n_qtiles, n_ktiles;
+    int64_t nnz, n_full, n_partial, n_pieces;
+    int64_t pairs;             /* admitted (query, key) pairs of one head */
+    int64_t touches;           /* (tile, slice) incidences the compile expanded */
+} bsfa_dcsr_view;
+
+bsfa_status bsfa_dcsr_build(const bsfa_slice *slices, int32_t n_slices, int32_t sq, int32_t sk,
+                            int32_t bq, int32_t bk, void *stream, bsfa_dcsr **out);
+bsfa_status bsfa_dcsr_view_get(bsfa_dcsr *csr, bsfa_dcsr_view *view);
+/* Waits for the compile and copies its arrays to host memory in the layouts of
+ * bsfa_plan_export_csr and bsfa_plan_export_pieces: row_ptr [n_qtiles + 1], col and tag
+ * [nnz], piece_ptr [nnz + 1], pieces [n_pieces][5].  cap_nnz / cap_pieces are the
+ * capacities of col, tag / pieces; BSFA_ERR_ARG if too small or a pointer is NULL
+ * (pieces may be NULL when n_pieces is 0). */
+bsfa_status bsfa_dcsr_export(bsfa_dcsr *csr, int32_t *row_ptr, int32_t *col, uint8_t *tag,
+                             int32_t *piece_ptr, int32_t *pieces, int64_t cap_nnz, int64_t cap_pieces);
+void bsfa_dcsr_destroy(bsfa_dcsr *csr);
 
 const char *bsfa_status_str(bsfa_status status);
 

@@ -146,3 +146,18 @@ def test_backward_rejects_bad_arguments():
     assert call(p, lse=None) == 1      # no LSE
     assert call(p, delta=None) == 1    # no delta scratch
     assert call(p) == 8                # not uploaded
+
+
+def test_device_compiler_rejects_bad_arguments():
+    """Checks of bsfa_dcsr_build that fail before any HIP call."""
+    lib = api.library()
+    h = ctypes.c_void_p()
+    one = (api.Slice * 1)(api.Slice(0, 10, 0, 10, 0))
+    assert lib.bsfa_dcsr_build(one, 1, 10, 10, 128, 512, None, ctypes.byref(h)) == 4   # bk > 256
+    bad = (api.Slice * 1)(api.Slice(0, 10, 0, 20, 0))
+    assert lib.bsfa_dcsr_build(bad, 1, 10, 10, 128, 128, None, ctypes.byref(h)) == 5   # k1 > sk
+    bad = (api.Slice * 1)(api.Slice(0, 10, 0, 10, 3))
+    assert lib.bsfa_dcsr_build(bad, 1, 10, 10, 128, 128, None, ctypes.byref(h)) == 5   # unknown type
+    assert lib.bsfa_dcsr_build(one, 1, 10, 10, 0, 128, None, ctypes.byref(h)) == 1     # bq = 0
+    assert lib.bsfa_dcsr_build(one, 1, 10, 10, 128, 128, None, None) == 1              # no out
+    assert lib.bsfa_dcsr_build(None, 1, 10, 10, 128, 128, None, ctypes.byref(h)) == 1  # no slices

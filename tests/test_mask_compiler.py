@@ -94,3 +94,40 @@ def test_blocks_and_varlen_forms_match_slices():
         sl = [(int(cu[i]), int(cu[i + 1]), int(cu[i]), int(cu[i + 1]), 1 if causal else 0)
               for i in range(len(cu) - 1) if cu[i + 1] > cu[i]]
         _compare(plan, sl, 777, 777, 128, 128)
+
+
+def _piece_mask(pieces, r0, r1, c0, c1):
+    m = np.zeros((r1 - r0, c1 - c0), bool)
+    for q_lo, q_hi, k_lo, k_hi, diag in pieces:
+        for i in range(q_lo, q_hi):
+            hi = min(k_hi, i + diag + 1)
+            if k_lo < hi:
+                m[i - r0, k_lo - c0:hi - c0] = True
+    return m
+
+
+@pytest.mark.parametrize("bq,bk", [(16, 16), (32, 64), (128, 128), (7, 13)])
+def test_pieces_reproduce_the_mask_of_partial_tiles(bq, bk):
+    """Inside every partial tile the union of its stored pieces admits exactly the pairs
+    of the oracle's row key sets (and every full tile admits all of its pairs)."""
+    rng = np.random.default_rng(7 * bq + bk)
+    for _ in range(6):
+        sq, sk = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+        slices = W.random_slices(rng, sq, sk, int(rng.integers(1, 7)))
+        plan = api.Plan.from_slices(slices, sq, sk, 1, 1, 64, bq=bq, bk=bk)
+        rp, col, tag = plan.csr()
+        pp, pcs = plan.pieces()
+        dense = np.zeros((sq, sk), bool)
+        for i in range(sq):
+            for lo, hi in oracle.row_key_set(slices, i):
+                dense[i, lo:hi] = True
+        for qt in range(len(rp) - 1):
+            r0, r1 = qt * bq, min(qt * bq + bq, sq)
+            for e in range(rp[qt], rp[qt + 1]):
+                c0, c1 = col[e] * bk, min(col[e] * bk + bk, sk)
+                want = dense[r0:r1, c0:c1]
+                if tag[e] == 1:
+                    assert want.all() and pp[e] == pp[e + 1]
+                else:
+                    got = _piece_mask(pcs[pp[e]:pp[e + 1]], r0, r1, c0, c1)
+                    assert np.array_equal(got, want), (qt, col[e])
