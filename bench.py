@@ -173,6 +173,39 @@ def other_workloads(api, W, reps=10):
     del q, k, v, g, o, lse, dq, dk, dv, delta
     torch.cuda.empty_cache()
 
+    # Mask compile: host plan creation (compile + column view + schedule) against the
+    # device compiler's tile CSR (host pair listing, allocation, upload and kernels, wall
+    # time to a finished CSR; events time the part on the stream).  Both take the slice
+    # array in its C layout.
+    mc = {}
+    S = 524288
+    cases = [("varlen_causal_t16384_docs8", W.config2(with_inputs=False).slices, 16384),
+             ("causal_s524288", [(0, S, 0, S, 1)], S),
+             ("strided_blocks_s524288", W.block_slices(W.strided_block_codes(S // 128, 8), 128, 128, S, S), S)]
+    for name, sl, s_ in cases:
+        sl = api.slice_array(sl)               # int32 [n, 5], the C layout, built untimed
+        t0 = time.perf_counter()
+        hp = api.Plan.from_slices(sl, s_, s_, 16, 16, 128)
+        host_ms = (time.perf_counter() - t0) * 1e3
+        nnz = hp.info()["nnz"]
+        hp.close()
+        api.DeviceCsr(sl, s_, s_).close()      # warm (first-use costs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        dc = api.DeviceCsr(sl, s_, s_, stream=stream)
+        e1.record(stream)
+        v = dc.view()
+        dev_ms = (time.perf_counter() - t0) * 1e3
+        assert v["nnz"] == nnz
+        mc[name] = {"slices": len(sl), "nnz": nnz, "touches": v["touches"], "host_plan_ms": host_ms,
+                    "device_csr_ms": dev_ms, "device_stream_ms": e0.elapsed_time(e1)}
+        log(f"mask compile {name}: host plan {host_ms:.1f} ms, device CSR {dev_ms:.2f} ms "
+            f"(stream {e0.elapsed_time(e1):.2f} ms), nnz {nnz}")
+        dc.close()
+    out["mask_compile"] = mc
+
     # Few query rows against a long context (a prefill chunk): 1 query tile x 32 heads is
     # 32 items for 512 workgroup slots, so the plan splits every row's key range into
     # parts whose partial results a second kernel merges inside the same call.

@@ -114,6 +114,14 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
+def slice_array(slices) -> np.ndarray:
+    """Slices (q0, q1, k0, k1, type) as a contiguous int32 [n, 5] array (bsfa_slice layout)."""
+    arr = np.ascontiguousarray(np.asarray(slices, dtype=np.int64).reshape(-1, 5))
+    if arr.size and (arr.min() < np.iinfo(np.int32).min or arr.max() > np.iinfo(np.int32).max):
+        raise ValueError("slice bounds must fit in int32")
+    return np.ascontiguousarray(arr.astype(np.int32))
+
+
 def _stream_handle(stream=None):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -132,11 +140,9 @@ class DeviceCsr:
     """Tile CSR compiled on the GPU (bsfa_dcsr_build); `view()` waits for it."""
 
     def __init__(self, slices, sq, sk, bq=128, bk=128, stream=None):
-        arr = (Slice * max(1, len(slices)))()
-        for t, sl in enumerate(slices):
-            arr[t] = Slice(*[int(x) for x in sl])
+        arr = slice_array(slices)
         h = ctypes.c_void_p()
-        _check("bsfa_dcsr_build", library().bsfa_dcsr_build(arr, len(slices), sq, sk, bq, bk,
+        _check("bsfa_dcsr_build", library().bsfa_dcsr_build(_ptr(arr), len(arr), sq, sk, bq, bk,
                                                              _stream_handle(stream), ctypes.byref(h)))
         self._h = h
 
@@ -180,11 +186,9 @@ class Plan:
     # -- constructors ---------------------------------------------------------
     @classmethod
     def from_slices(cls, slices, sq, sk, hq, hkv, d, bq=128, bk=128):
-        arr = (Slice * max(1, len(slices)))()
-        for t, s in enumerate(slices):
-            arr[t] = Slice(*[int(x) for x in s])
+        arr = slice_array(slices)
         h = ctypes.c_void_p()
-        _check("bsfa_plan_create", library().bsfa_plan_create(arr, len(slices), sq, sk, hq, hkv, d,
+        _check("bsfa_plan_create", library().bsfa_plan_create(_ptr(arr), len(arr), sq, sk, hq, hkv, d,
                                                                bq, bk, ctypes.byref(h)))
         return cls(h)
 

@@ -112,9 +112,6 @@ struct bsfa_dcsr {
     int device = -1;
     int32_t n_qt = 0, n_kt = 0;
     int64_t n_touch = 0;
-    std::vector<bsfa_slice> slices;      // host copies kept until destruction (their
-    std::vector<int32_t> pair_info;      // uploads are enqueued on the build stream)
-    std::vector<int64_t> pair_off;
     void *buf = nullptr;
     hipEvent_t done = nullptr;
     const int32_t *row_ptr = nullptr, *col = nullptr, *piece_ptr = nullptr, *pieces = nullptr;

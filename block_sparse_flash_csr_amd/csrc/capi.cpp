@@ -702,16 +702,11 @@ bsfa_status bsfa_dcsr_build(const bsfa_slice *slices, int32_t n_slices, int32_t 
     const uint64_t n_tiles = (uint64_t)n_qt * (uint64_t)n_kt;
     while (tbits < 63 && (1ull << tbits) < n_tiles) ++tbits;
     if (tbits + sbits > 64) return BSFA_ERR_UNSUPPORTED;
-    bsfa_dcsr *c = new (std::nothrow) bsfa_dcsr;
-    if (!c) return BSFA_ERR_OOM;
-    c->n_qt = n_qt;
-    c->n_kt = n_kt;
-    // (slice, query tile) pairs and the key tiles each reaches: the host compiler's walk
-    try {
-        c->slices.assign(slices, slices + n_slices);
-        int64_t total = 0;
-        for (int32_t s = 0; s < n_slices; ++s) {
-            const bsfa_slice &sl = slices[s];
+    // (slice, query tile) pairs and the key tiles each reaches (the host compiler's walk):
+    // counted first, then written straight into a pinned staging image
+    auto walk = [&](auto &&emit) {
+        for (int32_t sx = 0; sx < n_slices; ++sx) {
+            const bsfa_slice &sl = slices[sx];
             if (sl.q0 >= sl.q1 || sl.k0 >= sl.k1) continue;
             const int64_t diag = sl.type == BSFA_CAUSAL ? (int64_t)sl.k1 - sl.q1 : kDiagFull;
             for (int64_t qt = sl.q0 / bq; qt * bq < sl.q1; ++qt) {
@@ -719,52 +714,76 @@ bsfa_status bsfa_dcsr_build(const bsfa_slice *slices, int32_t n_slices, int32_t 
                 const int64_t b = std::min<int64_t>(sl.q1, r1);
                 const int64_t j_lo = sl.k0, j_hi = std::min<int64_t>(b - 1 + diag + 1, sl.k1);
                 if (j_lo >= j_hi) continue;
-                const int64_t kt_lo = j_lo / bk, kt_hi = (j_hi + bk - 1) / bk;
-                c->pair_info.insert(c->pair_info.end(), {s, (int32_t)qt, (int32_t)kt_lo, (int32_t)kt_hi});
-                c->pair_off.push_back(total);
-                total += kt_hi - kt_lo;
+                emit(sx, qt, j_lo / bk, (j_hi + bk - 1) / bk);
             }
         }
-        c->n_touch = total;
-    } catch (const std::bad_alloc &) {
-        delete c;
-        return BSFA_ERR_OOM;
-    }
-    if (c->n_touch >= INT32_MAX) {
-        delete c;
-        return BSFA_ERR_UNSUPPORTED;
-    }
-    const int64_t n = c->n_touch, n_pairs = (int64_t)c->pair_off.size();
-    const size_t temp = n > 0 ? dcsr_sort_temp_bytes(n, tbits + sbits) : 0;
-    // one device buffer, 256-byte aligned sections
+    };
+    int64_t n_pairs = 0, n = 0;
+    walk([&](int32_t, int64_t, int64_t lo, int64_t hi) {
+        ++n_pairs;
+        n += hi - lo;
+    });
+    if (n >= INT32_MAX) return BSFA_ERR_UNSUPPORTED;
+    // staging image = the head of the device buffer: slices | pair_info | pair_off
     size_t off = 0;
     auto place = [&](size_t bytes) {
         const size_t at = off;
         off += (bytes + 255) & ~(size_t)255;
         return at;
     };
+    const size_t o_sl = place((size_t)std::max(n_slices, 1) * sizeof(bsfa_slice));
+    const size_t o_pi = place((size_t)std::max<int64_t>(n_pairs, 1) * 16);
+    const size_t o_po = place((size_t)std::max<int64_t>(n_pairs, 1) * 8);
+    const size_t image_bytes = off;
     const size_t nn = (size_t)std::max<int64_t>(n, 1);
     const size_t o_tot = place(8 * sizeof(unsigned long long));
     const size_t o_row = place(((size_t)n_qt + 1) * 4), o_col = place(nn * 4), o_tag = place(nn);
     const size_t o_pp = place((nn + 1) * 4), o_pc = place(nn * sizeof(Piece));
-    const size_t o_sl = place((size_t)std::max(n_slices, 1) * sizeof(bsfa_slice));
-    const size_t o_pi = place((size_t)std::max<int64_t>(n_pairs, 1) * 16), o_po = place((size_t)std::max<int64_t>(n_pairs, 1) * 8);
     const size_t o_k0 = place(nn * 8), o_k1 = place(nn * 8);
     const size_t o_fl = place(nn * 4), o_sg = place(nn * 4), o_ef = place(nn * 4), o_en = place(nn * 4);
-    const size_t o_ep = place(nn * 4), o_po2 = place(nn * 4), o_eu = place(nn), o_tmp = place(std::max<size_t>(temp, 1));
-    if (hipGetDevice(&c->device) != hipSuccess) {
-        delete c;
-        return BSFA_ERR_HIP;
+    const size_t o_ep = place(nn * 4), o_po2 = place(nn * 4), o_eu = place(nn);
+    const size_t temp = n > 0 ? dcsr_sort_temp_bytes(n, tbits + sbits) : 0;
+    const size_t o_tmp = place(std::max<size_t>(temp, 1));
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BSFA_ERR_HIP;
+    Staging *stg = nullptr;
+    bsfa_status sst = staging_acquire(dev, image_bytes, &stg);
+    if (sst != BSFA_OK) return sst;
+    {
+        uint8_t *h = (uint8_t *)stg->host;
+        if (n_slices > 0) std::memcpy(h + o_sl, slices, (size_t)n_slices * sizeof(bsfa_slice));
+        int32_t *pi = (int32_t *)(h + o_pi);
+        int64_t *po = (int64_t *)(h + o_po);
+        int64_t k = 0, total = 0;
+        walk([&](int32_t sx, int64_t qt, int64_t lo, int64_t hi) {
+            pi[4 * k] = sx;
+            pi[4 * k + 1] = (int32_t)qt;
+            pi[4 * k + 2] = (int32_t)lo;
+            pi[4 * k + 3] = (int32_t)hi;
+            po[k++] = total;
+            total += hi - lo;
+        });
     }
+    bsfa_dcsr *c = new (std::nothrow) bsfa_dcsr;
+    if (!c) {
+        staging_release_now(stg);
+        return BSFA_ERR_OOM;
+    }
+    c->device = dev;
+    c->n_qt = n_qt;
+    c->n_kt = n_kt;
+    c->n_touch = n;
     void *buf = nullptr;
     if (hipMalloc(&buf, off) != hipSuccess) {
         (void)hipGetLastError();
+        staging_release_now(stg);
         delete c;
         return BSFA_ERR_OOM;
     }
     c->buf = buf;
     char *b = (char *)buf;
     if (hipEventCreateWithFlags(&c->done, hipEventDisableTiming) != hipSuccess) {
+        staging_release_now(stg);
         bsfa_dcsr_destroy(c);
         return BSFA_ERR_HIP;
     }
@@ -806,16 +825,10 @@ bsfa_status bsfa_dcsr_build(const bsfa_slice *slices, int32_t n_slices, int32_t 
     c->piece_ptr = a.piece_ptr;
     c->pieces = (const int32_t *)a.pieces;
     c->totals_dev = a.totals;
-    bool ok = true;
-    if (n_slices > 0)
-        ok = ok && hipMemcpyAsync((void *)a.slices, c->slices.data(), (size_t)n_slices * sizeof(bsfa_slice),
-                                  hipMemcpyHostToDevice, s) == hipSuccess;
-    if (n_pairs > 0) {
-        ok = ok && hipMemcpyAsync((void *)a.pair_info, c->pair_info.data(), (size_t)n_pairs * 16,
-                                  hipMemcpyHostToDevice, s) == hipSuccess;
-        ok = ok && hipMemcpyAsync((void *)a.pair_off, c->pair_off.data(), (size_t)n_pairs * 8,
-                                  hipMemcpyHostToDevice, s) == hipSuccess;
-    }
+    // the pinned image stays reserved until the copy recorded behind it has run
+    bool ok = hipMemcpyAsync(b, stg->host, image_bytes, hipMemcpyHostToDevice, s) == hipSuccess &&
+              hipEventRecord(stg->copied, s) == hipSuccess;
+    if (!ok) staging_release_now(stg);
     ok = ok && launch_dcsr(a, s) == hipSuccess;
     ok = ok && hipEventRecord(c->done, s) == hipSuccess;
     if (!ok) {

@@ -79,15 +79,11 @@ __device__ int64_t piece_pairs(const bsfa_slice &s, int64_t r0, int64_t r1, int6
     return total;
 }
 
-// Per entry (one thread per head of an equal-tile run): full / partial and counts.
-__global__ void entry_kernel(const uint64_t *__restrict__ keys, const int32_t *__restrict__ flag,
-                             const int32_t *__restrict__ seg, int64_t n, Geometry g,
-                             const bsfa_slice *__restrict__ slices, int32_t *__restrict__ e_first,
-                             int32_t *__restrict__ e_n, uint8_t *__restrict__ e_full,
-                             int32_t *__restrict__ e_pieces, unsigned long long *__restrict__ totals)
+__device__ void entry_one(const uint64_t *__restrict__ keys, const int32_t *__restrict__ seg, int64_t t, int64_t n,
+                          const Geometry &g, const bsfa_slice *__restrict__ slices, int32_t *__restrict__ e_first,
+                          int32_t *__restrict__ e_n, uint8_t *__restrict__ e_full, int32_t *__restrict__ e_pieces,
+                          unsigned long long &n_full, unsigned long long &n_part, unsigned long long &n_pairs)
 {
-    const int64_t t = (int64_t)blockIdx.x * kThreadsDev + threadIdx.x;
-    if (t >= n || !flag[t]) return;
     const uint64_t smask = (1ull << g.sbits) - 1ull;
     const uint64_t tile = keys[t] >> g.sbits;
     const int64_t qt = (int64_t)(tile / (uint64_t)g.n_kt), kt = (int64_t)(tile % (uint64_t)g.n_kt);
@@ -136,8 +132,41 @@ __global__ void entry_kernel(const uint64_t *__restrict__ keys, const int32_t *_
     e_n[e] = cnt;
     e_full[e] = full ? 1 : 0;
     e_pieces[e] = full ? 0 : cnt;
-    atomicAdd(&totals[full ? 1 : 2], 1ull);
-    atomicAdd(&totals[4], (unsigned long long)pairs);
+    (full ? n_full : n_part) = 1;
+    n_pairs = (unsigned long long)pairs;
+}
+
+// Sum over the workgroup, left in thread 0 (every thread must call it).
+__device__ void block_sum(unsigned long long &x)
+{
+    __shared__ unsigned long long part[kThreadsDev / 64];
+    for (int w = 32; w >= 1; w >>= 1) x += __shfl_xor(x, w, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        for (int w = 1; w < kThreadsDev / 64; ++w) x += part[w];
+}
+
+// Per entry (one thread per head of an equal-tile run): full / partial and counts.
+__global__ void entry_kernel(const uint64_t *__restrict__ keys, const int32_t *__restrict__ flag,
+                             const int32_t *__restrict__ seg, int64_t n, Geometry g,
+                             const bsfa_slice *__restrict__ slices, int32_t *__restrict__ e_first,
+                             int32_t *__restrict__ e_n, uint8_t *__restrict__ e_full,
+                             int32_t *__restrict__ e_pieces, unsigned long long *__restrict__ totals)
+{
+    const int64_t t = (int64_t)blockIdx.x * kThreadsDev + threadIdx.x;
+    unsigned long long n_full = 0, n_part = 0, n_pairs = 0;
+    if (t < n && flag[t]) entry_one(keys, seg, t, n, g, slices, e_first, e_n, e_full, e_pieces, n_full, n_part, n_pairs);
+    // one atomic per workgroup and total (8 million heads on one address serialise)
+    block_sum(n_full);
+    block_sum(n_part);
+    block_sum(n_pairs);
+    if (threadIdx.x == 0) {
+        if (n_full) atomicAdd(&totals[1], n_full);
+        if (n_part) atomicAdd(&totals[2], n_part);
+        if (n_pairs) atomicAdd(&totals[4], n_pairs);
+    }
 }
 
 // Output of entry e (one thread each): col, tag, piece_ptr, pieces, row_ptr.
