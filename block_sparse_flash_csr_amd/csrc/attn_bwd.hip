@@ -240,8 +240,9 @@ __global__ void __launch_bounds__(kThreads) bwd_delta_kernel(const BwdArgs a)
 // one wave per SIMD, 2 where two waves share the SIMD (and the register file).
 constexpr int kAheadKv = 3, kAheadQ = 2;
 
-// S = X Y^T and dP = Z W^T over one 64-row LDS tile pair (x_t, z_t) against the register
-// fragments yf, wf (one 32-row block per wave): product i -> S (i even) or dP (i odd),
+// S += X Y^T and dP += Z W^T over one 64-row LDS tile pair (x_t, z_t) against the register
+// fragments yf, wf (one 32-row block per wave), onto the caller's initial accumulators:
+// product i -> S (i even) or dP (i odd),
 // row block (i >> 1) & 1, k-step i >> 2, so four independent accumulator chains rotate.
 // The tile reads run kAhead products ahead; `tail` runs once the last read is issued.
 template <int D, int AH, typename Tail>
@@ -251,11 +252,6 @@ __device__ __forceinline__ void score_products(const char *x_t, const char *z_t,
 {
     constexpr int N1 = 4 * BCfg<D>::KS;
     auto rd1 = [&](int i) { return rd_row<D>((i & 1) ? z_t : x_t, ad, (i >> 1) & 1, i >> 2); };
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        s[b] = f32x16{};
-        dp[b] = f32x16{};
-    }
     bf16x8 op[AH + 1];
 #pragma unroll
     for (int i = 0; i < AH; ++i) op[i] = rd1(i);
@@ -289,7 +285,8 @@ struct DqTiles {
 };
 
 // One dQ step: issue the next step's K/V loads into (kd, vd) when `issue`, then
-// S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D_i), dQ^T += K^T dS^T on (kt, vt).
+// S^T = K Q^T, dP^T = V dO^T, dS^T = 2^(c S^T - LSE_i log2 e) (dP^T - D_i),
+// dQ^T += K^T dS^T on (kt, vt).
 // The restrict qualifiers tell the compiler that the loads in flight do not write the
 // tiles this step reads.
 template <int D>
@@ -297,7 +294,8 @@ __device__ __forceinline__ void dq_step(char *__restrict__ kd, char *__restrict_
                                         const char *__restrict__ vt, bool issue, __amdgpu_buffer_rsrc_t rk,
                                         __amdgpu_buffer_rsrc_t rv, int32_t k_st, int32_t v_st, int wave, int lane,
                                         const Addr<D> &ad, const bf16x8 (&qf)[BCfg<D>::KS], const bf16x8 (&gf)[BCfg<D>::KS], uint64_t m,
-                                        bool masked_step, float c, float nl, float dlt, f32x16 (&acc)[BCfg<D>::DB])
+                                        bool masked_step, float c, float nl, float dlt,
+                                        f32x16 (&acc)[BCfg<D>::DB])
 {
     using C = BCfg<D>;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -305,17 +303,23 @@ __device__ __forceinline__ void dq_step(char *__restrict__ kd, char *__restrict_
         tile_dma<D>(rk, k_st, kd, wave, lane);
         tile_dma<D>(rv, v_st, vd, wave, lane);
     }
+    // (the dK/dV kernel starts its accumulators at -LSE / scale and -D; here, at two waves
+    // per SIMD, those 64 live values would not fit beside Q, dO and dQ, so S and dP start
+    // at 0 and the offsets are applied in the exponential)
     f32x16 s[2], dp[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        s[b] = f32x16{};
+        dp[b] = f32x16{};
+    }
     score_products<D, kAheadQ>(kt, vt, qf, gf, ad, s, dp);
     if (masked_step) mask_scores(m, s);
     f32x16 ds[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, nl));
-            ds[b][r] = p * (dp[b][r] - dlt);
-        }
+        for (int r = 0; r < 16; ++r)
+            ds[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, nl)) * (dp[b][r] - dlt);
     bf16x8 dsb[4];
     to_bf16_operands(ds, dsb);
     // dQ^T += K^T dS^T: product i -> head-dim block i % DB, k-step i / DB
@@ -351,8 +355,10 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
                  qf);
     load_frag<D>((const __bf16 *)a.dout + (int64_t)qrow0 * a.do_st + (int64_t)h * a.do_sh, a.do_st,
                  a.sq - qrow0, l32, hh, gf);
+    // exponent offset -LSE_i log2 e; a row with no key or past the end gets -inf, so its
+    // P is 0 whatever the tile holds
     const float lse = qvalid ? a.lse[(int64_t)h * a.lse_sh + qrow] : -INFINITY;
-    const float nl = lse == -INFINITY ? -INFINITY : -lse * kLog2e;   // exponent offset
+    const float nl = lse == -INFINITY ? -INFINITY : -lse * kLog2e;
     const float dlt = qvalid ? a.delta[(int64_t)h * a.lse_sh + qrow] : 0.f;
     f32x16 acc[C::DB];
 #pragma unroll
@@ -461,14 +467,14 @@ __device__ __forceinline__ void kv_issue(char *__restrict__ dst, const RowSrc &r
     if (wave == 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(r.d, (lds_ptr)(dst + L::D0), 4, lane * 4, 0, 0, 0);
 }
 
-// One dK/dV step on the 64 query rows in `cur`: S = Q K^T, dP = dO V^T,
-// P = 2^(c S - LSE log2 e), dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.  Query rows
-// past the end arrive as zero rows with LSE = D = 0, so they add nothing.
+// One dK/dV step on the 64 query rows in `cur`: S = Q K^T - LSE / scale, dP = dO V^T - D,
+// P = 2^(c S), dS = P dP, dV^T += dO^T P, dK^T += Q^T dS.  Query rows past the end arrive
+// as zero rows with LSE = D = 0, so they add nothing.
 template <int D>
 __device__ __forceinline__ void kv_step(char *__restrict__ nxt, const char *__restrict__ cur, bool issue,
                                         const RowSrc &src, int32_t q_st, int32_t do_st, int wave, int lane,
                                         const Addr<D> &ad, const bf16x8 (&kf)[BCfg<D>::KS], const bf16x8 (&vf)[BCfg<D>::KS], uint64_t m,
-                                        bool masked_step, float c, f32x16 (&dk)[BCfg<D>::DB],
+                                        bool masked_step, float c, float kneg, f32x16 (&dk)[BCfg<D>::DB],
                                         f32x16 (&dv)[BCfg<D>::DB])
 {
     using C = BCfg<D>;
@@ -477,18 +483,26 @@ __device__ __forceinline__ void kv_step(char *__restrict__ nxt, const char *__re
     if (issue) kv_issue<D>(nxt, src, q_st, do_st, wave, lane);
     const char *qt_ = cur + L::Q0, *gt = cur + L::G0;
     const float *lse_s = (const float *)(cur + L::L0), *dlt_s = (const float *)(cur + L::D0);
-    // rows of the lane's registers: 32 b + 8 g4 + 4 hh + t
-    f32x4 l4[2][4], d4[2][4];
+    // accumulators start at -LSE / scale and -D of their rows (32 b + 8 g4 + 4 hh + t): then
+    // 2^(c S) is P and dP is dP - D.  A row with no key has LSE = -inf and starts at +inf,
+    // but such a row only meets partial tiles, whose mask sets all its scores to -inf.
     f32x16 s[2], dp[2];
-    score_products<D, kAheadKv>(qt_, gt, kf, vf, ad, s, dp, [&]() {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                l4[b][g4] = *(const f32x4 *)(lse_s + 32 * b + 8 * g4 + 4 * hh);
-                d4[b][g4] = *(const f32x4 *)(dlt_s + 32 * b + 8 * g4 + 4 * hh);
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 l4 = *(const f32x4 *)(lse_s + 32 * b + 8 * g4 + 4 * hh);
+            const f32x4 d4 = *(const f32x4 *)(dlt_s + 32 * b + 8 * g4 + 4 * hh);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                s[b][4 * g4 + t] = l4[t] * kneg;
+                dp[b][4 * g4 + t] = -d4[t];
             }
-    });
+        }
+    // S and dP stay in VGPRs (the exponentials read them), the dK / dV accumulators in
+    // AGPRs: left to itself the allocator shares AGPRs between the two and moves 64
+    // accumulator values out and back every step
+    score_products<D, kAheadKv>(qt_, gt, kf, vf, ad, s, dp);
     // the first operands of the gradient products load during the exponentials
     constexpr int N2 = 8 * C::DB;   // product i: dV (i even) or dK (i odd), block (i / 2) % DB, k-step i / (2 DB)
     auto rd2 = [&](int i) { return rd_tr<D>((i & 1) ? qt_ : gt, ad, (i >> 1) % C::DB, (i >> 1) / C::DB); };
@@ -501,15 +515,10 @@ __device__ __forceinline__ void kv_step(char *__restrict__ nxt, const char *__re
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float lv = l4[b][g4][t];
-                const float nl = lv == -INFINITY ? -INFINITY : -lv * kLog2e;
-                const int r = 4 * g4 + t;
-                p[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, nl));
-                ds[b][r] = p[b][r] * (dp[b][r] - d4[b][g4][t]);
-            }
+        for (int r = 0; r < 16; ++r) {
+            p[b][r] = __builtin_amdgcn_exp2f(s[b][r] * c);
+            ds[b][r] = p[b][r] * dp[b][r];
+        }
     bf16x8 pb[4], dsb[4];
     to_bf16_operands(p, pb);
     to_bf16_operands(ds, dsb);
@@ -600,7 +609,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(const BwdArgs a)
         __builtin_amdgcn_s_waitcnt(0);   // this step's rows are in LDS (own loads) ...
         __syncthreads();                 // ... for every wave, and the other buffer is free
         kv_step<D>(smem + (buf ^ 1) * L::BUF, smem + buf * L::BUF, more, src, a.q_st, a.do_st, wave, lane, ad, kf, vf, m,
-                   masked_step, a.c, dk, dv);
+                   masked_step, a.c, -1.f / a.scale, dk, dv);
         h = nh;
         t = ntt;
         sub = ns;
