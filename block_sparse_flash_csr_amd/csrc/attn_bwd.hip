@@ -276,7 +276,8 @@ __device__ __forceinline__ void score_products(const char *x_t, const char *z_t,
 }
 
 // ---------------------------------------------------------------------------
-// kernel 2: dQ by query tile (grid n_qt x hq), 64-key steps over the CSR row; the K and
+// kernel 2: dQ by query tile (one workgroup per (head, query tile), in the plan's launch
+// order), 64-key steps over the CSR row; the K and
 // V tiles of step j + 1 load (LDS double buffer) while step j computes
 // ---------------------------------------------------------------------------
 template <int D>
@@ -342,7 +343,8 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
     using C = BCfg<D>;
     using L = DqTiles<D>;
     __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
-    const int qt = blockIdx.x, h = blockIdx.y, g = h / (a.hq / a.hkv);
+    const int item = cload(a.meta.dq_order, (int)blockIdx.x);
+    const int h = item / a.n_qt, qt = item - h * a.n_qt, g = h / (a.hq / a.hkv);
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qrow0 = qt * kKernelBq + wave * 32, qrow = qrow0 + l32;
@@ -442,7 +444,8 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// kernel 3: dK, dV by key tile (grid n_kt x hkv); a wave owns 32 keys; 64-query
+// kernel 3: dK, dV by key tile (one workgroup per (kv head, key tile), in the plan's
+// launch order); a wave owns 32 keys; 64-query
 // steps over the CSR column, for every query head of the key/value head; the Q, dO,
 // LSE and D of step j + 1 load (LDS double buffer) while step j computes
 // ---------------------------------------------------------------------------
@@ -539,7 +542,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(const BwdArgs a)
     using C = BCfg<D>;
     using L = KvTiles<D>;
     __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
-    const int kt = blockIdx.x, g = blockIdx.y, group = a.hq / a.hkv;
+    const int item = cload(a.meta.dkv_order, (int)blockIdx.x);
+    const int g = item / a.n_kt, kt = item - g * a.n_kt, group = a.hq / a.hkv;
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int key0 = kt * a.bk_plan + wave * 32, key = key0 + l32;
@@ -640,9 +644,9 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream)
     constexpr int RPB = kThreads / (D / 8);
     if (a.sq > 0) {
         hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((a.sq + RPB - 1) / RPB, a.hq), dim3(kThreads), 0, stream, a);
-        hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.n_qt, a.hq), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.n_qt * a.hq), dim3(kThreads), 0, stream, a);
     }
-    if (a.sk > 0) hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.n_kt, a.hkv), dim3(kThreads), 0, stream, a);
+    if (a.sk > 0) hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.n_kt * a.hkv), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

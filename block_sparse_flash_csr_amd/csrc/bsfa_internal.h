@@ -70,6 +70,8 @@ struct DeviceMeta {
                                           // O [128][d] then LSE [128], fp32
     const int32_t *t_ptr = nullptr;       // transposed CSR: per key tile [n_kt + 1]
     const int32_t *t_list = nullptr;      // (query tile, entry) pairs, ascending query tile
+    const int32_t *dq_order = nullptr;    // gradient launch orders: workgroup -> item
+    const int32_t *dkv_order = nullptr;   // (h * n_qt + qt, resp. g * n_kt + kt)
 };
 
 }  // namespace bsfa
@@ -87,6 +89,9 @@ struct bsfa_plan {
     // the same CSR by key-tile column: t_ptr [n_kt + 1], t_list [2 * nnz] = (qt, entry)
     std::vector<int32_t> t_ptr;
     std::vector<int32_t> t_list;
+    // launch orders of the gradient kernels (workgroup index -> item), longest first per XCD
+    std::vector<int32_t> dq_order;     // items h * n_qt + qt
+    std::vector<int32_t> dkv_order;    // items g * n_kt + kt
     // schedule
     std::vector<float> item_cost;      // by item id = h * n_qt + qt
     std::vector<bsfa::Unit> units;     // by unit id; unit id == item id when no row is split
@@ -125,7 +130,8 @@ namespace bsfa {
 
 // Mask compiler: validated slices -> tile CSR with pieces and the pair count.
 bsfa_status compile_mask(const bsfa_slice *slices, int32_t n_slices, bsfa_plan &p);
-// Column view of the tile CSR (for the key/value gradients).
+// Column view of the tile CSR (for the key/value gradients) and the launch orders of the
+// gradient kernels.
 void build_transpose(bsfa_plan &p);
 // Scheduler: items, costs and the per-bin lists.
 void build_schedule(bsfa_plan &p, int n_bins_max);

@@ -323,6 +323,8 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     const size_t o_sp = place<Split>(off, p->splits.size());
     const size_t o_tp = place<int32_t>(off, p->t_ptr.size());
     const size_t o_tl = place<int32_t>(off, p->t_list.size());
+    const size_t o_oq = place<int32_t>(off, p->dq_order.size());
+    const size_t o_ok = place<int32_t>(off, p->dkv_order.size());
     const size_t bytes = (off + 255) & ~size_t(255);
     const size_t ws_bytes = workspace_bytes(*p);
 
@@ -344,6 +346,10 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     if (!p->splits.empty()) std::memcpy(h + o_sp, p->splits.data(), p->splits.size() * sizeof(Split));
     std::memcpy(h + o_tp, p->t_ptr.data(), p->t_ptr.size() * sizeof(int32_t));
     if (!p->t_list.empty()) std::memcpy(h + o_tl, p->t_list.data(), p->t_list.size() * sizeof(int32_t));
+    if (!p->dq_order.empty())
+        std::memcpy(h + o_oq, p->dq_order.data(), p->dq_order.size() * sizeof(int32_t));
+    if (!p->dkv_order.empty())
+        std::memcpy(h + o_ok, p->dkv_order.data(), p->dkv_order.size() * sizeof(int32_t));
 
     DevSlot *slot = nullptr;
     st = dev_acquire(dev, bytes + ws_bytes, &slot);
@@ -380,6 +386,8 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     p->dev.ws = ws_bytes ? (float *)(base + bytes) : nullptr;
     p->dev.t_ptr = (const int32_t *)(base + o_tp);
     p->dev.t_list = (const int32_t *)(base + o_tl);
+    p->dev.dq_order = (const int32_t *)(base + o_oq);
+    p->dev.dkv_order = (const int32_t *)(base + o_ok);
     p->dbuf = d;
     p->slot = slot;
     p->device = dev;
@@ -588,6 +596,7 @@ bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     if (dev != p->device) return BSFA_ERR_STATE;
     if (lse_stride_head < p->sq || lse_stride_head > INT32_MAX) return BSFA_ERR_ARG;
     if ((p->sq > 0 && !dq) || (p->sk > 0 && (!dk || !dv))) return BSFA_ERR_ARG;
+    if ((int64_t)p->n_kt * p->hkv >= INT32_MAX) return BSFA_ERR_UNSUPPORTED;   // one workgroup each
     const int32_t n_tok[5] = {p->sq, p->sk, p->sk, p->sq, p->sq};
     const int32_t n_head[5] = {p->hq, p->hkv, p->hkv, p->hq, p->hq};
     const bsfa_tensor *ts[5] = {q, k, v, o, dout};

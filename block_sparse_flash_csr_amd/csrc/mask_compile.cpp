@@ -213,6 +213,37 @@ void build_transpose(bsfa_plan &p)
             p.t_list[2 * (size_t)at] = qt;
             p.t_list[2 * (size_t)at + 1] = e;
         }
+
+    // Launch orders of the gradient kernels.  A workgroup's work is about its number of
+    // CSR entries (times the query heads of a key/value head for dK/dV), so items run
+    // longest first ([MA] Dispatch Solver: greedy, heaviest first).  The hardware hands
+    // workgroup i to XCD i mod 8; when the heads split evenly over the 8 XCDs, XCD x gets
+    // a contiguous block of heads (their rows share its L2) and item j of its own
+    // longest-first list runs as workgroup 8 j + x.
+    auto order = [&](int32_t n_heads, int32_t n_t, auto cost_of, std::vector<int32_t> &out) {
+        const int64_t n = (int64_t)n_heads * n_t;
+        out.resize((size_t)n);
+        auto by_cost = [&](int32_t a, int32_t b) {
+            const int64_t ca = cost_of(a % n_t), cb = cost_of(b % n_t);
+            return ca != cb ? ca > cb : a < b;
+        };
+        if (n_heads % kNumXcd == 0) {
+            const int32_t per = n_heads / kNumXcd;
+            std::vector<int32_t> list((size_t)per * n_t);
+            for (int32_t x = 0; x < kNumXcd; ++x) {
+                for (int32_t k = 0; k < per * n_t; ++k) list[(size_t)k] = (x * per) * n_t + k;
+                std::stable_sort(list.begin(), list.end(), by_cost);
+                for (int32_t j = 0; j < per * n_t; ++j) out[(size_t)j * kNumXcd + x] = list[(size_t)j];
+            }
+        } else {
+            for (int64_t k = 0; k < n; ++k) out[(size_t)k] = (int32_t)k;
+            std::stable_sort(out.begin(), out.end(), by_cost);
+        }
+    };
+    order(p.hq, p.n_qt, [&](int32_t qt) { return (int64_t)p.row_ptr[(size_t)qt + 1] - p.row_ptr[qt]; },
+          p.dq_order);
+    order(p.hkv, p.n_kt, [&](int32_t kt) { return (int64_t)p.t_ptr[(size_t)kt + 1] - p.t_ptr[kt]; },
+          p.dkv_order);
 }
 
 }  // namespace bsfa
