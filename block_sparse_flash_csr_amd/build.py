@@ -17,11 +17,8 @@ SOURCES = ["capi.cpp", "mask_compile.cpp", "schedule.cpp", "attn_fwd.hip", "attn
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
-# Per-source extras.  The gradient kernels run one wave per SIMD (512 registers), where
-# the backend otherwise issues every matrix product in its AGPR form; the score products
-# then have to be copied to VGPRs for the exponentials every step.  The VGPR form keeps
-# them where the vector ALU reads them (measured: 9 % less backward time).
-EXTRA = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra flags (none at present).
+EXTRA: dict = {}
 
 
 def build(verbose: bool = False) -> str:

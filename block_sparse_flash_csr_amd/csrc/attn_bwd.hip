@@ -18,14 +18,18 @@
 //     dP^T = V dO^T with Q and dO held as B operands, so a lane owns one query column
 //     and its LSE_i, D_i are scalars; dQ^T += K^T dS^T takes K^T from the LDS tile with
 //     ds_read_b64_tr_b16 and dS^T straight from the accumulator registers.
-//   * Kernel 3 takes S = Q K^T and dP = dO V^T with K and V held as B operands (a lane
-//     owns one key), dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
-//     transposed from LDS; the per-query LSE and D come from LDS as broadcasts.
+//   * Kernel 3 takes S = Q K^T and dP = dO V^T with the key tile's K and V rows as B
+//     operands read from LDS, where they stay for the whole workgroup (a lane owns one
+//     key), dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed from
+//     LDS; the accumulators of S and dP start at -LSE / scale and -D, read from LDS as
+//     broadcasts.  Eight waves, two per SIMD: a wave holds only its dK, dV partials.
 //   * Tiles go HBM -> LDS with direct buffer loads; 16-byte chunks of a row are
 //     XOR-swizzled by the row's low bits so that row reads are conflict-free.
-//   * A row without any admitted key (and a row past the end) has LSE = -inf: its
-//     weights are taken against -inf and come out exactly 0.
+//   * A row without any admitted key has LSE = -inf and only meets partial tiles, whose
+//     mask gives its scores -inf: its weights come out exactly 0.  Rows past the end are
+//     zero rows (with LSE = D = 0 in kernel 3, -inf in kernel 2) and contribute 0.
 #include <climits>
+#include <type_traits>
 
 #include "bsfa_internal.h"
 
@@ -97,16 +101,18 @@ __device__ __forceinline__ uint32_t extent(int n, int32_t st)
 
 __device__ __forceinline__ int32_t cload(const int32_t *p, int i) { return ((cptr_i32)p)[i]; }
 
-// 64 rows of a [tokens, heads, D] bf16 tensor (row stride st elements) from the
-// buffer range r into an LDS tile; the waves share the 1 KB blocks, rows outside the
-// range land as zeros.
-template <int D>
+// ROWS rows of a [tokens, heads, D] bf16 tensor (row stride st elements) from the
+// buffer range r into an LDS tile; the NW waves share the 1 KB blocks, rows outside
+// the range land as zeros.
+template <int D, int ROWS = kStep, int NW = 4>
 __device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t r, int32_t st, char *tile, int wave, int lane)
 {
     using C = BCfg<D>;
+    constexpr int NB = ROWS * C::ROWB / 1024;
+    static_assert(NB % NW == 0, "the waves share the blocks evenly");
 #pragma unroll
-    for (int i = 0; i < C::NBLK / 4; ++i) {
-        const int b = wave + 4 * i;
+    for (int i = 0; i < NB / NW; ++i) {
+        const int b = wave + NW * i;
         const int p = 64 * b + lane, row = p / C::NCH, phys = p % C::NCH;
         const uint32_t goff = (uint32_t)(row * st * 2 + ((phys ^ swz<D>(row)) << 4));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(tile + b * 1024), 16, (int)goff, 0, 0, 0);
@@ -236,8 +242,19 @@ __global__ void __launch_bounds__(kThreads) bwd_delta_kernel(const BwdArgs a)
     if (i < a.sq && (threadIdx.x % TPR) == 0) a.delta[(int64_t)h * a.lse_sh + i] = s;
 }
 
-// Operands are read this many products ahead of their MFMA: 3 where the kernel runs
-// one wave per SIMD, 2 where two waves share the SIMD (and the register file).
+// f(integral_constant<int, I>) for I = B .. E - 1, each with I a compile-time constant
+// (long unrolled sequences of products exceed the unroller's limits; this never leaves
+// one rolled with its accumulator arrays indexed at run time).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Operands are read this many products ahead of their MFMA (kernel 3, kernel 2).
 constexpr int kAheadKv = 3, kAheadQ = 2;
 
 // S += X Y^T and dP += Z W^T over one 64-row LDS tile pair (x_t, z_t) against the register
@@ -443,126 +460,153 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
     }
 }
 
-// ---------------------------------------------------------------------------
-// kernel 3: dK, dV by key tile (one workgroup per (kv head, key tile), in the plan's
-// launch order); a wave owns 32 keys; 64-query
-// steps over the CSR column, for every query head of the key/value head; the Q, dO,
-// LSE and D of step j + 1 load (LDS double buffer) while step j computes
-// ---------------------------------------------------------------------------
-template <int D>
-struct KvTiles {
-    static constexpr int Q0 = 0, G0 = BCfg<D>::TILE_B, L0 = 2 * BCfg<D>::TILE_B, D0 = L0 + 4 * kStep;
-    static constexpr int BUF = 2 * BCfg<D>::TILE_B + 1024, BYTES = 2 * BUF;
-};
-
 struct RowSrc {
     __amdgpu_buffer_rsrc_t q, g, l, d;
 };
 
+// ---------------------------------------------------------------------------
+// kernel 3: dK, dV by key tile (one workgroup per (kv head, key tile), in the plan's
+// launch order), 64-query steps over the CSR column for every query head of the key /
+// value head; the Q, dO, LSE and D of step j + 1 load (LDS double buffer) while step j
+// computes.  Two waves per SIMD: 8 waves per key tile; wave w owns keys 32 (w mod 4) ..
+// + 31 and query half w div 4 of every 64-query step.  K and V stay in LDS for the whole
+// workgroup and are read as MFMA operands (so a wave holds only its dK, dV partials and
+// the step's scores); the two waves of a key block add their partials at the end.
+// ---------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ void kv_issue(char *__restrict__ dst, const RowSrc &r, int32_t q_st, int32_t do_st,
-                                         int wave, int lane)
+struct Kv2Tiles {
+    static constexpr int K0 = 0, V0 = 2 * kStep * BCfg<D>::ROWB, T0 = 4 * kStep * BCfg<D>::ROWB;
+    static constexpr int Q0 = 0, G0 = BCfg<D>::TILE_B, L0 = 2 * BCfg<D>::TILE_B, D0 = L0 + 4 * kStep;
+    static constexpr int BUF = 2 * BCfg<D>::TILE_B + 1024, BYTES = T0 + 2 * BUF;
+};
+
+template <int D>
+__device__ __forceinline__ void kv2_issue(char *__restrict__ dst, const RowSrc &r, int32_t q_st, int32_t do_st,
+                                          int wave, int lane)
 {
-    using L = KvTiles<D>;
-    tile_dma<D>(r.q, q_st, dst + L::Q0, wave, lane);
-    tile_dma<D>(r.g, do_st, dst + L::G0, wave, lane);
-    if (wave == 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(r.l, (lds_ptr)(dst + L::L0), 4, lane * 4, 0, 0, 0);
-    if (wave == 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(r.d, (lds_ptr)(dst + L::D0), 4, lane * 4, 0, 0, 0);
+    using L = Kv2Tiles<D>;
+    tile_dma<D, kStep, 8>(r.q, q_st, dst + L::Q0, wave, lane);
+    tile_dma<D, kStep, 8>(r.g, do_st, dst + L::G0, wave, lane);
+    if (wave == 6) __builtin_amdgcn_raw_ptr_buffer_load_lds(r.l, (lds_ptr)(dst + L::L0), 4, lane * 4, 0, 0, 0);
+    if (wave == 7) __builtin_amdgcn_raw_ptr_buffer_load_lds(r.d, (lds_ptr)(dst + L::D0), 4, lane * 4, 0, 0, 0);
 }
 
-// One dK/dV step on the 64 query rows in `cur`: S = Q K^T - LSE / scale, dP = dO V^T - D,
-// P = 2^(c S), dS = P dP, dV^T += dO^T P, dK^T += Q^T dS.  Query rows past the end arrive
-// as zero rows with LSE = D = 0, so they add nothing.
+// One step of one wave on its 32 queries (half qh of the 64 in `cur`) against its 32 keys
+// (block kb of the resident K, V): S = Q K^T - LSE / scale, dP = dO V^T - D, P = 2^(c S),
+// dS = P dP, dV^T += dO^T P, dK^T += Q^T dS.
 template <int D>
-__device__ __forceinline__ void kv_step(char *__restrict__ nxt, const char *__restrict__ cur, bool issue,
-                                        const RowSrc &src, int32_t q_st, int32_t do_st, int wave, int lane,
-                                        const Addr<D> &ad, const bf16x8 (&kf)[BCfg<D>::KS], const bf16x8 (&vf)[BCfg<D>::KS], uint64_t m,
-                                        bool masked_step, float c, float kneg, f32x16 (&dk)[BCfg<D>::DB],
-                                        f32x16 (&dv)[BCfg<D>::DB])
+__device__ __forceinline__ void kv2_step(char *__restrict__ nxt, const char *__restrict__ cur,
+                                         const char *__restrict__ kv, bool issue, const RowSrc &src, int32_t q_st,
+                                         int32_t do_st, int wave, int lane, int kb, int qh, const Addr<D> &ad,
+                                         uint32_t mw, bool masked_step, float c, float kneg,
+                                         f32x16 (&dk)[BCfg<D>::DB], f32x16 (&dv)[BCfg<D>::DB])
 {
     using C = BCfg<D>;
-    using L = KvTiles<D>;
-    const int l32 = lane & 31, hh = lane >> 5;
-    if (issue) kv_issue<D>(nxt, src, q_st, do_st, wave, lane);
-    const char *qt_ = cur + L::Q0, *gt = cur + L::G0;
+    using L = Kv2Tiles<D>;
+    const int hh = lane >> 5;
+    if (issue) kv2_issue<D>(nxt, src, q_st, do_st, wave, lane);
+    const char *qt_ = cur + L::Q0, *gt = cur + L::G0, *kt = kv + L::K0, *vt = kv + L::V0;
     const float *lse_s = (const float *)(cur + L::L0), *dlt_s = (const float *)(cur + L::D0);
-    // accumulators start at -LSE / scale and -D of their rows (32 b + 8 g4 + 4 hh + t): then
-    // 2^(c S) is P and dP is dP - D.  A row with no key has LSE = -inf and starts at +inf,
-    // but such a row only meets partial tiles, whose mask sets all its scores to -inf.
-    f32x16 s[2], dp[2];
+    // accumulators start at -LSE / scale and -D of rows 32 qh + 8 g4 + 4 hh + t
+    f32x16 s, dp;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 l4 = *(const f32x4 *)(lse_s + 32 * qh + 8 * g4 + 4 * hh);
+        const f32x4 d4 = *(const f32x4 *)(dlt_s + 32 * qh + 8 * g4 + 4 * hh);
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 l4 = *(const f32x4 *)(lse_s + 32 * b + 8 * g4 + 4 * hh);
-            const f32x4 d4 = *(const f32x4 *)(dlt_s + 32 * b + 8 * g4 + 4 * hh);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                s[b][4 * g4 + t] = l4[t] * kneg;
-                dp[b][4 * g4 + t] = -d4[t];
-            }
+        for (int t = 0; t < 4; ++t) {
+            s[4 * g4 + t] = l4[t] * kneg;
+            dp[4 * g4 + t] = -d4[t];
         }
-    // S and dP stay in VGPRs (the exponentials read them), the dK / dV accumulators in
-    // AGPRs: left to itself the allocator shares AGPRs between the two and moves 64
-    // accumulator values out and back every step
-    score_products<D, kAheadKv>(qt_, gt, kf, vf, ad, s, dp);
-    // the first operands of the gradient products load during the exponentials
-    constexpr int N2 = 8 * C::DB;   // product i: dV (i even) or dK (i odd), block (i / 2) % DB, k-step i / (2 DB)
-    auto rd2 = [&](int i) { return rd_tr<D>((i & 1) ? qt_ : gt, ad, (i >> 1) % C::DB, (i >> 1) / C::DB); };
-    bf16x8 op[kAheadKv + 1];
-#pragma unroll
-    for (int i = 0; i < kAheadKv; ++i) op[i] = rd2(i);
+    }
+    // score products: i -> S (even) / dP (odd), k-step i >> 1; A = query rows, B = key rows
+    constexpr int N1 = 2 * C::KS;
+    bf16x8 oa[kAheadKv + 1], ob[kAheadKv + 1];
+    auto rd1 = [&](int i, bf16x8 &a_, bf16x8 &b_) {
+        a_ = rd_row<D>((i & 1) ? gt : qt_, ad, qh, i >> 1);
+        b_ = rd_row<D>((i & 1) ? vt : kt, ad, kb, i >> 1);
+    };
+    static_for<0, kAheadKv>([&](auto ic) { rd1(ic.value, oa[ic.value], ob[ic.value]); });
     __builtin_amdgcn_sched_barrier(0);
-    if (masked_step) mask_scores(m, s);
-    f32x16 p[2], ds[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
+    static_for<0, N1>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + kAheadKv < N1)
+            rd1(i + kAheadKv, oa[(i + kAheadKv) % (kAheadKv + 1)], ob[(i + kAheadKv) % (kAheadKv + 1)]);
+        constexpr int r = i % (kAheadKv + 1);
+        if constexpr (i & 1) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[r], ob[r], dp, 0, 0, 0);
+        else s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[r], ob[r], s, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    // gradient products: i -> dV (even) / dK (odd), block (i >> 1) % DB, k-step 2 qh + (i >> 1) / DB
+    constexpr int N2 = 4 * C::DB;
+    auto rd2 = [&](int i) { return rd_tr<D>((i & 1) ? qt_ : gt, ad, (i >> 1) % C::DB, 2 * qh + (i >> 1) / C::DB); };
+    static_for<0, kAheadKv>([&](auto ic) { oa[ic.value] = rd2(ic.value); });
+    __builtin_amdgcn_sched_barrier(0);
+    if (masked_step) {
+        const int32_t w = (int32_t)mw;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            p[b][r] = __builtin_amdgcn_exp2f(s[b][r] * c);
-            ds[b][r] = p[b][r] * dp[b][r];
+            const int off = 8 * (r >> 2) + (r & 3);
+            const int32_t keep = (w << (31 - off)) >> 31;
+            s[r] = __int_as_float((keep & __float_as_int(s[r])) | (~keep & __float_as_int(-INFINITY)));
         }
-    bf16x8 pb[4], dsb[4];
-    to_bf16_operands(p, pb);
-    to_bf16_operands(ds, dsb);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < N2; ++i) {
-        if (i + kAheadKv < N2) op[(i + kAheadKv) % (kAheadKv + 1)] = rd2(i + kAheadKv);
-        const int db = (i >> 1) % C::DB, ks = (i >> 1) / C::DB;
-        if (i & 1) dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (kAheadKv + 1)], dsb[ks], dk[db], 0, 0, 0);
-        else dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (kAheadKv + 1)], pb[ks], dv[db], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
     }
+    f32x8 tp[2], td[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(s[r] * c);
+        tp[r >> 3][r & 7] = p;
+        td[r >> 3][r & 7] = p * dp[r];
+    }
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        pb[k] = __builtin_convertvector(tp[k], bf16x8);
+        dsb[k] = __builtin_convertvector(td[k], bf16x8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, N2>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + kAheadKv < N2) oa[(i + kAheadKv) % (kAheadKv + 1)] = rd2(i + kAheadKv);
+        constexpr int db = (i >> 1) % C::DB, kk = (i >> 1) / C::DB, r = i % (kAheadKv + 1);
+        if constexpr (i & 1) dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[r], dsb[kk], dk[db], 0, 0, 0);
+        else dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[r], pb[kk], dv[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    });
 }
 
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(const BwdArgs a)
+__global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv2_kernel(const BwdArgs a)
 {
     using C = BCfg<D>;
-    using L = KvTiles<D>;
+    using L = Kv2Tiles<D>;
     __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
     const int item = cload(a.meta.dkv_order, (int)blockIdx.x);
     const int g = item / a.n_kt, kt = item - g * a.n_kt, group = a.hq / a.hkv;
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int key0 = kt * a.bk_plan + wave * 32, key = key0 + l32;
+    const int kb = wave & 3, qh = wave >> 2;
+    const int key = kt * a.bk_plan + 32 * kb + l32;
     const int nsub = kKernelBq / kStep;
     const Addr<D> ad = make_addr<D>(lane);
 
-    bf16x8 kf[C::KS], vf[C::KS];
-    load_frag<D>((const __bf16 *)a.k + (int64_t)key0 * a.k_st + (int64_t)g * a.k_sh, a.k_st, a.sk - key0, l32, hh, kf);
-    load_frag<D>((const __bf16 *)a.v + (int64_t)key0 * a.v_st + (int64_t)g * a.v_sh, a.v_st, a.sk - key0, l32, hh, vf);
+    // resident K and V rows of the key tile (rows past the end load as zeros)
+    {
+        const int k0 = kt * a.bk_plan, nk = min(2 * kStep, a.sk - k0);
+        const __bf16 *kb_ = (const __bf16 *)a.k + (int64_t)k0 * a.k_st + (int64_t)g * a.k_sh;
+        const __bf16 *vb_ = (const __bf16 *)a.v + (int64_t)k0 * a.v_st + (int64_t)g * a.v_sh;
+        tile_dma<D, 2 * kStep, 8>(make_rsrc(kb_, extent<D>(nk, a.k_st)), a.k_st, smem + L::K0, wave, lane);
+        tile_dma<D, 2 * kStep, 8>(make_rsrc(vb_, extent<D>(nk, a.v_st)), a.v_st, smem + L::V0, wave, lane);
+    }
     f32x16 dk[C::DB], dv[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
         dk[db] = f32x16{};
         dv[db] = f32x16{};
     }
-
+    char *const tiles = smem + L::T0;
     const int t0 = cload(a.meta.t_ptr, kt), t1 = cload(a.meta.t_ptr, kt + 1);
     const int h_end = (g + 1) * group;
-    // steps (head h, column entry t, 64-query part sub); a part past the last query is skipped
     auto q_start = [&](int t, int sub) { return cload(a.meta.t_list, 2 * t) * kKernelBq + sub * kStep; };
     auto advance = [&](int &h, int &t, int &sub) {
         ++sub;
@@ -585,7 +629,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(const BwdArgs a)
         return r;
     };
     int h = g * group, t = t0, sub = 0, buf = 0;
-    if (t0 < t1) kv_issue<D>(smem, sources(h, q_start(t, 0)), a.q_st, a.do_st, wave, lane);
+    if (t0 < t1) kv2_issue<D>(tiles, sources(h, q_start(t, 0)), a.q_st, a.do_st, wave, lane);
     else h = h_end;
     while (h < h_end) {
         const int e = cload(a.meta.t_list, 2 * t + 1);
@@ -596,41 +640,56 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(const BwdArgs a)
         const bool more = nh < h_end;
         RowSrc src = sources(h, q0);   // placeholder when there is no next step
         if (more) src = sources(nh, q_start(ntt, ns));
-        // mask of partial tiles: this lane's key over the 64 query rows
+        // mask of partial tiles: this lane's key over the wave's 32 query rows
         const bool masked_step = en[3] == BSFA_TILE_PARTIAL;
-        uint64_t m = ~0ull;
+        uint32_t mw = ~0u;
         if (masked_step) {
             const int base = q0 + 4 * hh;
-            m = 0;
+            uint64_t m = 0;
             for (int pi = 0; pi < en[2]; ++pi) {
                 const i32x4 pc = ((cptr_i32x4)a.meta.pieces)[2 * (en[1] + pi)];
                 const int diag = ((cptr_i32)a.meta.pieces)[8 * (en[1] + pi) + 4];
                 if (key < pc[2] || key >= pc[3]) continue;
-                // rows i of the piece with key <= i + diag
                 m |= range_bits(max(pc[0], key - diag) - base, pc[1] - base);
             }
+            mw = qh ? (uint32_t)(m >> 32) : (uint32_t)m;
         }
-        __builtin_amdgcn_s_waitcnt(0);   // this step's rows are in LDS (own loads) ...
+        __builtin_amdgcn_s_waitcnt(0);   // this step's rows (and the resident K, V) are in ...
         __syncthreads();                 // ... for every wave, and the other buffer is free
-        kv_step<D>(smem + (buf ^ 1) * L::BUF, smem + buf * L::BUF, more, src, a.q_st, a.do_st, wave, lane, ad, kf, vf, m,
-                   masked_step, a.c, -1.f / a.scale, dk, dv);
+        kv2_step<D>(tiles + (buf ^ 1) * L::BUF, tiles + buf * L::BUF, smem, more, src, a.q_st, a.do_st, wave, lane,
+                    kb, qh, ad, mw, masked_step, a.c, -1.f / a.scale, dk, dv);
         h = nh;
         t = ntt;
         sub = ns;
         buf ^= 1;
     }
-    // lane (key l32, half hh) holds dims 32 db + 8 g4 + 4 hh + 0..3 of its key
-    if (key < a.sk) {
+    // the two waves of a key block add their partials: waves 4..7 pass theirs through LDS
+    // (over the tiles; every load into them, the resident K and V included, has landed)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x4 *xch = (f32x4 *)smem + (size_t)kb * (2 * C::DB * 4) * 64 + lane;
+    if (qh == 1) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                xch[(2 * (4 * db + g4)) * 64] = f32x4{dk[db][4 * g4], dk[db][4 * g4 + 1], dk[db][4 * g4 + 2], dk[db][4 * g4 + 3]};
+                xch[(2 * (4 * db + g4) + 1) * 64] = f32x4{dv[db][4 * g4], dv[db][4 * g4 + 1], dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]};
+            }
+    }
+    __syncthreads();
+    if (qh == 0 && key < a.sk) {
         float *ok = a.dk + ((int64_t)key * a.hkv + g) * D, *ov = a.dv + ((int64_t)key * a.hkv + g) * D;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 pk = xch[(2 * (4 * db + g4)) * 64], pv = xch[(2 * (4 * db + g4) + 1) * 64];
                 f32x4 wk, wv;
 #pragma unroll
                 for (int t4 = 0; t4 < 4; ++t4) {
-                    wk[t4] = a.scale * dk[db][4 * g4 + t4];
-                    wv[t4] = dv[db][4 * g4 + t4];
+                    wk[t4] = a.scale * (dk[db][4 * g4 + t4] + pk[t4]);
+                    wv[t4] = dv[db][4 * g4 + t4] + pv[t4];
                 }
                 *(f32x4 *)(ok + 32 * db + 8 * g4 + 4 * hh) = wk;
                 *(f32x4 *)(ov + 32 * db + 8 * g4 + 4 * hh) = wv;
@@ -646,7 +705,7 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream)
         hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((a.sq + RPB - 1) / RPB, a.hq), dim3(kThreads), 0, stream, a);
         hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.n_qt * a.hq), dim3(kThreads), 0, stream, a);
     }
-    if (a.sk > 0) hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.n_kt * a.hkv), dim3(kThreads), 0, stream, a);
+    if (a.sk > 0) hipLaunchKernelGGL(bwd_dkdv2_kernel<D>, dim3(a.n_kt * a.hkv), dim3(2 * kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
