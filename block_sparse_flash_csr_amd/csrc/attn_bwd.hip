@@ -5,7 +5,7 @@
 // forward and backward; FlashAttention-T blog, lineage paragraph: the tiled pass
 // recomputes the softmax from the saved log-sum-exp instead of storing it):
 //   P_ij  = 2^(c s_ij - LSE_i log2 e) on admitted pairs, s_ij = q_i . k_j, c = scale log2 e
-//   D_i   = sum_e dO_ie O_ie                       (kernel 1)
+//   D_i   = sum_e dO_ie O_ie                       (kernel 2, which also stores it)
 //   dS_ij = P_ij (dO_i . v_j - D_i)
 //   dQ_i  = scale sum_j dS_ij k_j                  (kernel 2: by query tile, CSR row)
 //   dK_j  = scale sum_(h,i) dS_ij q_i,  dV_j = sum_(h,i) P_ij dO_i
@@ -219,29 +219,6 @@ __device__ __forceinline__ void to_bf16_operands(const f32x16 (&x)[2], bf16x8 (&
     }
 }
 
-// ---------------------------------------------------------------------------
-// kernel 1: D = rowsum(dO * O), one lane group of D/8 per (token, head) row
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(kThreads) bwd_delta_kernel(const BwdArgs a)
-{
-    constexpr int TPR = D / 8, RPB = kThreads / TPR;
-    const int h = blockIdx.y;
-    const int i = (int)blockIdx.x * RPB + (int)threadIdx.x / TPR;
-    const int c = ((int)threadIdx.x % TPR) * 8;
-    float s = 0.f;
-    if (i < a.sq) {
-        const bf16x8 o = *(const bf16x8 *)((const __bf16 *)a.o + (int64_t)i * a.o_st + (int64_t)h * a.o_sh + c);
-        const bf16x8 g = *(const bf16x8 *)((const __bf16 *)a.dout + (int64_t)i * a.do_st + (int64_t)h * a.do_sh + c);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s += (float)o[e] * (float)g[e];
-    }
-    // reduce over the TPR lanes of the row (they are adjacent and TPR divides 64)
-#pragma unroll
-    for (int w = TPR / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, 64);
-    if (i < a.sq && (threadIdx.x % TPR) == 0) a.delta[(int64_t)h * a.lse_sh + i] = s;
-}
-
 // f(integral_constant<int, I>) for I = B .. E - 1, each with I a compile-time constant
 // (long unrolled sequences of products exceed the unroller's limits; this never leaves
 // one rolled with its accumulator arrays indexed at run time).
@@ -378,7 +355,23 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
     // P is 0 whatever the tile holds
     const float lse = qvalid ? a.lse[(int64_t)h * a.lse_sh + qrow] : -INFINITY;
     const float nl = lse == -INFINITY ? -INFINITY : -lse * kLog2e;
-    const float dlt = qvalid ? a.delta[(int64_t)h * a.lse_sh + qrow] : 0.f;
+    // D_i = sum_e dO_ie O_ie: this lane holds half of row i's dims of dO (gf) and loads
+    // the same half of O; lanes l and l ^ 32 hold the two halves.  The dK/dV kernel,
+    // launched after this one, reads D from `delta`.
+    float dlt = 0.f;
+    {
+        bf16x8 of[C::KS];
+        load_frag<D>((const __bf16 *)a.o + (int64_t)qrow0 * a.o_st + (int64_t)h * a.o_sh, a.o_st, a.sq - qrow0, l32,
+                     hh, of);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dlt = __builtin_fmaf((float)gf[ks][e], (float)of[ks][e], dlt);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(dlt), __float_as_int(dlt), false, false);
+        dlt = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+        if (qvalid && hh == 0) a.delta[(int64_t)h * a.lse_sh + qrow] = dlt;
+        if (!qvalid) dlt = 0.f;
+    }
     f32x16 acc[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
@@ -700,11 +693,7 @@ __global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv2_kernel(const BwdArg
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream)
 {
-    constexpr int RPB = kThreads / (D / 8);
-    if (a.sq > 0) {
-        hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((a.sq + RPB - 1) / RPB, a.hq), dim3(kThreads), 0, stream, a);
-        hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.n_qt * a.hq), dim3(kThreads), 0, stream, a);
-    }
+    if (a.sq > 0) hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.n_qt * a.hq), dim3(kThreads), 0, stream, a);
     if (a.sk > 0) hipLaunchKernelGGL(bwd_dkdv2_kernel<D>, dim3(a.n_kt * a.hkv), dim3(2 * kThreads), 0, stream, a);
     return hipGetLastError();
 }

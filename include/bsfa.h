@@ -215,9 +215,9 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
  * [sk, hkv, d]: fp32, contiguous, 16-byte aligned, fully written (rows no key reaches
  * get zeros).  delta: caller scratch of LSE's shape (fp32 [hq, lse_stride_head]),
  * overwritten with D.  The plan must have bq = 128 and bk = 128 and be uploaded to the
- * current device.  Three kernels on stream: D, dQ (by query tile), dK/dV (by key tile
- * over the query heads of its key/value head: no atomics, deterministic).  No
- * allocation, no synchronisation.
+ * current device.  Two kernels on stream: dQ by query tile (which also computes and
+ * stores D), then dK/dV by key tile over the query heads of its key/value head (no
+ * atomics, deterministic).  No allocation, no synchronisation.
  * Errors: BSFA_ERR_ARG, BSFA_ERR_ALIGN, BSFA_ERR_SHAPE, BSFA_ERR_UNSUPPORTED (d not 64/
  * 128, tiles not 128 x 128), BSFA_ERR_STATE, BSFA_ERR_HIP. */
 bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
