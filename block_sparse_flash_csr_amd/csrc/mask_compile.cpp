@@ -220,30 +220,38 @@ void build_transpose(bsfa_plan &p)
     // workgroup i to XCD i mod 8; when the heads split evenly over the 8 XCDs, XCD x gets
     // a contiguous block of heads (their rows share its L2) and item j of its own
     // longest-first list runs as workgroup 8 j + x.
-    auto order = [&](int32_t n_heads, int32_t n_t, auto cost_of, std::vector<int32_t> &out) {
-        const int64_t n = (int64_t)n_heads * n_t;
-        out.resize((size_t)n);
-        auto by_cost = [&](int32_t a, int32_t b) {
-            const int64_t ca = cost_of(a % n_t), cb = cost_of(b % n_t);
-            return ca != cb ? ca > cb : a < b;
+    // The cost is the same for every head, so the tiles are sorted once (counting sort
+    // by cost, descending, ties by tile) and expanded: among equal costs, items go in
+    // ascending id (head-major), which is the same order as sorting the items by
+    // (cost descending, id ascending).
+    auto order = [&](int32_t n_heads, int32_t n_t, const std::vector<int32_t> &ptr, std::vector<int32_t> &out) {
+        int32_t cmax = 0;
+        for (int32_t t = 0; t < n_t; ++t) cmax = std::max(cmax, ptr[(size_t)t + 1] - ptr[t]);
+        std::vector<int32_t> start((size_t)cmax + 2, 0), tiles((size_t)n_t);
+        for (int32_t t = 0; t < n_t; ++t) ++start[(size_t)(cmax - (ptr[(size_t)t + 1] - ptr[t])) + 1];
+        for (int32_t c = 0; c <= cmax; ++c) start[(size_t)c + 1] += start[c];
+        {
+            std::vector<int32_t> fill(start.begin(), start.end() - 1);
+            for (int32_t t = 0; t < n_t; ++t) tiles[(size_t)fill[(size_t)(cmax - (ptr[(size_t)t + 1] - ptr[t]))]++] = t;
+        }
+        // items of heads [h0, h1) in (cost desc, id asc) order, written at out[o0 + j * stride]
+        auto expand = [&](int32_t h0, int32_t h1, size_t o0, size_t stride) {
+            size_t j = 0;
+            for (int32_t c = 0; c <= cmax; ++c)
+                for (int32_t h = h0; h < h1; ++h)
+                    for (int32_t k = start[c]; k < start[(size_t)c + 1]; ++k)
+                        out[o0 + (j++) * stride] = h * n_t + tiles[(size_t)k];
         };
+        out.resize((size_t)n_heads * n_t);
         if (n_heads % kNumXcd == 0) {
             const int32_t per = n_heads / kNumXcd;
-            std::vector<int32_t> list((size_t)per * n_t);
-            for (int32_t x = 0; x < kNumXcd; ++x) {
-                for (int32_t k = 0; k < per * n_t; ++k) list[(size_t)k] = (x * per) * n_t + k;
-                std::stable_sort(list.begin(), list.end(), by_cost);
-                for (int32_t j = 0; j < per * n_t; ++j) out[(size_t)j * kNumXcd + x] = list[(size_t)j];
-            }
+            for (int32_t x = 0; x < kNumXcd; ++x) expand(x * per, (x + 1) * per, (size_t)x, kNumXcd);
         } else {
-            for (int64_t k = 0; k < n; ++k) out[(size_t)k] = (int32_t)k;
-            std::stable_sort(out.begin(), out.end(), by_cost);
+            expand(0, n_heads, 0, 1);
         }
     };
-    order(p.hq, p.n_qt, [&](int32_t qt) { return (int64_t)p.row_ptr[(size_t)qt + 1] - p.row_ptr[qt]; },
-          p.dq_order);
-    order(p.hkv, p.n_kt, [&](int32_t kt) { return (int64_t)p.t_ptr[(size_t)kt + 1] - p.t_ptr[kt]; },
-          p.dkv_order);
+    order(p.hq, p.n_qt, p.row_ptr, p.dq_order);
+    order(p.hkv, p.n_kt, p.t_ptr, p.dkv_order);
 }
 
 }  // namespace bsfa
