@@ -232,7 +232,7 @@ __device__ __forceinline__ void static_for(F &&f)
 }
 
 // Operands are read this many products ahead of their MFMA (kernel 3, kernel 2).
-constexpr int kAheadKv = 3, kAheadQ = 2;
+constexpr int kAheadKv = 2, kAheadQ = 2;
 
 // S += X Y^T and dP += Z W^T over one 64-row LDS tile pair (x_t, z_t) against the register
 // fragments yf, wf (one 32-row block per wave), onto the caller's initial accumulators:
