@@ -80,3 +80,16 @@ def test_edge_cases():
     check([(0, 512, 0, 512, 1), (0, 512, 0, 512, 1), (100, 400, 50, 300, 0)], 512, 512, 128, 128,
           "duplicates")
     check([(0, 1, 0, 1, 0)], 1, 1, 128, 128, "one pair")
+
+
+@pytest.mark.parametrize("kind", ["causal", "strided"])
+def test_benchmark_sizes_524288(kind):
+    """The 524,288-token masks the benchmark times: every array equal to the host plan's
+    (the oracle's row-by-row classification would take minutes at this size)."""
+    S = 524288
+    if kind == "causal":
+        sl = [(0, S, 0, S, 1)]
+    else:
+        sl = W.block_slices(W.strided_block_codes(S // 128, 8), 128, 128, S, S)
+    v = check(api.slice_array(sl), S, S, 128, 128, f"{kind} s{S}", with_oracle=False)
+    say(f"{kind} s{S}: nnz {v['nnz']} ({v['n_full']} F + {v['n_partial']} P), {v['touches']} touches")
