@@ -235,14 +235,13 @@ __device__ __forceinline__ void static_for(F &&f)
 constexpr int kAheadKv = 2, kAheadQ = 2;
 
 // S += X Y^T and dP += Z W^T over one 64-row LDS tile pair (x_t, z_t) against the register
-// fragments yf, wf (one 32-row block per wave), onto the caller's initial accumulators:
-// product i -> S (i even) or dP (i odd),
-// row block (i >> 1) & 1, k-step i >> 2, so four independent accumulator chains rotate.
-// The tile reads run kAhead products ahead; `tail` runs once the last read is issued.
-template <int D, int AH, typename Tail>
+// fragments yf, wf (one 32-row block per wave): product i -> S (i even) or dP (i odd),
+// row block (i >> 1) & 1, k-step i >> 2, so four independent accumulator chains rotate;
+// the tile reads run AH products ahead.
+template <int D, int AH>
 __device__ __forceinline__ void score_products(const char *x_t, const char *z_t, const bf16x8 (&yf)[BCfg<D>::KS],
                                                const bf16x8 (&wf)[BCfg<D>::KS], const Addr<D> &ad, f32x16 (&s)[2],
-                                               f32x16 (&dp)[2], Tail tail)
+                                               f32x16 (&dp)[2])
 {
     constexpr int N1 = 4 * BCfg<D>::KS;
     auto rd1 = [&](int i) { return rd_row<D>((i & 1) ? z_t : x_t, ad, (i >> 1) & 1, i >> 2); };
@@ -253,20 +252,11 @@ __device__ __forceinline__ void score_products(const char *x_t, const char *z_t,
 #pragma unroll
     for (int i = 0; i < N1; ++i) {
         if (i + AH < N1) op[(i + AH) % (AH + 1)] = rd1(i + AH);
-        if (i + AH == N1) tail();
         const int b = (i >> 1) & 1, ks = i >> 2;
         if (i & 1) dp[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (AH + 1)], wf[ks], dp[b], 0, 0, 0);
         else s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % (AH + 1)], yf[ks], s[b], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
-}
-
-template <int D, int AH>
-__device__ __forceinline__ void score_products(const char *x_t, const char *z_t, const bf16x8 (&yf)[BCfg<D>::KS],
-                                               const bf16x8 (&wf)[BCfg<D>::KS], const Addr<D> &ad, f32x16 (&s)[2],
-                                               f32x16 (&dp)[2])
-{
-    score_products<D, AH>(x_t, z_t, yf, wf, ad, s, dp, []() {});
 }
 
 // ---------------------------------------------------------------------------
