@@ -61,8 +61,6 @@ struct BCfg {
     static constexpr int TILE_B = kStep * ROWB; // bytes of a 64-row tile
     static constexpr int KS = D / 16;           // k-steps over the head dim
     static constexpr int DB = D / 32;           // 32-row blocks over the head dim
-    static constexpr int NBLK = TILE_B / 1024;  // 1 KB direct-load blocks per tile
-    static_assert(NBLK % 4 == 0, "the 4 waves share a tile's blocks evenly");
 };
 
 // 16-byte chunk c of tile row r sits at chunk c ^ swz(r).  The pattern serves both reads
@@ -261,8 +259,8 @@ __device__ __forceinline__ void score_products(const char *x_t, const char *z_t,
 
 // ---------------------------------------------------------------------------
 // kernel 2: dQ by query tile (one workgroup per (head, query tile), in the plan's launch
-// order), 64-key steps over the CSR row; the K and
-// V tiles of step j + 1 load (LDS double buffer) while step j computes
+// order), 64-key steps over the CSR row; the K and V tiles of step j + 1 load (LDS
+// double buffer) while step j computes
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqTiles {
@@ -283,7 +281,6 @@ __device__ __forceinline__ void dq_step(char *__restrict__ kd, char *__restrict_
                                         f32x16 (&acc)[BCfg<D>::DB])
 {
     using C = BCfg<D>;
-    const int l32 = lane & 31, hh = lane >> 5;
     if (issue) {
         tile_dma<D>(rk, k_st, kd, wave, lane);
         tile_dma<D>(rv, v_st, vd, wave, lane);
@@ -443,10 +440,6 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
     }
 }
 
-struct RowSrc {
-    __amdgpu_buffer_rsrc_t q, g, l, d;
-};
-
 // ---------------------------------------------------------------------------
 // kernel 3: dK, dV by key tile (one workgroup per (kv head, key tile), in the plan's
 // launch order), 64-query steps over the CSR column for every query head of the key /
@@ -456,6 +449,11 @@ struct RowSrc {
 // workgroup and are read as MFMA operands (so a wave holds only its dK, dV partials and
 // the step's scores); the two waves of a key block add their partials at the end.
 // ---------------------------------------------------------------------------
+// buffer ranges of one step's Q rows, dO rows, LSE and D
+struct RowSrc {
+    __amdgpu_buffer_rsrc_t q, g, l, d;
+};
+
 template <int D>
 struct Kv2Tiles {
     static constexpr int K0 = 0, V0 = 2 * kStep * BCfg<D>::ROWB, T0 = 4 * kStep * BCfg<D>::ROWB;
