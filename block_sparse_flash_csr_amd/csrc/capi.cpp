@@ -667,6 +667,8 @@ bsfa_status bsfa_attn_merge(const void *const *o_parts, const float *const *lse_
     if (n < 1 || n > BSFA_MERGE_MAX_PARTS || n_tok < 0 || n_head < 0 || n_head > 65535)
         return BSFA_ERR_ARG;
     if (d != 64 && d != 128) return BSFA_ERR_UNSUPPORTED;
+    // one workgroup per (16 tokens, head) at d 128 (32 at d 64) in a 1-D grid
+    if (((int64_t)n_tok + 15) / 16 * n_head >= INT32_MAX) return BSFA_ERR_UNSUPPORTED;
     if (lse_stride_head < n_tok) return BSFA_ERR_ARG;
     if (!stride_ok(part_stride_tok) || !stride_ok(part_stride_head) || !stride_ok(o->stride_tok) ||
         !stride_ok(o->stride_head))

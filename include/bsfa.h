@@ -233,7 +233,8 @@ bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
  * [n_tok, n_head, d] tensor with the strides of o_parts_view, every LSE_t an fp32
  * [n_head, lse_stride_head] array.  o (bf16, strides from o->stride_*) and lse receive
  * the result and must not overlap any partial.  1 <= n <= BSFA_MERGE_MAX_PARTS,
- * d in {64, 128}.
+ * d in {64, 128}, ceil(n_tok / 16) * n_head < 2^31.  Partials and result are streamed
+ * with non-temporal accesses (they bypass the caches' retention).
  * Errors: BSFA_ERR_ARG, BSFA_ERR_ALIGN, BSFA_ERR_UNSUPPORTED, BSFA_ERR_HIP. */
 enum { BSFA_MERGE_MAX_PARTS = 16 };
 bsfa_status bsfa_attn_merge(const void *const *o_parts, const float *const *lse_parts, int32_t n,
