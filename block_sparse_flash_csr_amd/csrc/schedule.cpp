@@ -26,22 +26,39 @@ namespace bsfa {
 
 // LPT of items already in decreasing-cost order onto the given bins: each item to
 // the least-loaded bin (ties by bin id).  Appends (bin, item) in assignment order.
+// The bins sit in a binary min-heap keyed on (load, bin id); the root takes the item,
+// its load grows and one sift-down restores the heap (keys are unique, so the choice
+// is the same as any other exact min-heap's).
 void lpt_sorted(const std::vector<int32_t> &order, const std::vector<float> &cost,
                 const std::vector<int32_t> &bins, std::vector<std::pair<int32_t, int32_t>> &assign,
                 std::vector<double> &load)
 {
-    using Key = std::pair<double, int32_t>;
-    std::vector<Key> heap;
-    heap.reserve(bins.size());
-    for (int32_t b : bins) heap.push_back({load[b], b});
-    std::make_heap(heap.begin(), heap.end(), std::greater<Key>());
+    const size_t n = bins.size();
+    if (n == 0) return;
+    std::vector<double> hl(n);
+    std::vector<int32_t> hb(n);
+    auto less = [&](size_t i, size_t j) { return hl[i] < hl[j] || (hl[i] == hl[j] && hb[i] < hb[j]); };
+    auto sift_down = [&](size_t i) {
+        for (;;) {
+            size_t c = 2 * i + 1;
+            if (c >= n) break;
+            if (c + 1 < n && less(c + 1, c)) ++c;
+            if (!less(c, i)) break;
+            std::swap(hl[i], hl[c]);
+            std::swap(hb[i], hb[c]);
+            i = c;
+        }
+    };
+    for (size_t i = 0; i < n; ++i) {
+        hl[i] = load[(size_t)bins[i]];
+        hb[i] = bins[i];
+    }
+    for (size_t i = n / 2; i-- > 0;) sift_down(i);
     for (int32_t it : order) {
-        std::pop_heap(heap.begin(), heap.end(), std::greater<Key>());
-        Key &k = heap.back();
-        assign.push_back({k.second, it});
-        k.first += cost[it];
-        load[k.second] = k.first;
-        std::push_heap(heap.begin(), heap.end(), std::greater<Key>());
+        assign.push_back({hb[0], it});
+        hl[0] += cost[(size_t)it];
+        load[(size_t)hb[0]] = hl[0];
+        sift_down(0);
     }
 }
 
