@@ -285,6 +285,8 @@ __device__ __forceinline__ void dq_step(char *__restrict__ kd, char *__restrict_
         tile_dma<D>(rk, k_st, kd, wave, lane);
         tile_dma<D>(rv, v_st, vd, wave, lane);
     }
+    // a wave none of whose (query, key) pairs in this step is admitted adds nothing
+    if (masked_step && __builtin_amdgcn_ballot_w64(m != 0ull) == 0ull) return;
     // (the dK/dV kernel starts its accumulators at -LSE / scale and -D; here, at two waves
     // per SIMD, those 64 live values would not fit beside Q, dO and dQ, so S and dP start
     // at 0 and the offsets are applied in the exponential)
@@ -486,6 +488,8 @@ __device__ __forceinline__ void kv2_step(char *__restrict__ nxt, const char *__r
     using L = Kv2Tiles<D>;
     const int hh = lane >> 5;
     if (issue) kv2_issue<D>(nxt, src, q_st, do_st, wave, lane);
+    // a block no pair of which is admitted adds nothing (every lane's mask word is empty)
+    if (masked_step && __builtin_amdgcn_ballot_w64(mw != 0u) == 0ull) return;
     const char *qt_ = cur + L::Q0, *gt = cur + L::G0, *kt = kv + L::K0, *vt = kv + L::V0;
     const float *lse_s = (const float *)(cur + L::L0), *dlt_s = (const float *)(cur + L::D0);
     // accumulators start at -LSE / scale and -D of rows 32 qh + 8 g4 + 4 hh + t
