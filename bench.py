@@ -57,6 +57,23 @@ def measured_traffic():
         return None
 
 
+MFMA_PROFILE = os.path.join(ROOT, "profiles", "mfma_busy_and_stalls_default_workloads.md")
+
+
+def measured_mfma_busy():
+    """Percent of cycles the matrix cores were busy in the headline forward kernel
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs) from the committed counter
+    summary, or None when the kernel sources have changed since it was taken."""
+    try:
+        with open(MFMA_PROFILE) as f:
+            fields = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+        if fields.get("kernel_source_sha256", "").strip() != kernel_digest():
+            return None
+        return float(fields["headline_forward_mfma_busy_pct"].split()[0])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -365,7 +382,9 @@ def main():
                      "traffic_unit": "bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, copy-calibrated)",
                      "algorithmic_bytes": w.sq * w.hq * (4 * w.d + 4) + w.sk * w.hkv * 4 * w.d,
                      "kernel": "attn_fwd_kernel<128>", "kernel_ms": kernel_ms,
-                     "flops_per_launch": flops},
+                     "flops_per_launch": flops, "mfma_busy_pct": measured_mfma_busy(),
+                     "mfma_busy_source": "rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs), "
+                                         "committed counter summary; null once the kernel changed"},
         "cpu_baseline": cpu,
         "other_workloads": others,
     }

@@ -1,0 +1,52 @@
+"""Host-side checks of the benchmark script: the one-GPU guard and the committed
+counter summaries it reads its traffic and MFMA-busy figures from."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("path,key", [
+    (bench.TRAFFIC_PROFILE, "traffic_bytes_per_launch"),
+    (bench.MFMA_PROFILE, "headline_forward_mfma_busy_pct"),
+])
+def test_counter_summaries_carry_their_figure_and_source_digest(path, key):
+    with open(path) as f:
+        text = f.read()
+    assert f"\n{key}:" in text
+    assert "\nkernel_source_sha256:" in text
+    assert "rocprofv3 --pmc" in text          # the command that produced it
+
+
+def test_counter_figures_are_plausible_or_withheld():
+    t = bench.measured_traffic()
+    if t is not None:                          # withheld (None) once the kernel changed
+        algorithmic = 16384 * 16 * (4 * 128 + 4) + 16384 * 16 * 4 * 128
+        assert algorithmic <= t <= 10 * algorithmic
+    m = bench.measured_mfma_busy()
+    if m is not None:
+        assert 0.0 < m <= 100.0
+
+
+def test_digest_follows_the_kernel_sources(tmp_path, monkeypatch):
+    d0 = bench.kernel_digest()
+    src = tmp_path / "k.hip"
+    src.write_text("// a different kernel\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", (str(src),))
+    monkeypatch.setattr(bench, "ROOT", "/")
+    assert bench.kernel_digest() != d0
+    assert bench.measured_traffic() is None
+    assert bench.measured_mfma_busy() is None
