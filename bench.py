@@ -74,6 +74,25 @@ def measured_mfma_busy():
         return None
 
 
+MERGE_PROFILE = os.path.join(ROOT, "profiles", "merge_and_backward_hbm_traffic.md")
+
+
+def measured_merge_traffic():
+    """HBM bytes per launch of the merge kernel (8 partials x 8192 tokens x 32 heads) from
+    the committed FETCH_SIZE / WRITE_SIZE summary, or None when attn_merge.hip changed."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "block_sparse_flash_csr_amd/csrc/attn_merge.hip"), "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+        with open(MERGE_PROFILE) as f:
+            fields = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+        if fields.get("merge_kernel_source_sha256", "").strip() != digest:
+            return None
+        return int(fields["merge_traffic_bytes_per_launch"].split()[0])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -275,12 +294,15 @@ def other_workloads(api, W, reps=10):
     fwd_ms = float(np.median(event_times(fwd_all, reps, stream)))
     merge_ms = float(np.median(event_times(merge, reps * 2, stream)))
     merge_bytes = (nc + 1) * c * w.hq * (2 * w.d + 4)
+    merge_traffic = measured_merge_traffic()    # HBM bytes per merge launch (counters)
     out[w.name] = {"forward_ms": fwd_ms, "merge_ms": merge_ms,
                    "forward_tflops": fl / fwd_ms * 1e-9,
                    "forward_frac_of_peak": fl / fwd_ms * 1e-9 / PEAK_BF16_TFLOPS,
                    "forward_plus_merge_tflops": fl / (fwd_ms + merge_ms) * 1e-9,
                    "merge_gbs": merge_bytes / merge_ms * 1e-6,
                    "merge_frac_of_hbm_peak": merge_bytes / merge_ms * 1e-6 / PEAK_HBM_GBS,
+                   "merge_traffic": merge_traffic,
+                   "merge_gbs_from_counters": None if merge_traffic is None else merge_traffic / merge_ms * 1e-6,
                    "pairs_per_head": pairs}
     log(f"{w.name}: fwd {fwd_ms:.3f} ms ({fl / fwd_ms * 1e-9:.1f} TFLOPS), merge {merge_ms:.3f} ms "
         f"({merge_bytes / merge_ms * 1e-6:.0f} GB/s)")

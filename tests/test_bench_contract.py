@@ -22,12 +22,13 @@ def test_more_than_one_gpu_is_refused():
 @pytest.mark.parametrize("path,key", [
     (bench.TRAFFIC_PROFILE, "traffic_bytes_per_launch"),
     (bench.MFMA_PROFILE, "headline_forward_mfma_busy_pct"),
+    (bench.MERGE_PROFILE, "merge_traffic_bytes_per_launch"),
 ])
 def test_counter_summaries_carry_their_figure_and_source_digest(path, key):
     with open(path) as f:
         text = f.read()
     assert f"\n{key}:" in text
-    assert "\nkernel_source_sha256:" in text
+    assert "kernel_source_sha256:" in text
     assert "rocprofv3 --pmc" in text          # the command that produced it
 
 
@@ -39,6 +40,10 @@ def test_counter_figures_are_plausible_or_withheld():
     m = bench.measured_mfma_busy()
     if m is not None:
         assert 0.0 < m <= 100.0
+    mt = bench.measured_merge_traffic()
+    if mt is not None:                         # 8 partials + result, O bf16 and LSE fp32
+        algorithmic = 9 * 8192 * 32 * (2 * 128 + 4)
+        assert algorithmic <= mt <= 1.05 * algorithmic
 
 
 def test_digest_follows_the_kernel_sources(tmp_path, monkeypatch):
