@@ -230,6 +230,26 @@ def random_inputs(rng, sq: int, sk: int, hq: int, hkv: int, d: int):
     return _draw_qkv(rng, sq, sk, hq, hkv, d)
 
 
+def device_normal_bf16(shape, seed: int):
+    """Standard normal bf16 tensor drawn on the current GPU by torch's seeded generator
+    (for inputs too large to draw on the host; tests copy back the parts they check)."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device="cuda", dtype=torch.bfloat16)
+
+
+def doc_lengths(rng, total: int, lo: int, hi: int):
+    """Document lengths drawn uniformly in [lo, hi) until they cover `total` tokens; the
+    last one is cut to fit (at least 1 token)."""
+    out, n = [], 0
+    while n < total:
+        L = min(int(rng.integers(lo, hi)), total - n)
+        out.append(L)
+        n += L
+    return out
+
+
 def random_grad(rng, sq: int, hq: int, d: int):
     """Upstream gradient dO [sq, hq, d]: standard normal, as bf16 bit patterns."""
     return bf16_bits(rng.standard_normal((sq, hq, d), dtype=np.float32))
