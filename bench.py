@@ -180,8 +180,32 @@ def other_workloads(api, W, reps=10):
         del q, k, v, o, lse
         torch.cuda.empty_cache()
 
-    # Backward at the varlen causal workload: one call runs delta = rowsum(dO*O), the dQ
-    # kernel (by query tile) and the dK/dV kernel (by key tile).  Algorithmic work is 5
+    # Head dim 64 on the headline mask (not a reference workload): per admitted pair the
+    # softmax's vector work is the same as at d = 128 and the matrix work half of it, so
+    # this line shows how far the vector units bound the smaller head dim.
+    w = W.config2(with_inputs=False)
+    hd = 64
+    q, k, v = (W.device_normal_bf16((w.sq, w.hq, hd), s) for s in (641, 642, 643))
+    plan = api.Plan.from_slices(w.slices, w.sq, w.sk, w.hq, w.hkv, hd).upload(stream)
+    info = plan.info()
+    fl = 4.0 * hd * info["pairs"] * w.hq
+    o = torch.empty((w.sq, w.hq, hd), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.hq, w.sq), dtype=torch.float32, device="cuda")
+    f = lambda: api.attn_fwd(q, k, v, plan, 1.0 / np.sqrt(hd), out=o, lse=lse, stream=stream)
+    for _ in range(3):
+        f()
+    ms = float(np.median(event_times(f, reps * 2, stream)))
+    name = "varlen_causal_t16384_docs8_h16_d64"
+    out[name] = {"kernel_ms": ms, "tflops": fl / ms * 1e-9, "frac_of_peak": fl / ms * 1e-9 / PEAK_BF16_TFLOPS,
+                 "pairs_per_head": info["pairs"],
+                 "note": "not a reference workload: the headline mask at head dim 64 (vector-bound)"}
+    log(f"{name}: {ms:.3f} ms  {fl / ms * 1e-9:.1f} TFLOPS")
+    plan.close()
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+    # Backward at the varlen causal workload: one call runs the dQ kernel (by query tile,
+    # which also forms D = rowsum(dO*O)) and the dK/dV kernel (by key tile).  Algorithmic work is 5
     # products of 2*d flops per admitted pair (S, dP, dV, dK, dQ); the kernels execute 7
     # (S and dP are recomputed by both gradient kernels instead of using atomics).
     w = W.config2()
