@@ -154,8 +154,23 @@ def headline(args, api, W):
     return w, info, flops, ms_per_step, kernel_ms, host_ms
 
 
-def other_workloads(api, W, reps=10):
-    """Kernel-time figures of the remaining workloads (event-timed, plan prebuilt)."""
+def sustain(f, seconds):
+    """Untimed launches of f for about `seconds`: the GPU clock ramps up over the first
+    few hundred milliseconds of load, so every timed figure starts from the sustained
+    clock, as the headline's pre-warm does."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    while True:
+        for _ in range(4):
+            f()
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            return
+
+
+def other_workloads(api, W, reps=10, warm_s=0.5):
+    """Kernel-time figures of the remaining workloads (event-timed, plan prebuilt, each
+    after warm_s seconds of untimed launches of the same call)."""
     import torch
     stream = torch.cuda.current_stream()
     out = {}
@@ -168,8 +183,7 @@ def other_workloads(api, W, reps=10):
         o = torch.empty((w.sq, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((w.hq, w.sq), dtype=torch.float32, device="cuda")
         f = lambda: api.attn_fwd(q, k, v, plan, w.scale, out=o, lse=lse, stream=stream)
-        for _ in range(3):
-            f()
+        sustain(f, warm_s)
         ms = float(np.median(event_times(f, reps, stream)))
         out[w.name] = {"kernel_ms": ms, "tflops": fl / ms * 1e-9,
                        "frac_of_peak": fl / ms * 1e-9 / PEAK_BF16_TFLOPS,
@@ -192,8 +206,7 @@ def other_workloads(api, W, reps=10):
     o = torch.empty((w.sq, w.hq, hd), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.hq, w.sq), dtype=torch.float32, device="cuda")
     f = lambda: api.attn_fwd(q, k, v, plan, 1.0 / np.sqrt(hd), out=o, lse=lse, stream=stream)
-    for _ in range(3):
-        f()
+    sustain(f, warm_s)
     ms = float(np.median(event_times(f, reps * 2, stream)))
     name = "varlen_causal_t16384_docs8_h16_d64"
     out[name] = {"kernel_ms": ms, "tflops": fl / ms * 1e-9, "frac_of_peak": fl / ms * 1e-9 / PEAK_BF16_TFLOPS,
@@ -221,8 +234,7 @@ def other_workloads(api, W, reps=10):
     delta = torch.empty_like(lse)
     f = lambda: api.attn_bwd(q, k, v, o, g, lse, plan, w.scale, dq=dq, dk=dk, dv=dv, delta=delta,
                              stream=stream)
-    for _ in range(3):
-        f()
+    sustain(f, warm_s)
     ms = float(np.median(event_times(f, reps * 2, stream)))
     name = w.name + "_backward"
     out[name] = {"kernel_ms": ms, "tflops": fl / ms * 1e-9, "frac_of_peak": fl / ms * 1e-9 / PEAK_BF16_TFLOPS,
@@ -279,8 +291,7 @@ def other_workloads(api, W, reps=10):
     o = torch.empty((sq, hq, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((hq, sq), dtype=torch.float32, device="cuda")
     f = lambda: api.attn_fwd(q, k, v, plan, 1.0 / np.sqrt(d), out=o, lse=lse, stream=stream)
-    for _ in range(3):
-        f()
+    sustain(f, warm_s)
     ms = float(np.median(event_times(f, reps * 2, stream)))
     name = f"prefill_chunk_q{sq}_ctx{sk}_gqa{hq}x{hkv}_d{d}"
     out[name] = {"kernel_ms": ms, "tflops": fl / ms * 1e-9, "frac_of_peak": fl / ms * 1e-9 / PEAK_BF16_TFLOPS,
@@ -312,9 +323,7 @@ def other_workloads(api, W, reps=10):
     def merge():
         api.attn_merge(os_, ls_, out=om, lse=lm, stream=stream)
 
-    for _ in range(2):
-        fwd_all()
-        merge()
+    sustain(lambda: (fwd_all(), merge()), warm_s)
     fwd_ms = float(np.median(event_times(fwd_all, reps, stream)))
     merge_ms = float(np.median(event_times(merge, reps * 2, stream)))
     merge_bytes = (nc + 1) * c * w.hq * (2 * w.d + 4)
@@ -400,7 +409,7 @@ def main():
     log(f"headline: step {ms_per_step:.4f} ms ({value:.1f} TFLOPS; host issue {host_ms:.4f} ms), "
         f"forward kernel {kernel_ms:.4f} ms "
         f"({achieved:.1f} TFLOPS, {achieved / PEAK_BF16_TFLOPS:.3f} of peak)")
-    others = {} if args.quick else other_workloads(api, W)
+    others = {} if args.quick else other_workloads(api, W, warm_s=0.5 * args.prewarm_s)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, info, args.cpu_seconds)
 
     result = {
