@@ -55,3 +55,25 @@ def test_digest_follows_the_kernel_sources(tmp_path, monkeypatch):
     assert bench.kernel_digest() != d0
     assert bench.measured_traffic() is None
     assert bench.measured_mfma_busy() is None
+
+
+def test_per_workload_counters_cover_every_reference_workload():
+    with open(bench.COUNTERS_PROFILE) as f:
+        text = f.read()
+    assert "rocprofv3 --pmc" in text and "bench.py --counter-pass" in text
+    c = bench.measured_workload_counters()
+    if not c:                                  # withheld once the kernels changed
+        return
+    from block_sparse_flash_csr_amd import workloads as W
+    names = [W.CONFIGS[i](with_inputs=False).name for i in (1, 2, 3, 4, 5)]
+    for name in names + [names[-1] + "_merge"]:
+        assert name in c, name
+        assert 0.0 <= c[name]["mfma_busy_pct"] <= 100.0
+        assert 0.0 <= c[name]["l2_hit_pct"] <= 100.0
+        assert c[name]["hbm_bytes_per_launch"] > 0
+
+
+def test_per_workload_counters_are_withheld_when_the_kernel_changes(monkeypatch):
+    monkeypatch.setattr(bench, "kernel_digest", lambda: "0" * 64)
+    c = bench.measured_workload_counters()
+    assert all(name.endswith("_merge") for name in c)
