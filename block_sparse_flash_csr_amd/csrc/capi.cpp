@@ -4,6 +4,7 @@
 #include <cmath>
 #include <algorithm>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -167,6 +168,8 @@ struct DevSlot {
     bool lent = false;
     std::vector<hipEvent_t> released;   // recorded at destruction, one per stream
     int n_released = 0;                 // how many of them the last destruction recorded
+    hipEvent_t ready = nullptr;         // recorded on the copy stream behind the upload
+    std::atomic<bool> ready_seen{false};  // the upload is known to have completed
 };
 std::mutex g_dev_mu;
 std::vector<DevSlot *> g_dev;
@@ -185,6 +188,7 @@ bsfa_status dev_acquire(int dev, size_t bytes, DevSlot **out)
         if (d->device != dev || d->cap < bytes || d->lent || !slot_idle(d)) continue;
         d->lent = true;
         d->n_released = 0;
+        d->ready_seen = false;
         *out = d;
         return BSFA_OK;
     }
@@ -197,18 +201,40 @@ bsfa_status dev_acquire(int dev, size_t bytes, DevSlot **out)
         delete d;
         return e == hipErrorOutOfMemory ? BSFA_ERR_OOM : BSFA_ERR_HIP;
     }
+    if (hipEventCreateWithFlags(&d->ready, hipEventDisableTiming) != hipSuccess) {
+        (void)hipFree(d->ptr);
+        delete d;
+        return BSFA_ERR_HIP;
+    }
     d->cap = cap;
     d->device = dev;
     d->lent = true;
     try {
         g_dev.push_back(d);
     } catch (const std::bad_alloc &) {
+        (void)hipEventDestroy(d->ready);
         (void)hipFree(d->ptr);
         delete d;
         return BSFA_ERR_OOM;
     }
     *out = d;
     return BSFA_OK;
+}
+
+// Orders a launch that reads the plan's device metadata after the copy that filled
+// it: nothing to do once the copy is known to have completed (then no cross-stream
+// dependency is enqueued at all), else the launch stream waits for it.
+bsfa_status meta_ready(const bsfa_plan *p, hipStream_t s)
+{
+    DevSlot *d = (DevSlot *)p->slot;
+    if (d->ready_seen.load(std::memory_order_acquire)) return BSFA_OK;
+    const hipError_t q = hipEventQuery(d->ready);
+    if (q == hipSuccess) {
+        d->ready_seen.store(true, std::memory_order_release);
+        return BSFA_OK;
+    }
+    if (q != hipErrorNotReady) return BSFA_ERR_HIP;
+    return hipStreamWaitEvent(s, d->ready, 0) == hipSuccess ? BSFA_OK : BSFA_ERR_HIP;
 }
 
 // Hands the buffer back behind the work already enqueued on the given streams.  If an
@@ -359,7 +385,9 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     }
     void *d = slot->ptr;
     // The copy runs on the internal copy stream (the buffer is idle, nothing earlier on
-    // s touches it) and s waits for it; the pinned image stays reserved until it has run.
+    // s touches it); the pinned image stays reserved until it has run.  Launches that
+    // read the metadata are ordered after it (meta_ready): a plan built ahead of its
+    // launch costs the launch stream no cross-stream dependency.
     hipStream_t cs = nullptr;
     try {
         cs = copy_stream(dev);
@@ -367,7 +395,7 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
         cs = nullptr;
     }
     if (!cs || hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, cs) != hipSuccess ||
-        hipEventRecord(stg->copied, cs) != hipSuccess || hipStreamWaitEvent(s, stg->copied, 0) != hipSuccess) {
+        hipEventRecord(stg->copied, cs) != hipSuccess || hipEventRecord(slot->ready, cs) != hipSuccess) {
         std::vector<hipStream_t> rel;
         if (cs) rel.push_back(cs);
         rel.push_back(s);
@@ -563,6 +591,8 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
             }
         }
     }
+    const bsfa_status rs = meta_ready(p, s);
+    if (rs != BSFA_OK) return rs;
     if (launch_attn_fwd(a, p->d, s) != hipSuccess) return BSFA_ERR_HIP;
     if (!p->splits.empty()) {
         SplitMergeArgs m;
@@ -654,6 +684,8 @@ bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
             }
         }
     }
+    const bsfa_status rs = meta_ready(p, s);
+    if (rs != BSFA_OK) return rs;
     if (launch_attn_bwd(a, p->d, s) != hipSuccess) return BSFA_ERR_HIP;
     return BSFA_OK;
 }

@@ -121,9 +121,12 @@ bsfa_status bsfa_plan_from_blocks(const uint8_t *codes, int32_t nbq, int32_t nbk
                                   bsfa_plan **out);
 
 /* Copy the plan's metadata to the current HIP device.  The copy runs on an internal
- * per-device copy stream (so it overlaps kernels already enqueued on stream) and
- * stream waits for it: work enqueued on stream afterwards sees the metadata; other
- * streams must be ordered after stream by the caller.  The device buffer comes from a
+ * per-device copy stream (so it overlaps kernels already enqueued on stream); every
+ * library launch that reads the metadata (bsfa_attn_fwd, bsfa_attn_bwd), on any
+ * stream, is ordered after it: once the copy is seen complete nothing is enqueued,
+ * before that the launch stream waits for it, so a plan uploaded ahead of its launch
+ * adds no cross-stream dependency.  stream is the stream the device buffer is also
+ * released behind (with every launch stream) at bsfa_plan_destroy.  The device buffer comes from a
  * per-device pool the library owns: buffers are
  * allocated on first need, reused by later plans and held until process exit, so a
  * steady stream of plans allocates nothing and never synchronises.  Must precede

@@ -274,6 +274,43 @@ def test_plan_churn_reuses_buffers_safely():
         assert torch.equal(o, ref[m][0]) and torch.equal(l, ref[m][1]), f"plan {i} (mask {m}) differs"
 
 
+def test_plans_uploaded_ahead_and_launched_on_any_stream():
+    """Each plan is uploaded one iteration before its launch (the benchmark's pipeline)
+    and launched on a stream the caller never ordered after the upload: every launch is
+    ordered after its plan's copy by the library itself."""
+    import torch
+    sq = sk = 512
+    d = 128
+    rng = np.random.default_rng(23)
+    qb, kb, vb = W.random_inputs(rng, sq, sk, 2, 2, d)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    masks = [[(0, sq, 0, sk, 1)], W.random_slices(rng, sq, sk, 7), W.random_slices(rng, sq, sk, 3)]
+    ref = []
+    for m in masks:
+        p = api.Plan.from_slices(m, sq, sk, 2, 2, d).upload()
+        o, l = api.attn_fwd(q, k, v, p, 0.09)
+        torch.cuda.synchronize()
+        ref.append((o.clone(), l.clone()))
+        p.close()
+    n = 30
+    outs = [(torch.empty((sq, 2, d), dtype=torch.bfloat16, device="cuda"),
+             torch.empty((2, sq), dtype=torch.float32, device="cuda")) for _ in range(n)]
+    up = torch.cuda.Stream()
+    runs = [torch.cuda.current_stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    say(f"plans uploaded ahead: {n} launches over two streams, uploads on a third")
+    nxt = api.Plan.from_slices(masks[0], sq, sk, 2, 2, d).upload(up)
+    for i in range(n):
+        cur = nxt
+        nxt = api.Plan.from_slices(masks[(i + 1) % 3], sq, sk, 2, 2, d).upload(up)
+        api.attn_fwd(q, k, v, cur, 0.09, out=outs[i][0], lse=outs[i][1], stream=runs[i % 2])
+        cur.close()
+    nxt.close()
+    torch.cuda.synchronize()
+    for i, (o, l) in enumerate(outs):
+        assert torch.equal(o, ref[i % 3][0]) and torch.equal(l, ref[i % 3][1]), f"launch {i} differs"
+
+
 # ---------------------------------------------------------------------------
 # rows split into parts inside one call (partials merged by a second kernel)
 # ---------------------------------------------------------------------------
