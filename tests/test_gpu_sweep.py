@@ -1,0 +1,90 @@
+"""Seeded sweep of small random problems through the C ABI against the fp64 oracle:
+shapes, head groupings, head dims, plan key-tile widths and slice lists all drawn from
+one generator per case, so that ragged tails, empty rows, overlapping full and causal
+slices and GQA groupings meet in combinations the hand-written cases do not list.
+Forward: max|dO| <= 1e-2, max|dLSE| <= 1e-3; backward: max|d| <= 1e-2 * max(1, max|ref|).
+
+V is drawn with standard deviation 0.5 (the N(0,1) draw halved, exactly in bf16): with
+few keys per row an output is a mix of one or two value rows, and where |O| >= 2 the
+bf16 output format alone rounds by up to 2^-7 (0.0078; 0.0156 at |O| >= 4), which leaves
+the 1e-2 bar no room for the bf16 weights; the workload tests keep N(0,1) V, whose rows
+mix many keys."""
+import numpy as np
+import pytest
+
+import oracle
+from block_sparse_flash_csr_amd import api
+from block_sparse_flash_csr_amd import workloads as W
+
+from gpu_helpers import compare, dev_bf16, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = 1e-2
+HEADS = [(1, 1), (2, 1), (2, 2), (4, 2), (3, 3), (8, 2), (6, 1)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    api.library()
+    yield
+    torch.cuda.synchronize()
+
+
+def draw_case(seed):
+    rng = np.random.default_rng(10_000 + seed)
+    sq = int(rng.integers(1, 700))
+    sk = int(rng.integers(1, 700))
+    hq, hkv = HEADS[int(rng.integers(0, len(HEADS)))]
+    d = (64, 128)[int(rng.integers(0, 2))]
+    bk = (64, 128)[int(rng.integers(0, 2))]
+    n = int(rng.integers(0, 11))
+    slices = W.random_slices(rng, sq, sk, n)
+    if rng.random() < 0.3:      # a whole-range slice of either type on top
+        slices.append((0, sq, 0, sk, int(rng.integers(0, 2))))
+    scale = float(rng.uniform(0.03, 0.3))
+    qb, kb, vb = W.random_inputs(rng, sq, sk, hq, hkv, d)
+    vb = W.bf16_bits(0.5 * W.bf16_to_f32(vb))
+    return rng, sq, sk, hq, hkv, d, bk, slices, scale, qb, kb, vb
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_forward_sweep(seed):
+    import torch
+    _, sq, sk, hq, hkv, d, bk, slices, scale, qb, kb, vb = draw_case(seed)
+    what = f"sweep fwd seed={seed} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} bk={bk} slices={len(slices)}"
+    say(what)
+    plan = api.Plan.from_slices(slices, sq, sk, hq, hkv, d, bk=bk).upload()
+    o, lse = api.attn_fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), plan, scale)
+    torch.cuda.synchronize()
+    plan.close()
+    o_ref, lse_ref = oracle.attn_fwd(qb, kb, vb, slices, scale)
+    compare(W.bf16_to_f32(host_bits(o)), lse.cpu().numpy().T, o_ref, lse_ref.T, what)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_backward_sweep(seed):
+    import torch
+    rng, sq, sk, hq, hkv, d, bk, slices, scale, qb, kb, vb = draw_case(seed)
+    if bk != 128:               # the backward runs on 128-key tile plans
+        bk = 128
+    gb = W.random_grad(rng, sq, hq, d)
+    what = f"sweep bwd seed={seed} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} slices={len(slices)}"
+    say(what)
+    plan = api.Plan.from_slices(slices, sq, sk, hq, hkv, d, bk=bk).upload()
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    o, lse = api.attn_fwd(q, k, v, plan, scale)
+    got = api.attn_bwd(q, k, v, o, dev_bf16(gb), lse, plan, scale)
+    torch.cuda.synchronize()
+    plan.close()
+    ref = oracle.attn_bwd(qb, kb, vb, gb, slices, scale)
+    for name, x, r in zip(("dQ", "dK", "dV"), got, ref):
+        x = x.cpu().numpy().astype(np.float64)
+        assert not np.isnan(x).any(), f"{what}: NaN in {name}"
+        err = float(np.max(np.abs(x - r))) if r.size else 0.0
+        mag = float(np.max(np.abs(r))) if r.size else 0.0
+        say(f"  {name}: max|d| {err:.3e} (max|ref| {mag:.3e})")
+        assert err <= GRAD_TOL * max(1.0, mag), f"{what}: {name} error {err} (max|ref| {mag})"
