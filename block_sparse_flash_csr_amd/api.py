@@ -115,7 +115,11 @@ def _ptr(a: np.ndarray):
 
 
 def slice_array(slices) -> np.ndarray:
-    """Slices (q0, q1, k0, k1, type) as a contiguous int32 [n, 5] array (bsfa_slice layout)."""
+    """Slices (q0, q1, k0, k1, type) as a contiguous int32 [n, 5] array (bsfa_slice layout).
+    An array already in that layout is passed through without a copy."""
+    if (isinstance(slices, np.ndarray) and slices.dtype == np.int32 and slices.ndim == 2
+            and slices.shape[1] == 5 and slices.flags.c_contiguous):
+        return slices
     arr = np.ascontiguousarray(np.asarray(slices, dtype=np.int64).reshape(-1, 5))
     if arr.size and (arr.min() < np.iinfo(np.int32).min or arr.max() > np.iinfo(np.int32).max):
         raise ValueError("slice bounds must fit in int32")
