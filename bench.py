@@ -322,10 +322,16 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
         v = dc.view()
         dev_ms = (time.perf_counter() - t0) * 1e3
         assert v["nnz"] == nnz
+        # a full plan (column view and schedule too) from the device CSR
+        t0 = time.perf_counter()
+        dp = dc.plan(16, 16, 128)
+        dplan_ms = dev_ms + (time.perf_counter() - t0) * 1e3
+        dp.close()
         mc[name] = {"slices": len(sl), "nnz": nnz, "touches": v["touches"], "host_plan_ms": host_ms,
-                    "device_csr_ms": dev_ms, "device_stream_ms": e0.elapsed_time(e1)}
+                    "device_csr_ms": dev_ms, "device_stream_ms": e0.elapsed_time(e1),
+                    "plan_from_device_csr_ms": dplan_ms}
         log(f"mask compile {name}: host plan {host_ms:.1f} ms, device CSR {dev_ms:.2f} ms "
-            f"(stream {e0.elapsed_time(e1):.2f} ms), nnz {nnz}")
+            f"(stream {e0.elapsed_time(e1):.2f} ms), plan from device CSR {dplan_ms:.1f} ms, nnz {nnz}")
         dc.close()
     out["mask_compile"] = mc
 

@@ -92,6 +92,7 @@ def library():
     lib.bsfa_dcsr_view_get.argtypes = [P, ctypes.POINTER(DcsrView)]
     lib.bsfa_dcsr_export.argtypes = [P, P, P, P, P, P, I64, I64]
     lib.bsfa_dcsr_destroy.argtypes = [P]
+    lib.bsfa_plan_from_dcsr.argtypes = [P, I32, I32, I32, PP]
     lib.bsfa_dcsr_destroy.restype = None
     lib.bsfa_status_str.argtypes = [I32]
     lib.bsfa_status_str.restype = ctypes.c_char_p
@@ -99,7 +100,7 @@ def library():
                  "bsfa_plan_upload", "bsfa_plan_get_info", "bsfa_plan_export_csr",
                  "bsfa_plan_export_schedule", "bsfa_plan_export_units", "bsfa_attn_fwd",
                  "bsfa_attn_merge", "bsfa_attn_bwd", "bsfa_plan_export_pieces", "bsfa_dcsr_build",
-                 "bsfa_dcsr_view_get", "bsfa_dcsr_export"):
+                 "bsfa_dcsr_view_get", "bsfa_dcsr_export", "bsfa_plan_from_dcsr"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -167,6 +168,13 @@ class DeviceCsr:
             self._h, _ptr(row_ptr), _ptr(col), _ptr(tag), _ptr(piece_ptr), _ptr(pieces),
             v["nnz"], v["n_pieces"]))
         return row_ptr, col[:v["nnz"]], tag[:v["nnz"]], piece_ptr, pieces[:v["n_pieces"]]
+
+    def plan(self, hq, hkv, d) -> "Plan":
+        """A (not yet uploaded) plan over this CSR: the same plan Plan.from_slices builds
+        for the same slices and tile sizes (bsfa_plan_from_dcsr)."""
+        h = ctypes.c_void_p()
+        _check("bsfa_plan_from_dcsr", library().bsfa_plan_from_dcsr(self._h, hq, hkv, d, ctypes.byref(h)))
+        return Plan(h)
 
     def close(self):
         if self._h is not None and self._h.value:

@@ -269,6 +269,12 @@ void dev_release(DevSlot *d, const std::vector<hipStream_t> &streams)
     if (ok) d->lent = false;
 }
 
+// A device-compiled CSR with the extents it was compiled for (a plan built from it
+// needs them).  Created and destroyed only in this file.
+struct DcsrEx : bsfa_dcsr {
+    int32_t sq = 0, sk = 0, bq = 0, bk = 0;
+};
+
 }  // namespace
 
 extern "C" {
@@ -807,12 +813,16 @@ bsfa_status bsfa_dcsr_build(const bsfa_slice *slices, int32_t n_slices, int32_t 
             total += hi - lo;
         });
     }
-    bsfa_dcsr *c = new (std::nothrow) bsfa_dcsr;
+    DcsrEx *c = new (std::nothrow) DcsrEx;
     if (!c) {
         staging_release_now(stg);
         return BSFA_ERR_OOM;
     }
     c->device = dev;
+    c->sq = sq;
+    c->sk = sk;
+    c->bq = bq;
+    c->bk = bk;
     c->n_qt = n_qt;
     c->n_kt = n_kt;
     c->n_touch = n;
@@ -937,6 +947,70 @@ bsfa_status bsfa_dcsr_export(bsfa_dcsr *c, int32_t *row_ptr, int32_t *col, uint8
     return ok ? BSFA_OK : BSFA_ERR_HIP;
 }
 
+bsfa_status bsfa_plan_from_dcsr(bsfa_dcsr *csr, int32_t hq, int32_t hkv, int32_t d, bsfa_plan **out)
+{
+    if (!out) return BSFA_ERR_ARG;
+    *out = nullptr;
+    if (!csr || hq <= 0 || hkv <= 0 || d <= 0) return BSFA_ERR_ARG;
+    if (hq % hkv != 0) return BSFA_ERR_SHAPE;
+    const DcsrEx *x = static_cast<const DcsrEx *>(csr);
+    if ((int64_t)hq * x->n_qt >= (int64_t)1 << 31) return BSFA_ERR_ARG;
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return BSFA_ERR_HIP;
+    if (cur != x->device) return BSFA_ERR_STATE;
+    bsfa_dcsr_view v;
+    bsfa_status st = bsfa_dcsr_view_get(csr, &v);
+    if (st != BSFA_OK) return st;
+    bsfa_plan *p = new (std::nothrow) bsfa_plan;
+    if (!p) return BSFA_ERR_OOM;
+    p->sq = x->sq;
+    p->sk = x->sk;
+    p->hq = hq;
+    p->hkv = hkv;
+    p->d = d;
+    p->bq = x->bq;
+    p->bk = x->bk;
+    p->n_qt = x->n_qt;
+    p->n_kt = x->n_kt;
+    try {
+        p->row_ptr.resize((size_t)p->n_qt + 1);
+        p->col.resize((size_t)v.nnz);
+        p->tag.resize((size_t)v.nnz);
+        p->piece_ptr.resize((size_t)v.nnz + 1);
+        p->pieces.resize((size_t)v.n_pieces);
+    } catch (const std::bad_alloc &) {
+        delete p;
+        return BSFA_ERR_OOM;
+    }
+    // the device arrays are laid out as the host compiler's (Piece is the same 32-byte record)
+    bool ok = hipMemcpy(p->row_ptr.data(), v.row_ptr, p->row_ptr.size() * 4, hipMemcpyDeviceToHost) == hipSuccess;
+    ok = ok && hipMemcpy(p->piece_ptr.data(), v.piece_ptr, p->piece_ptr.size() * 4, hipMemcpyDeviceToHost) ==
+                   hipSuccess;
+    if (v.nnz > 0) {
+        ok = ok && hipMemcpy(p->col.data(), v.col, p->col.size() * 4, hipMemcpyDeviceToHost) == hipSuccess;
+        ok = ok && hipMemcpy(p->tag.data(), v.tag, p->tag.size(), hipMemcpyDeviceToHost) == hipSuccess;
+    }
+    if (v.n_pieces > 0)
+        ok = ok && hipMemcpy(p->pieces.data(), v.pieces, p->pieces.size() * sizeof(Piece), hipMemcpyDeviceToHost) ==
+                       hipSuccess;
+    if (!ok) {
+        delete p;
+        return BSFA_ERR_HIP;
+    }
+    p->n_full = v.n_full;
+    p->n_partial = v.n_partial;
+    p->pairs = v.pairs;
+    try {
+        build_transpose(*p);
+        build_schedule(*p, kNumCu * kBinsPerCu);
+    } catch (const std::bad_alloc &) {
+        delete p;
+        return BSFA_ERR_OOM;
+    }
+    *out = p;
+    return BSFA_OK;
+}
+
 void bsfa_dcsr_destroy(bsfa_dcsr *c)
 {
     if (!c) return;
@@ -945,7 +1019,7 @@ void bsfa_dcsr_destroy(bsfa_dcsr *c)
         (void)hipEventDestroy(c->done);
     }
     if (c->buf) (void)hipFree(c->buf);
-    delete c;
+    delete static_cast<DcsrEx *>(c);
 }
 
 const char *bsfa_status_str(bsfa_status s)

@@ -293,6 +293,17 @@ bsfa_status bsfa_dcsr_export(bsfa_dcsr *csr, int32_t *row_ptr, int32_t *col, uin
                              int32_t *piece_ptr, int32_t *pieces, int64_t cap_nnz, int64_t cap_pieces);
 void bsfa_dcsr_destroy(bsfa_dcsr *csr);
 
+/* A plan over a device-compiled tile CSR ([MA]: block-sparse mask generation without a
+ * dense mask, CSR mask metadata driving the kernels): waits for the compile, copies its
+ * CSR to the host and builds the column view and the schedule exactly as
+ * bsfa_plan_create does from the same slices and tile sizes, so the plan (CSR, pieces,
+ * schedule, launch orders) equals that plan field for field.  hq, hkv, d as for
+ * bsfa_plan_create; the extents and tile sizes are those csr was compiled with.  csr
+ * stays owned by the caller and may be destroyed afterwards.  The current device must
+ * be the one csr was built on.  Errors: BSFA_ERR_ARG, BSFA_ERR_SHAPE (hq % hkv),
+ * BSFA_ERR_STATE (another current device), BSFA_ERR_OOM, BSFA_ERR_HIP. */
+bsfa_status bsfa_plan_from_dcsr(bsfa_dcsr *csr, int32_t hq, int32_t hkv, int32_t d, bsfa_plan **out);
+
 const char *bsfa_status_str(bsfa_status status);
 
 #ifdef __cplusplus

@@ -161,3 +161,5 @@ def test_device_compiler_rejects_bad_arguments():
     assert lib.bsfa_dcsr_build(one, 1, 10, 10, 0, 128, None, ctypes.byref(h)) == 1     # bq = 0
     assert lib.bsfa_dcsr_build(one, 1, 10, 10, 128, 128, None, None) == 1              # no out
     assert lib.bsfa_dcsr_build(None, 1, 10, 10, 128, 128, None, ctypes.byref(h)) == 1  # no slices
+    assert lib.bsfa_plan_from_dcsr(None, 2, 1, 128, ctypes.byref(h)) == 1              # no csr
+    assert lib.bsfa_plan_from_dcsr(None, 2, 1, 128, None) == 1                         # no out

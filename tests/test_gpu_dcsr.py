@@ -93,3 +93,54 @@ def test_benchmark_sizes_524288(kind):
         sl = W.block_slices(W.strided_block_codes(S // 128, 8), 128, 128, S, S)
     v = check(api.slice_array(sl), S, S, 128, 128, f"{kind} s{S}", with_oracle=False)
     say(f"{kind} s{S}: nnz {v['nnz']} ({v['n_full']} F + {v['n_partial']} P), {v['touches']} touches")
+
+
+def _same_plan(a, b, what):
+    for name in ("csr", "pieces", "schedule", "units"):
+        for x, y in zip(getattr(a, name)(), getattr(b, name)()):
+            assert np.array_equal(x, y), f"{what}: {name}"
+    ia, ib = a.info(), b.info()
+    for k in ("nnz", "n_full", "n_partial", "n_pieces", "pairs", "n_items", "n_bins", "n_units", "n_splits"):
+        assert ia[k] == ib[k], f"{what}: {k}"
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_plan_from_device_csr_equals_host_plan(cfg):
+    """A plan over the device-compiled CSR is the host plan: CSR, pieces, schedule and
+    units equal, and the forward and backward outputs bit-identical."""
+    import torch
+    w = W.CONFIGS[cfg]()
+    say(f"plan from device CSR: {w.name}")
+    host = api.Plan.from_slices(w.slices, w.sq, w.sk, w.hq, w.hkv, w.d)
+    dc = api.DeviceCsr(w.slices, w.sq, w.sk)
+    dev = dc.plan(w.hq, w.hkv, w.d)
+    dc.close()                      # the plan owns copies of everything it needs
+    _same_plan(host, dev, w.name)
+    q, k, v = api.to_device_bf16(w.q), api.to_device_bf16(w.k), api.to_device_bf16(w.v)
+    host.upload()
+    dev.upload()
+    oh, lh = api.attn_fwd(q, k, v, host, w.scale)
+    od, ld = api.attn_fwd(q, k, v, dev, w.scale)
+    g = api.to_device_bf16(W.random_grad(np.random.default_rng(cfg), w.sq, w.hq, w.d))
+    gh = api.attn_bwd(q, k, v, oh, g, lh, host, w.scale)
+    gd = api.attn_bwd(q, k, v, od, g, ld, dev, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(oh.view(torch.int16), od.view(torch.int16)) and torch.equal(lh, ld)
+    for x, y in zip(gh, gd):
+        assert torch.equal(x, y)
+    host.close()
+    dev.close()
+
+
+def test_plan_from_device_csr_split_rows_and_ragged_tails():
+    """Few query rows against long keys (rows split into parts) and ragged extents."""
+    rng = np.random.default_rng(31)
+    for sq, sk, hq, hkv in ((100, 9000, 8, 2), (333, 1001, 4, 4)):
+        slices = W.random_slices(rng, sq, sk, 6) + [(0, sq, 0, sk, 1)]
+        host = api.Plan.from_slices(slices, sq, sk, hq, hkv, 128)
+        dc = api.DeviceCsr(slices, sq, sk)
+        dev = dc.plan(hq, hkv, 128)
+        dc.close()
+        _same_plan(host, dev, f"sq={sq} sk={sk}")
+        host.close()
+        dev.close()
