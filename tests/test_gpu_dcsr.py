@@ -133,14 +133,28 @@ def test_plan_from_device_csr_equals_host_plan(cfg):
 
 
 def test_plan_from_device_csr_split_rows_and_ragged_tails():
-    """Few query rows against long keys (rows split into parts) and ragged extents."""
+    """Few query rows against long keys (rows split into parts), ragged extents, head
+    dim 64 and 64-key plan tiles; the forward on the device CSR's plan equals the host
+    plan's bit for bit."""
+    import torch
     rng = np.random.default_rng(31)
-    for sq, sk, hq, hkv in ((100, 9000, 8, 2), (333, 1001, 4, 4)):
+    for sq, sk, hq, hkv, d, bk in ((100, 9000, 8, 2, 128, 128), (333, 1001, 4, 4, 64, 128),
+                                   (517, 700, 6, 2, 128, 64)):
+        say(f"plan from device CSR: sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} bk={bk}")
         slices = W.random_slices(rng, sq, sk, 6) + [(0, sq, 0, sk, 1)]
-        host = api.Plan.from_slices(slices, sq, sk, hq, hkv, 128)
-        dc = api.DeviceCsr(slices, sq, sk)
-        dev = dc.plan(hq, hkv, 128)
+        host = api.Plan.from_slices(slices, sq, sk, hq, hkv, d, bk=bk)
+        dc = api.DeviceCsr(slices, sq, sk, bk=bk)
+        with pytest.raises(api.BsfaError):
+            dc.plan(hq + 1, hkv + 1, d) if (hq + 1) % (hkv + 1) else dc.plan(hq, hkv + 1, d)
+        dev = dc.plan(hq, hkv, d)
         dc.close()
         _same_plan(host, dev, f"sq={sq} sk={sk}")
+        qb, kb, vb = W.random_inputs(rng, sq, sk, hq, hkv, d)
+        q, k, v = api.to_device_bf16(qb), api.to_device_bf16(kb), api.to_device_bf16(vb)
+        oh, lh = api.attn_fwd(q, k, v, host.upload(), 0.1)
+        od, ld = api.attn_fwd(q, k, v, dev.upload(), 0.1)
+        torch.cuda.synchronize()
+        assert torch.equal(oh.view(torch.int16), od.view(torch.int16))
+        assert torch.equal(lh.nan_to_num(neginf=-1e30), ld.nan_to_num(neginf=-1e30))
         host.close()
         dev.close()
