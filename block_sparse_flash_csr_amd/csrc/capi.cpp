@@ -6,6 +6,7 @@
 #include <cstring>
 #include <atomic>
 #include <mutex>
+#include <thread>
 #include <new>
 #include <vector>
 
@@ -31,6 +32,39 @@ bsfa_status check_slices(const bsfa_slice *s, int32_t n, int32_t sq, int32_t sk)
     return BSFA_OK;
 }
 
+// Column view and schedule of a compiled plan.  They read the same CSR and write
+// disjoint fields, so a large plan builds them on two threads (each is a few passes over
+// the entries: tens of milliseconds at millions of tiles); a small one, or a host where
+// no thread can be started, builds them one after the other.
+bsfa_status finish_plan(bsfa_plan &p)
+{
+    constexpr size_t kThreadedNnz = (size_t)1 << 20;
+    std::thread tr;
+    bool tr_oom = false;
+    if (p.col.size() >= kThreadedNnz) {
+        try {
+            tr = std::thread([&p, &tr_oom] {
+                try {
+                    build_transpose(p);
+                } catch (const std::bad_alloc &) {
+                    tr_oom = true;
+                }
+            });
+        } catch (const std::exception &) {
+            // no thread: build the column view below
+        }
+    }
+    bool oom = false;
+    try {
+        if (!tr.joinable()) build_transpose(p);
+        build_schedule(p, kNumCu * kBinsPerCu);
+    } catch (const std::bad_alloc &) {
+        oom = true;
+    }
+    if (tr.joinable()) tr.join();
+    return oom || tr_oom ? BSFA_ERR_OOM : BSFA_OK;
+}
+
 bsfa_status build_plan(const bsfa_slice *slices, int32_t n_slices, int32_t sq, int32_t sk,
                        int32_t hq, int32_t hkv, int32_t d, int32_t bq, int32_t bk, bsfa_plan **out)
 {
@@ -53,14 +87,7 @@ bsfa_status build_plan(const bsfa_slice *slices, int32_t n_slices, int32_t sq, i
     p->bq = bq;
     p->bk = bk;
     st = compile_mask(slices, n_slices, *p);
-    if (st == BSFA_OK) {
-        try {
-            build_transpose(*p);
-            build_schedule(*p, kNumCu * kBinsPerCu);
-        } catch (const std::bad_alloc &) {
-            st = BSFA_ERR_OOM;
-        }
-    }
+    if (st == BSFA_OK) st = finish_plan(*p);
     if (st != BSFA_OK) {
         delete p;
         return st;
@@ -1000,12 +1027,10 @@ bsfa_status bsfa_plan_from_dcsr(bsfa_dcsr *csr, int32_t hq, int32_t hkv, int32_t
     p->n_full = v.n_full;
     p->n_partial = v.n_partial;
     p->pairs = v.pairs;
-    try {
-        build_transpose(*p);
-        build_schedule(*p, kNumCu * kBinsPerCu);
-    } catch (const std::bad_alloc &) {
+    st = finish_plan(*p);
+    if (st != BSFA_OK) {
         delete p;
-        return BSFA_ERR_OOM;
+        return st;
     }
     *out = p;
     return BSFA_OK;
