@@ -465,7 +465,14 @@ def cpu_baseline(w, info, target_s):
     pairs = info["pairs"] * n_heads
     tflops = 4.0 * w.d * pairs / dt * 1e-12
     what = "the whole workload" if n_heads == w.hq else f"{n_heads} of {w.hq} heads"
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": tflops, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "host_cpu": model, "host_cpu_count": os.cpu_count(),
             "sample": f"{what}: {len(rows)} (head, row) outputs, {pairs} unmasked pairs, "
                       f"{dt:.1f} s wall on {threads} threads"}
 
