@@ -158,3 +158,23 @@ def test_plan_from_device_csr_split_rows_and_ragged_tails():
         assert torch.equal(lh.nan_to_num(neginf=-1e30), ld.nan_to_num(neginf=-1e30))
         host.close()
         dev.close()
+
+
+def test_plan_from_device_csr_of_an_empty_mask():
+    """No slice at all: the plan has no tiles, every row gets O = 0 and LSE = -inf."""
+    import torch
+    sq, sk, hq, hkv, d = 300, 200, 2, 1, 128
+    dc = api.DeviceCsr([], sq, sk)
+    dev = dc.plan(hq, hkv, d)
+    dc.close()
+    host = api.Plan.from_slices([], sq, sk, hq, hkv, d)
+    _same_plan(host, dev, "empty mask")
+    assert dev.info()["nnz"] == 0
+    rng = np.random.default_rng(5)
+    qb, kb, vb = W.random_inputs(rng, sq, sk, hq, hkv, d)
+    o, lse = api.attn_fwd(api.to_device_bf16(qb), api.to_device_bf16(kb), api.to_device_bf16(vb),
+                          dev.upload(), 0.1)
+    torch.cuda.synchronize()
+    assert bool((o.float() == 0).all()) and bool(torch.isneginf(lse).all())
+    host.close()
+    dev.close()
