@@ -336,3 +336,56 @@ def test_split_rows_full(seed, sq, sk, hq, hkv, d, kind):
     say(f"split rows {kind}: units={inf['n_units']} splits={inf['n_splits']}")
     plan.close()
     full_check(qb, kb, vb, slices, 1.0 / np.sqrt(d), f"split rows {kind}")
+
+
+def test_plans_from_several_host_threads():
+    """Four host threads build, upload, launch and destroy plans at the same time, each on
+    its own stream (the plan pools, the staging images and the copy ordering are shared
+    by all of them); every output equals the single-threaded reference bit for bit."""
+    import threading
+    import torch
+    sq = sk = 384
+    d = 128
+    rng = np.random.default_rng(29)
+    qb, kb, vb = W.random_inputs(rng, sq, sk, 2, 2, d)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    masks = [[(0, sq, 0, sk, 1)], W.random_slices(rng, sq, sk, 5), W.random_slices(rng, sq, sk, 9)]
+    ref = []
+    for m in masks:
+        p = api.Plan.from_slices(m, sq, sk, 2, 2, d).upload()
+        o, l = api.attn_fwd(q, k, v, p, 0.09)
+        torch.cuda.synchronize()
+        ref.append((o.clone(), l.clone()))
+        p.close()
+    n_threads, n_iter = 4, 12
+    outs = [[(torch.empty((sq, 2, d), dtype=torch.bfloat16, device="cuda"),
+              torch.empty((2, sq), dtype=torch.float32, device="cuda")) for _ in range(n_iter)]
+            for _ in range(n_threads)]
+    streams = [torch.cuda.Stream() for _ in range(n_threads)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(t):
+        try:
+            torch.cuda.set_device(0)
+            s = streams[t]
+            for i in range(n_iter):
+                m = (t + i) % 3
+                p = api.Plan.from_slices(masks[m], sq, sk, 2, 2, d).upload(s)
+                api.attn_fwd(q, k, v, p, 0.09, out=outs[t][i][0], lse=outs[t][i][1], stream=s)
+                p.close()
+        except Exception as e:   # reported below, in the test's own thread
+            errors.append(repr(e))
+
+    say(f"plans from {n_threads} host threads x {n_iter}")
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(n_threads)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t in range(n_threads):
+        for i in range(n_iter):
+            m = (t + i) % 3
+            assert torch.equal(outs[t][i][0], ref[m][0]) and torch.equal(outs[t][i][1], ref[m][1]), (t, i)
