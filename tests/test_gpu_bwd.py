@@ -231,3 +231,20 @@ def test_config4_bwd_rows_and_identity():
     assert err <= GRAD_TOL * max(1.0, mag)
     check_dv_sum_identity(w, gb, lse, dv, "config4 backward")
     plan.close()
+
+
+def test_bwd_on_a_plan_with_split_rows():
+    """Few queries against long keys: the forward splits every row into parts (merged by
+    its second kernel); the backward runs over whole CSR rows and columns regardless."""
+    sq, sk, hq, hkv, d = 200, 9000, 4, 2, 128
+    rng = np.random.default_rng(43)
+    slices = [(0, sq, 0, sk, 1)] + W.random_slices(rng, sq, sk, 3)
+    qb, kb, vb = W.random_inputs(rng, sq, sk, hq, hkv, d)
+    plan = api.Plan.from_slices(slices, sq, sk, hq, hkv, d)
+    assert plan.info()["n_splits"] > 0
+    plan.upload()
+    gb = W.random_grad(np.random.default_rng(44), sq, hq, d)
+    say(f"bwd on a split plan: sq={sq} sk={sk} splits={plan.info()['n_splits']}")
+    got = run_bwd(qb, kb, vb, gb, slices, 0.088, plan=plan)
+    plan.close()
+    check_grads(got, oracle.attn_bwd(qb, kb, vb, gb, slices, 0.088), "bwd split plan")
