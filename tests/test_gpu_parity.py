@@ -389,3 +389,13 @@ def test_plans_from_several_host_threads():
         for i in range(n_iter):
             m = (t + i) % 3
             assert torch.equal(outs[t][i][0], ref[m][0]) and torch.equal(outs[t][i][1], ref[m][1]), (t, i)
+
+
+@pytest.mark.parametrize("bk", [192, 256])
+def test_wide_key_tile_plans(bk):
+    """Plans with key tiles of 192 and 256 keys (3 and 4 kernel steps per CSR entry)."""
+    rng = np.random.default_rng(bk)
+    sq, sk = 517, 1100
+    slices = W.random_slices(rng, sq, sk, 6) + [(0, sq, 0, sk, 1)]
+    qb, kb, vb = W.random_inputs(rng, sq, sk, 4, 2, 128)
+    full_check(qb, kb, vb, slices, 1.0 / np.sqrt(128), f"plan bk={bk}", bk=bk)
