@@ -561,7 +561,8 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
                           const bsfa_plan *p, float scale, bsfa_tensor *o, float *lse,
                           int64_t lse_stride_head, void *stream)
 {
-    if (!q || !k || !v || !p || !o || !lse) return BSFA_ERR_ARG;
+    if (!q || !k || !v || !p || !o) return BSFA_ERR_ARG;
+    if (!lse && p->sq > 0) return BSFA_ERR_ARG;   // no query: nothing is written
     if (!(scale > 0.f) || !std::isfinite(scale)) return BSFA_ERR_ARG;
     if (p->d != 64 && p->d != 128) return BSFA_ERR_UNSUPPORTED;
     if (p->bq != kKernelBq || p->bk % kKernelBk != 0) return BSFA_ERR_UNSUPPORTED;
@@ -649,7 +650,8 @@ bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
                           int64_t lse_stride_head, const bsfa_plan *p, float scale, float *dq, float *dk,
                           float *dv, float *delta, void *stream)
 {
-    if (!q || !k || !v || !o || !dout || !p || !lse || !delta) return BSFA_ERR_ARG;
+    if (!q || !k || !v || !o || !dout || !p) return BSFA_ERR_ARG;
+    if (p->sq > 0 && (!lse || !delta)) return BSFA_ERR_ARG;   // no query: neither is read
     if (!(scale > 0.f) || !std::isfinite(scale)) return BSFA_ERR_ARG;
     if (p->d != 64 && p->d != 128) return BSFA_ERR_UNSUPPORTED;
     if (p->bq != kKernelBq || p->bk != 2 * kKernelBk) return BSFA_ERR_UNSUPPORTED;
@@ -728,10 +730,12 @@ bsfa_status bsfa_attn_merge(const void *const *o_parts, const float *const *lse_
                             int64_t lse_stride_head, int32_t n_tok, int32_t n_head, int32_t d,
                             bsfa_tensor *o, float *lse, void *stream)
 {
-    if (!o_parts || !lse_parts || !o || !lse) return BSFA_ERR_ARG;
+    if (!o_parts || !lse_parts || !o) return BSFA_ERR_ARG;
     if (n < 1 || n > BSFA_MERGE_MAX_PARTS || n_tok < 0 || n_head < 0 || n_head > 65535)
         return BSFA_ERR_ARG;
     if (d != 64 && d != 128) return BSFA_ERR_UNSUPPORTED;
+    if (n_tok == 0 || n_head == 0) return BSFA_OK;   // nothing to merge; pointers may be NULL
+    if (!lse) return BSFA_ERR_ARG;
     // one workgroup per (16 tokens, head) at d 128 (32 at d 64) in a 1-D grid
     if (((int64_t)n_tok + 15) / 16 * n_head >= INT32_MAX) return BSFA_ERR_UNSUPPORTED;
     if (lse_stride_head < n_tok) return BSFA_ERR_ARG;

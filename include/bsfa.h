@@ -193,7 +193,8 @@ double bsfa_lpt_assign(const float *cost, int32_t n_items, int32_t n_bins, int32
  * row i, for every query row i < sq and query head h; LSE[h * lse_stride_head + i] =
  * natural log-sum-exp of the scaled scores.  A row with no admitted key gets O = 0
  * and LSE = -inf.  Query head h reads key/value head h / (hq / hkv).
- * q, o: [sq, hq, d]; k, v: [sk, hkv, d]; lse: fp32, lse_stride_head >= sq.
+ * q, o: [sq, hq, d]; k, v: [sk, hkv, d]; lse: fp32, lse_stride_head >= sq.  Pointers of
+ * empty extents may be NULL (sq == 0: q, o, lse; sk == 0: k, v).
  * Shapes come from the plan, which must be uploaded to the current device.
  * No allocation, no synchronisation; deterministic (no atomics).  The stream is
  * remembered so that bsfa_plan_destroy releases the plan's buffer behind it.
@@ -217,7 +218,8 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
  * lse: the forward's fp32 LSE [hq, lse_stride_head].  dq [sq, hq, d], dk and dv
  * [sk, hkv, d]: fp32, contiguous, 16-byte aligned, fully written (rows no key reaches
  * get zeros).  delta: caller scratch of LSE's shape (fp32 [hq, lse_stride_head]),
- * overwritten with D.  The plan must have bq = 128 and bk = 128 and be uploaded to the
+ * overwritten with D.  With sq == 0, q, o, dout, lse, delta and dq may be NULL; with
+ * sk == 0, k, v, dk and dv.  The plan must have bq = 128 and bk = 128 and be uploaded to the
  * current device.  Two kernels on stream: dQ by query tile (which also computes and
  * stores D), then dK/dV by key tile over the query heads of its key/value head (no
  * atomics, deterministic).  No allocation, no synchronisation.
@@ -236,7 +238,8 @@ bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
  * [n_tok, n_head, d] tensor with the strides of o_parts_view, every LSE_t an fp32
  * [n_head, lse_stride_head] array.  o (bf16, strides from o->stride_*) and lse receive
  * the result and must not overlap any partial.  1 <= n <= BSFA_MERGE_MAX_PARTS,
- * d in {64, 128}, ceil(n_tok / 16) * n_head < 2^31.  Partials and result are streamed
+ * d in {64, 128}, ceil(n_tok / 16) * n_head < 2^31.  With n_tok == 0 or n_head == 0 the
+ * call does nothing and returns BSFA_OK (its pointers may then be NULL).  Partials and result are streamed
  * with non-temporal accesses (they bypass the caches' retention).
  * Errors: BSFA_ERR_ARG, BSFA_ERR_ALIGN, BSFA_ERR_UNSUPPORTED, BSFA_ERR_HIP. */
 enum { BSFA_MERGE_MAX_PARTS = 16 };

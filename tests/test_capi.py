@@ -125,6 +125,11 @@ def test_merge_rejects_bad_arguments():
                                ctypes.c_void_p(16), None) == 3
     assert lib.bsfa_attn_merge(ptrs, lptr, 2, 1024, 128, 10, 64, 8, 128, ctypes.byref(t),
                                ctypes.c_void_p(16), None) == 1
+    # nothing to merge: no pointer is read, the call succeeds (still checking d)
+    empty = api.Tensor(ctypes.c_void_p(None), 1024, 128)
+    nulls = (ctypes.c_void_p * 2)(None, None)
+    assert lib.bsfa_attn_merge(nulls, nulls, 2, 1024, 128, 0, 0, 8, 128, ctypes.byref(empty), None, None) == 0
+    assert lib.bsfa_attn_merge(nulls, nulls, 2, 1024, 128, 0, 0, 8, 96, ctypes.byref(empty), None, None) == 4
 
 
 def test_backward_rejects_bad_arguments():

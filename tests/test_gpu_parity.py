@@ -399,3 +399,43 @@ def test_wide_key_tile_plans(bk):
     slices = W.random_slices(rng, sq, sk, 6) + [(0, sq, 0, sk, 1)]
     qb, kb, vb = W.random_inputs(rng, sq, sk, 4, 2, 128)
     full_check(qb, kb, vb, slices, 1.0 / np.sqrt(128), f"plan bk={bk}", bk=bk)
+
+
+def test_zero_length_extents():
+    """No keys at all (every row gets O = 0, LSE = -inf) and no queries (nothing to do)."""
+    import torch
+    d = 128
+    rng = np.random.default_rng(61)
+    qb, _, _ = W.random_inputs(rng, 100, 1, 2, 1, d)
+    q = dev_bf16(qb)
+    k = torch.empty((0, 1, d), dtype=torch.bfloat16, device="cuda")
+    plan = api.Plan.from_slices([], 100, 0, 2, 1, d).upload()
+    o = torch.full((100, 2, d), 3.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((2, 100), dtype=torch.float32, device="cuda")
+    api.attn_fwd(q, k, k, plan, 0.1, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((o.float() == 0).all()) and bool(torch.isneginf(lse).all())
+    plan.close()
+    q0 = torch.empty((0, 2, d), dtype=torch.bfloat16, device="cuda")
+    kv = dev_bf16(W.random_inputs(rng, 1, 50, 2, 1, d)[1])
+    plan = api.Plan.from_slices([], 0, 50, 2, 1, d).upload()
+    o0, l0 = api.attn_fwd(q0, kv, kv, plan, 0.1)
+    torch.cuda.synchronize()
+    assert o0.numel() == 0
+    # backward without queries: every key's gradient is zero
+    dq, dk, dv = api.attn_bwd(q0, kv, kv, o0, q0, l0, plan, 0.1)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and bool((dk == 0).all()) and bool((dv == 0).all())
+    plan.close()
+    # backward without keys: dQ is zero
+    plan = api.Plan.from_slices([], 100, 0, 2, 1, d).upload()
+    g = dev_bf16(W.random_grad(rng, 100, 2, d))
+    dq, dk, dv = api.attn_bwd(q, k, k, o, g, lse, plan, 0.1)
+    torch.cuda.synchronize()
+    assert bool((dq == 0).all()) and dk.numel() == 0 and dv.numel() == 0
+    plan.close()
+    # merge of empty partials
+    e = torch.empty((0, 2, d), dtype=torch.bfloat16, device="cuda")
+    le = torch.empty((2, 0), dtype=torch.float32, device="cuda")
+    om, lm = api.attn_merge([e, e], [le, le])
+    assert om.numel() == 0 and lm.numel() == 0
