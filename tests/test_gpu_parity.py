@@ -439,3 +439,21 @@ def test_zero_length_extents():
     le = torch.empty((2, 0), dtype=torch.float32, device="cuda")
     om, lm = api.attn_merge([e, e], [le, le])
     assert om.numel() == 0 and lm.numel() == 0
+
+
+def test_block_code_plan_with_ragged_blocks():
+    """A plan from a block code map (blocks of 48 x 40, clipped at ragged extents, codes
+    empty / full / causal drawn at random) against the oracle on the equivalent slices."""
+    import torch
+    sq, sk, hq, hkv, d = 517, 389, 4, 2, 128
+    rng = np.random.default_rng(47)
+    nbq, nbk = -(-sq // 48), -(-sk // 40)
+    codes = rng.integers(0, 3, size=(nbq, nbk)).astype(np.uint8)
+    qb, kb, vb = W.random_inputs(rng, sq, sk, hq, hkv, d)
+    plan = api.Plan.from_blocks(codes, 48, 40, sq, sk, hq, hkv, d).upload()
+    say(f"block code plan: {nbq} x {nbk} blocks of 48 x 40, sq={sq} sk={sk}")
+    o, lse = api.attn_fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), plan, 0.1)
+    torch.cuda.synchronize()
+    plan.close()
+    o_ref, lse_ref = oracle.attn_fwd(qb, kb, vb, W.block_slices(codes, 48, 40, sq, sk), 0.1)
+    compare(W.bf16_to_f32(host_bits(o)), lse.cpu().numpy().T, o_ref, lse_ref.T, "block code plan")
