@@ -457,3 +457,24 @@ def test_block_code_plan_with_ragged_blocks():
     plan.close()
     o_ref, lse_ref = oracle.attn_fwd(qb, kb, vb, W.block_slices(codes, 48, 40, sq, sk), 0.1)
     compare(W.bf16_to_f32(host_bits(o)), lse.cpu().numpy().T, o_ref, lse_ref.T, "block code plan")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_plans_with_empty_and_tiny_documents(causal):
+    """Varlen plans, causal and full within documents, including an empty document and
+    one-token documents, against the oracle on the equivalent slices."""
+    import torch
+    lengths = [0, 1, 130, 1, 257, 0, 64, 300]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    s, hq, hkv, d = int(cu[-1]), 4, 2, 128
+    rng = np.random.default_rng(53 + causal)
+    qb, kb, vb = W.random_inputs(rng, s, s, hq, hkv, d)
+    plan = api.Plan.from_varlen(cu, hq, hkv, d, causal=causal).upload()
+    say(f"varlen plan causal={causal}: documents {lengths}")
+    o, lse = api.attn_fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), plan, 0.1)
+    torch.cuda.synchronize()
+    plan.close()
+    slices = [(int(cu[t]), int(cu[t + 1]), int(cu[t]), int(cu[t + 1]), 1 if causal else 0)
+              for t in range(len(lengths)) if lengths[t] > 0]
+    o_ref, lse_ref = oracle.attn_fwd(qb, kb, vb, slices, 0.1)
+    compare(W.bf16_to_f32(host_bits(o)), lse.cpu().numpy().T, o_ref, lse_ref.T, f"varlen causal={causal}")
