@@ -109,15 +109,19 @@ size_t place(size_t &off, size_t count)
     return at;
 }
 
-// Pinned host images of plan metadata, reused across uploads.  An image is busy
-// from its upload until the copy recorded behind it has run; uploads never wait for
-// it, they take another image (or pin a new one).  Images live until process exit.
+// Pinned host images of plan metadata, reused across uploads.  An image is taken by
+// one caller from its acquisition until the copy recorded behind it has run: while
+// the caller fills it and enqueues the copy (`filling`) nobody else may look at its
+// event, which still belongs to an earlier copy; after that (`busy`) it is free again
+// once the event reports the copy done.  Uploads never wait for an image, they take
+// another one (or pin a new one).  Images live until process exit.
 struct Staging {
     void *host = nullptr;
     size_t cap = 0;
     int device = -1;
     hipEvent_t copied = nullptr;
     bool busy = false;
+    bool filling = false;
 };
 std::mutex g_staging_mu;
 std::vector<Staging *> g_staging;
@@ -126,9 +130,10 @@ bsfa_status staging_acquire(int dev, size_t bytes, Staging **out)
 {
     std::lock_guard<std::mutex> lk(g_staging_mu);
     for (Staging *st : g_staging) {
-        if (st->device != dev || st->cap < bytes) continue;
+        if (st->device != dev || st->cap < bytes || st->filling) continue;
         if (st->busy && hipEventQuery(st->copied) != hipSuccess) continue;
         st->busy = true;
+        st->filling = true;
         *out = st;
         return BSFA_OK;
     }
@@ -148,6 +153,7 @@ bsfa_status staging_acquire(int dev, size_t bytes, Staging **out)
     st->cap = cap;
     st->device = dev;
     st->busy = true;
+    st->filling = true;
     try {
         g_staging.push_back(st);
     } catch (const std::bad_alloc &) {
@@ -164,6 +170,15 @@ void staging_release_now(Staging *st)
 {
     std::lock_guard<std::mutex> lk(g_staging_mu);
     st->busy = false;
+    st->filling = false;
+}
+
+// The copy out of the image and its event are enqueued: from now on the event tells
+// when the image is free.
+void staging_in_flight(Staging *st)
+{
+    std::lock_guard<std::mutex> lk(g_staging_mu);
+    st->filling = false;
 }
 
 // One internal copy stream per device (default priority, non-blocking): metadata
@@ -427,8 +442,11 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     } catch (const std::bad_alloc &) {
         cs = nullptr;
     }
-    if (!cs || hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, cs) != hipSuccess ||
-        hipEventRecord(stg->copied, cs) != hipSuccess || hipEventRecord(slot->ready, cs) != hipSuccess) {
+    const bool copied = cs && hipMemcpyAsync(d, h, bytes, hipMemcpyHostToDevice, cs) == hipSuccess;
+    if (!copied || hipEventRecord(stg->copied, cs) != hipSuccess || hipEventRecord(slot->ready, cs) != hipSuccess) {
+        // an enqueued copy may still read the image: let it finish before the image is
+        // handed out again (error path only)
+        if (copied) (void)hipStreamSynchronize(cs);
         std::vector<hipStream_t> rel;
         if (cs) rel.push_back(cs);
         rel.push_back(s);
@@ -436,6 +454,7 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
         staging_release_now(stg);
         return BSFA_ERR_HIP;
     }
+    staging_in_flight(stg);
     uint8_t *base = (uint8_t *)d;
     p->dev.row_ptr = (const int32_t *)(base + o_row);
     p->dev.entries = (const Entry *)(base + o_ent);
@@ -910,9 +929,14 @@ bsfa_status bsfa_dcsr_build(const bsfa_slice *slices, int32_t n_slices, int32_t 
     c->pieces = (const int32_t *)a.pieces;
     c->totals_dev = a.totals;
     // the pinned image stays reserved until the copy recorded behind it has run
-    bool ok = hipMemcpyAsync(b, stg->host, image_bytes, hipMemcpyHostToDevice, s) == hipSuccess &&
-              hipEventRecord(stg->copied, s) == hipSuccess;
-    if (!ok) staging_release_now(stg);
+    const bool copied = hipMemcpyAsync(b, stg->host, image_bytes, hipMemcpyHostToDevice, s) == hipSuccess;
+    bool ok = copied && hipEventRecord(stg->copied, s) == hipSuccess;
+    if (ok) {
+        staging_in_flight(stg);
+    } else {
+        if (copied) (void)hipStreamSynchronize(s);   // error path: the copy may still read the image
+        staging_release_now(stg);
+    }
     ok = ok && launch_dcsr(a, s) == hipSuccess;
     ok = ok && hipEventRecord(c->done, s) == hipSuccess;
     if (!ok) {
