@@ -178,3 +178,49 @@ def test_plan_from_device_csr_of_an_empty_mask():
     assert bool((o.float() == 0).all()) and bool(torch.isneginf(lse).all())
     host.close()
     dev.close()
+
+
+def test_device_compiles_from_several_host_threads():
+    """Four host threads compile masks on the GPU at once (each on its own stream; the
+    pinned staging images are shared) and upload plans in between; every CSR equals the
+    host compiler's."""
+    import threading
+    import torch
+    rng = np.random.default_rng(59)
+    cases = []
+    for _ in range(6):
+        sq, sk = int(rng.integers(100, 900)), int(rng.integers(100, 900))
+        cases.append((W.random_slices(rng, sq, sk, int(rng.integers(1, 12))), sq, sk))
+    refs = []
+    for sl, sq, sk in cases:
+        p = api.Plan.from_slices(sl, sq, sk, 1, 1, 64)
+        refs.append(p.csr())
+        p.close()
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    errors = []
+
+    def worker(t):
+        try:
+            torch.cuda.set_device(0)
+            for i in range(12):
+                c = (t + i) % len(cases)
+                sl, sq, sk = cases[c]
+                dc = api.DeviceCsr(sl, sq, sk, stream=streams[t])
+                up = api.Plan.from_slices(sl, sq, sk, 2, 1, 128).upload(streams[t])   # shares the images
+                rp, col, tag, _, _ = dc.export()
+                dc.close()
+                up.close()
+                if not (np.array_equal(rp, refs[c][0]) and np.array_equal(col, refs[c][1])
+                        and np.array_equal(tag, refs[c][2])):
+                    errors.append(f"thread {t} iteration {i}: CSR of case {c} differs")
+        except Exception as e:   # reported below, in the test's own thread
+            errors.append(repr(e))
+
+    say("device compiles from 4 host threads x 12")
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
