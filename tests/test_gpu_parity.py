@@ -478,3 +478,40 @@ def test_varlen_plans_with_empty_and_tiny_documents(causal):
               for t in range(len(lengths)) if lengths[t] > 0]
     o_ref, lse_ref = oracle.attn_fwd(qb, kb, vb, slices, 0.1)
     compare(W.bf16_to_f32(host_bits(o)), lse.cpu().numpy().T, o_ref, lse_ref.T, f"varlen causal={causal}")
+
+
+def test_plan_churn_over_many_sizes():
+    """Plans of very different sizes (so pooled staging images and device buffers of
+    several capacities are taken, outgrown and reused) built, launched and destroyed
+    back to back on two streams with no synchronisation; every output equals the output
+    of the same plan run alone."""
+    import torch
+    rng = np.random.default_rng(67)
+    shapes = [(int(rng.integers(1, 4500)), int(rng.integers(1, 4500))) for _ in range(8)]
+    cases = []
+    for sq, sk in shapes:
+        sl = W.random_slices(rng, sq, sk, int(rng.integers(1, 9))) + [(0, sq, 0, sk, int(rng.integers(0, 2)))]
+        qb, kb, vb = W.random_inputs(rng, sq, sk, 2, 1, 128)
+        q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+        p = api.Plan.from_slices(sl, sq, sk, 2, 1, 128).upload()
+        o, l = api.attn_fwd(q, k, v, p, 0.1)
+        torch.cuda.synchronize()
+        p.close()
+        cases.append((sl, sq, sk, q, k, v, o.clone(), l.clone()))
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+    order = [int(x) for x in rng.integers(0, len(cases), 40)]
+    outs = []
+    say(f"plan churn over sizes {shapes}: 40 launches")
+    for n, c in enumerate(order):
+        sl, sq, sk, q, k, v, _, _ = cases[c]
+        s = streams[n % 2]
+        o = torch.empty((sq, 2, 128), dtype=torch.bfloat16, device="cuda")
+        l = torch.empty((2, sq), dtype=torch.float32, device="cuda")
+        s.wait_stream(torch.cuda.current_stream())   # the outputs were allocated on the current stream
+        p = api.Plan.from_slices(sl, sq, sk, 2, 1, 128).upload(s)
+        api.attn_fwd(q, k, v, p, 0.1, out=o, lse=l, stream=s)
+        p.close()
+        outs.append((c, o, l))
+    torch.cuda.synchronize()
+    for n, (c, o, l) in enumerate(outs):
+        assert torch.equal(o, cases[c][6]) and torch.equal(l, cases[c][7]), f"launch {n} (case {c}) differs"
