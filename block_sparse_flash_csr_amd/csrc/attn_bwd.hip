@@ -296,7 +296,12 @@ __device__ __forceinline__ void dq_step(char *__restrict__ kd, char *__restrict_
         s[b] = f32x16{};
         dp[b] = f32x16{};
     }
+    // The score products run at raised wave priority: the SIMD's other wave (of the other
+    // resident workgroup, at its own point of the step) then gets the matrix unit back
+    // while this wave exponentiates, instead of both waves contending for it in step.
+    __builtin_amdgcn_s_setprio(1);
     score_products<D, kAheadQ>(kt, vt, qf, gf, ad, s, dp);
+    __builtin_amdgcn_s_setprio(0);
     if (masked_step) mask_scores(m, s);
     f32x16 ds[2];
 #pragma unroll
