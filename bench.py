@@ -147,7 +147,7 @@ def event_times(fn, reps, stream):
 def headline(args, api, W):
     """Varlen causal workload: timed steps of plan build + upload + forward."""
     import torch
-    w = W.config2()
+    w = W.varlen_causal_t16384()
     q, k, v = api.to_device_bf16(w.q), api.to_device_bf16(w.k), api.to_device_bf16(w.v)
     stream = torch.cuda.current_stream()
     o = torch.empty((w.sq, w.hq, w.d), dtype=torch.bfloat16, device="cuda")
@@ -221,7 +221,7 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
     out = {}
     counters = measured_workload_counters()   # committed rocprofv3 summary (digest-checked)
     for cfg in (1, 3, 4):
-        w = W.CONFIGS[cfg]()
+        w = W.WORKLOADS[cfg]()
         q, k, v = api.to_device_bf16(w.q), api.to_device_bf16(w.k), api.to_device_bf16(w.v)
         plan = api.plan_from_workload(w, stream=stream)
         info = plan.info()
@@ -248,7 +248,7 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
     # Head dim 64 on the headline mask (not a reference workload): per admitted pair the
     # softmax's vector work is the same as at d = 128 and the matrix work half of it, so
     # this line shows how far the vector units bound the smaller head dim.
-    w = W.config2(with_inputs=False)
+    w = W.varlen_causal_t16384(with_inputs=False)
     hd = 64
     q, k, v = (W.device_normal_bf16((w.sq, w.hq, hd), s) for s in (641, 642, 643))
     plan = api.Plan.from_slices(w.slices, w.sq, w.sk, w.hq, w.hkv, hd).upload(stream)
@@ -272,7 +272,7 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
     # which also forms D = rowsum(dO*O)) and the dK/dV kernel (by key tile).  Algorithmic work is 5
     # products of 2*d flops per admitted pair (S, dP, dV, dK, dQ); the kernels execute 7
     # (S and dP are recomputed by both gradient kernels instead of using atomics).
-    w = W.config2()
+    w = W.varlen_causal_t16384()
     q, k, v = api.to_device_bf16(w.q), api.to_device_bf16(w.k), api.to_device_bf16(w.v)
     g = api.to_device_bf16(W.random_grad(np.random.default_rng(2002), w.sq, w.hq, w.d))
     plan = api.plan_from_workload(w, stream=stream)
@@ -302,7 +302,7 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
     # array in its C layout.
     mc = {}
     S = 524288
-    cases = [("varlen_causal_t16384_docs8", W.config2(with_inputs=False).slices, 16384),
+    cases = [("varlen_causal_t16384_docs8", W.varlen_causal_t16384(with_inputs=False).slices, 16384),
              ("causal_s524288", [(0, S, 0, S, 1)], S),
              ("strided_blocks_s524288", W.block_slices(W.strided_block_codes(S // 128, 8), 128, 128, S, S), S)]
     for name, sl, s_ in cases:
@@ -360,7 +360,7 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
     torch.cuda.empty_cache()
 
     # KV split: 8 partial forwards over 8192-token KV chunks, then the merge
-    w = W.config5()
+    w = W.kv_split_q8192()
     c, nc = w.extra["chunk"], w.extra["n_chunks"]
     q, k, v = api.to_device_bf16(w.q), api.to_device_bf16(w.k), api.to_device_bf16(w.v)
     plans = [api.Plan.from_slices(sl, c, c, w.hq, w.hkv, w.d).upload(stream)
@@ -417,7 +417,7 @@ def counter_pass(api, W):
     import torch
     stream = torch.cuda.current_stream()
     for cfg, reps in COUNTER_ORDER:
-        w = W.CONFIGS[cfg]()
+        w = W.WORKLOADS[cfg]()
         q, k, v = api.to_device_bf16(w.q), api.to_device_bf16(w.k), api.to_device_bf16(w.v)
         torch.cuda.synchronize()
         if cfg == 5:

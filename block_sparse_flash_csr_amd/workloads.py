@@ -134,7 +134,7 @@ def range_slice_mask(rng, s: int, n_frames: int, frame: int, n_seeded: int, qblk
 # The five workloads
 # ----------------------------------------------------------------------------
 
-def config1(with_inputs: bool = True) -> Workload:
+def causal_s256(with_inputs: bool = True) -> Workload:
     """Single-sequence causal: batch 1, 2 heads, S = 256, d = 64, scale 1/8 (seed 1)."""
     rng = np.random.default_rng(1)
     s, h, d = 256, 2, 64
@@ -144,7 +144,7 @@ def config1(with_inputs: bool = True) -> Workload:
     return w
 
 
-def config2(with_inputs: bool = True) -> Workload:
+def varlen_causal_t16384(with_inputs: bool = True) -> Workload:
     """Varlen causal: 16384 packed tokens, 8 documents U[512, 4096) rescaled, 16 heads, d 128."""
     rng = np.random.default_rng(2)
     total, h, d = 16384, 16, 128
@@ -157,7 +157,7 @@ def config2(with_inputs: bool = True) -> Workload:
     return w
 
 
-def config3(with_inputs: bool = True) -> Workload:
+def block_sparse_strided_s32768(with_inputs: bool = True) -> Workload:
     """Block-sparse strided: S = 32768, 128x128 blocks, column 0 + causal diagonal + every
     8th diagonal below it; 16 heads, d 128 (seed 3)."""
     rng = np.random.default_rng(3)
@@ -171,7 +171,7 @@ def config3(with_inputs: bool = True) -> Workload:
     return w
 
 
-def config4(with_inputs: bool = True) -> Workload:
+def range_slices_s65536(with_inputs: bool = True) -> Workload:
     """Range slices: S = 65536, 16 full 4096-token frames + 64 seeded slices; GQA 32/8, d 128."""
     rng = np.random.default_rng(4)
     s, hq, hkv, d = 65536, 32, 8, 128
@@ -182,7 +182,7 @@ def config4(with_inputs: bool = True) -> Workload:
     return w
 
 
-def config5(with_inputs: bool = True, q_chunk: int = 7) -> Workload:
+def kv_split_q8192(with_inputs: bool = True, q_chunk: int = 7) -> Workload:
     """KV-split share: a Q chunk of 8192 tokens at global chunk ``q_chunk`` against 8 KV
     chunks of 8192 tokens, causal over the 65536 global positions; 32 heads, d 128 (seed 5).
 
@@ -211,7 +211,7 @@ def config5(with_inputs: bool = True, q_chunk: int = 7) -> Workload:
     return w
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+WORKLOADS = {1: causal_s256, 2: varlen_causal_t16384, 3: block_sparse_strided_s32768, 4: range_slices_s65536, 5: kv_split_q8192}
 
 
 def random_slices(rng, sq: int, sk: int, n: int, allow_empty: bool = True) -> list:

@@ -65,7 +65,7 @@ def test_per_workload_counters_cover_every_reference_workload():
     if not c:                                  # withheld once the kernels changed
         return
     from block_sparse_flash_csr_amd import workloads as W
-    names = [W.CONFIGS[i](with_inputs=False).name for i in (1, 2, 3, 4, 5)]
+    names = [W.WORKLOADS[i](with_inputs=False).name for i in (1, 2, 3, 4, 5)]
     for name in names + [names[-1] + "_merge"]:
         assert name in c, name
         assert 0.0 <= c[name]["mfma_busy_pct"] <= 100.0

@@ -77,9 +77,9 @@ def full_check(qb, kb, vb, slices, scale, what, seed=0):
     return got, ref
 
 
-def test_config1_bwd():
-    w = W.config1()
-    full_check(w.q, w.k, w.v, w.slices, w.scale, "bwd config1 causal S=256 d=64")
+def test_causal_s256_bwd():
+    w = W.causal_s256()
+    full_check(w.q, w.k, w.v, w.slices, w.scale, "bwd causal S=256 d=64")
 
 
 @pytest.mark.parametrize("seed,sq,sk,hq,hkv,d,n", [
@@ -187,9 +187,9 @@ def check_dv_sum_identity(w, gb, lse, dv, what):
     say(f"{what}: sum_j dV identity holds, worst error {worst:.3f} of the bound")
 
 
-def test_config2_bwd_sampled():
+def test_varlen_causal_t16384_bwd_sampled():
     import torch
-    w = W.config2()
+    w = W.varlen_causal_t16384()
     plan = api.plan_from_workload(w)
     gb, lse, dq, dk, dv = full_size_run(w, plan, 2002)
     cu = [int(x) for x in w.cu_seqlens]
@@ -201,23 +201,23 @@ def test_config2_bwd_sampled():
     kj = sorted(set([c - 1 for c in cu[1:]] + short + [c + 5 for c in short]
                     + [int(x) for x in rng.integers(0, w.sk, 4)]))
     keys = [(int(rng.integers(0, w.hkv)), j) for j in kj]
-    say(f"config2 backward: oracle on {len(rows)} rows and {len(keys)} keys")
+    say(f"varlen causal t16384 backward: oracle on {len(rows)} rows and {len(keys)} keys")
     rq, rk, rv = oracle.attn_bwd_sampled(w.q, w.k, w.v, gb, w.slices, w.scale, rows=rows, keys=keys)
     r = np.array(rows, np.int64)
     gq = dq[torch.from_numpy(r[:, 1]).cuda(), torch.from_numpy(r[:, 0]).cuda()].cpu().numpy()
     kk = np.array(keys, np.int64)
     ki, kg = torch.from_numpy(kk[:, 1]).cuda(), torch.from_numpy(kk[:, 0]).cuda()
     gk, gv = dk[ki, kg].cpu().numpy(), dv[ki, kg].cpu().numpy()
-    check_grads((gq, gk, gv), (rq, rk, rv), "config2 backward sampled")
-    check_dv_sum_identity(w, gb, lse, dv, "config2 backward")
+    check_grads((gq, gk, gv), (rq, rk, rv), "varlen causal t16384 backward sampled")
+    check_dv_sum_identity(w, gb, lse, dv, "varlen causal t16384 backward")
     plan.close()
 
 
-def test_config4_bwd_rows_and_identity():
+def test_range_slices_s65536_bwd_rows_and_identity():
     """GQA 32/8 at 65536 tokens: sampled dQ rows and the dV identity on every kv head
     (a sampled key there would cost the oracle tens of seconds)."""
     import torch
-    w = W.config4()
+    w = W.range_slices_s65536()
     plan = api.plan_from_workload(w)
     gb, lse, dq, dk, dv = full_size_run(w, plan, 2004)
     extra = [s[0] for s in w.slices[16:30]] + [s[1] - 1 for s in w.slices[16:30]]
@@ -227,9 +227,9 @@ def test_config4_bwd_rows_and_identity():
     gq = dq[torch.from_numpy(r[:, 1]).cuda(), torch.from_numpy(r[:, 0]).cuda()].cpu().numpy()
     err = float(np.max(np.abs(gq - rq)))
     mag = float(np.max(np.abs(rq)))
-    say(f"config4 backward sampled: max|ddQ| = {err:.3e} (max|ref| {mag:.2e})")
+    say(f"range slices s65536 backward sampled: max|ddQ| = {err:.3e} (max|ref| {mag:.2e})")
     assert err <= GRAD_TOL * max(1.0, mag)
-    check_dv_sum_identity(w, gb, lse, dv, "config4 backward")
+    check_dv_sum_identity(w, gb, lse, dv, "range slices s65536 backward")
     plan.close()
 
 

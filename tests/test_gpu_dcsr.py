@@ -47,17 +47,17 @@ def check(slices, sq, sk, bq, bk, what, with_oracle=True):
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_workloads(cfg):
-    w = W.CONFIGS[cfg](with_inputs=False)
+    w = W.WORKLOADS[cfg](with_inputs=False)
     v = check(w.slices, w.sq, w.sk, 128, 128, w.name)
     say(f"{w.name}: nnz {v['nnz']} ({v['n_full']} F + {v['n_partial']} P), {v['touches']} touches")
 
 
 def test_workload5_chunks_and_unsplit():
-    w = W.config5(with_inputs=False)
+    w = W.kv_split_q8192(with_inputs=False)
     c = w.extra["chunk"]
     for sl in w.extra["chunk_slices"]:
-        check(sl, c, c, 128, 128, "config5 chunk")
-    check(w.slices, w.sq, w.sk, 128, 128, "config5 unsplit")
+        check(sl, c, c, 128, 128, "kv split q8192 chunk")
+    check(w.slices, w.sq, w.sk, 128, 128, "kv split q8192 unsplit")
 
 
 @pytest.mark.parametrize("bq,bk", [(16, 16), (16, 32), (32, 16), (64, 128), (128, 128), (128, 64),
@@ -109,7 +109,7 @@ def test_plan_from_device_csr_equals_host_plan(cfg):
     """A plan over the device-compiled CSR is the host plan: CSR, pieces, schedule and
     units equal, and the forward and backward outputs bit-identical."""
     import torch
-    w = W.CONFIGS[cfg]()
+    w = W.WORKLOADS[cfg]()
     say(f"plan from device CSR: {w.name}")
     host = api.Plan.from_slices(w.slices, w.sq, w.sk, w.hq, w.hkv, w.d)
     dc = api.DeviceCsr(w.slices, w.sq, w.sk)

@@ -49,9 +49,9 @@ def full_check(qb, kb, vb, slices, scale, what, bk=128):
 # ---------------------------------------------------------------------------
 # element-by-element at sizes the oracle finishes in seconds
 # ---------------------------------------------------------------------------
-def test_config1_full():
-    w = W.config1()
-    full_check(w.q, w.k, w.v, w.slices, w.scale, "config1 causal S=256 d=64")
+def test_causal_s256_full():
+    w = W.causal_s256()
+    full_check(w.q, w.k, w.v, w.slices, w.scale, "causal S=256 d=64")
 
 
 @pytest.mark.parametrize("seed,sq,sk,hq,hkv,d,n", [
@@ -157,37 +157,37 @@ def sampled_check(w, plan, rows, what):
     return o, lse
 
 
-def test_config2_sampled():
-    w = W.config2()
+def test_varlen_causal_t16384_sampled():
+    w = W.varlen_causal_t16384()
     plan = api.plan_from_workload(w)
     cu = w.cu_seqlens
     extra = list(cu[:-1]) + list(cu[:-1] + 1) + list(cu[1:] - 1) + list(cu[1:] - 2)
-    sampled_check(w, plan, sample_rows(w, 256, 2, extra), "config2 varlen causal")
+    sampled_check(w, plan, sample_rows(w, 256, 2, extra), "varlen causal t16384")
 
 
-def test_config3_sampled():
-    w = W.config3()
+def test_block_sparse_strided_s32768_sampled():
+    w = W.block_sparse_strided_s32768()
     plan = api.plan_from_workload(w)
     extra = [128 * 8 * t + o for t in range(0, 32, 5) for o in (0, 1, 127)]
-    sampled_check(w, plan, sample_rows(w, 256, 3, extra), "config3 block-sparse strided")
+    sampled_check(w, plan, sample_rows(w, 256, 3, extra), "block-sparse strided s32768")
 
 
-def test_config4_sampled():
-    w = W.config4()
+def test_range_slices_s65536_sampled():
+    w = W.range_slices_s65536()
     plan = api.plan_from_workload(w)
     extra = [s[0] for s in w.slices[16:40]] + [s[1] - 1 for s in w.slices[16:40]]
-    sampled_check(w, plan, sample_rows(w, 256, 4, extra), "config4 range slices GQA")
+    sampled_check(w, plan, sample_rows(w, 256, 4, extra), "range slices s65536 GQA")
 
 
 @pytest.mark.parametrize("q_chunk", [7, 3])
-def test_config5_split_merge_sampled(q_chunk):
+def test_kv_split_q8192_split_merge_sampled(q_chunk):
     import torch
-    w = W.config5(q_chunk=q_chunk)
+    w = W.kv_split_q8192(q_chunk=q_chunk)
     c, nc = w.extra["chunk"], w.extra["n_chunks"]
     q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
     plans = [api.Plan.from_slices(sl, c, c, w.hq, w.hkv, w.d).upload()
              for sl in w.extra["chunk_slices"]]
-    say(f"config5 q_chunk={q_chunk}: 8 partial forwards + merge")
+    say(f"kv split q8192 q_chunk={q_chunk}: 8 partial forwards + merge")
     parts = [api.attn_fwd(q, k[t * c:(t + 1) * c], v[t * c:(t + 1) * c], plans[t], w.scale)
              for t in range(nc)]
     o, lse = api.attn_merge([p[0] for p in parts], [p[1] for p in parts])
@@ -199,7 +199,7 @@ def test_config5_split_merge_sampled(q_chunk):
     o_s = W.bf16_to_f32(host_bits(o[is_, hs]))
     l_s = lse[hs, is_].cpu().numpy()
     o_ref, lse_ref = oracle.attn_fwd(w.q, w.k, w.v, w.slices, w.scale, rows=rows)
-    compare(o_s, l_s, o_ref, lse_ref, f"config5 split+merge q_chunk={q_chunk}")
+    compare(o_s, l_s, o_ref, lse_ref, f"kv split q8192 split+merge q_chunk={q_chunk}")
     for p in plans:
         p.close()
 

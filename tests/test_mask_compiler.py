@@ -19,7 +19,7 @@ def _compare(plan, slices, sq, sk, bq, bk):
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_workload_csr_bit_exact(cfg):
-    w = W.CONFIGS[cfg](with_inputs=False)
+    w = W.WORKLOADS[cfg](with_inputs=False)
     plan = api.plan_from_workload(w, upload=False)
     _compare(plan, w.slices, w.sq, w.sk, 128, 128)
     # the slice form of the same mask compiles to the same CSR
@@ -30,7 +30,7 @@ def test_workload_csr_bit_exact(cfg):
 
 
 def test_workload5_chunks_bit_exact():
-    w = W.config5(with_inputs=False)
+    w = W.kv_split_q8192(with_inputs=False)
     c = w.extra["chunk"]
     for sl in w.extra["chunk_slices"]:
         plan = api.Plan.from_slices(sl, c, c, w.hq, w.hkv, w.d)
@@ -43,7 +43,7 @@ def test_workload5_chunks_bit_exact():
 def test_workload_tile_counts():
     expect = {1: (1, 2), 2: (1135, 358), 3: (4192, 256), 4: (52496, 736)}
     for cfg, (nf, npart) in expect.items():
-        w = W.CONFIGS[cfg](with_inputs=False)
+        w = W.WORKLOADS[cfg](with_inputs=False)
         inf = api.plan_from_workload(w, upload=False).info()
         assert (inf["n_full"], inf["n_partial"]) == (nf, npart), cfg
 

@@ -292,12 +292,12 @@ def test_merge_closed_forms():
 # Pair counts and tile classes: closed forms, brute force, the pages' examples
 # --------------------------------------------------------------------------
 def test_pair_counts_closed_forms():
-    assert oracle.pair_count(W.config1(False).slices, 256) == 256 * 257 // 2 == 32896
-    w2 = W.config2(False)
+    assert oracle.pair_count(W.causal_s256(False).slices, 256) == 256 * 257 // 2 == 32896
+    w2 = W.varlen_causal_t16384(False)
     assert oracle.pair_count(w2.slices, w2.sq) == sum(L * (L + 1) // 2 for L in w2.extra["lengths"])
-    w3 = W.config3(False)
+    w3 = W.block_sparse_strided_s32768(False)
     assert oracle.pair_count(w3.slices, w3.sq) == 4192 * 128 * 128 + 256 * (128 * 129 // 2)
-    w5 = W.config5(False)
+    w5 = W.kv_split_q8192(False)
     assert oracle.pair_count(w5.slices, w5.sq) == 7 * 8192 ** 2 + 8192 * 8193 // 2
 
 
@@ -328,12 +328,12 @@ def test_tile_csr_brute_force(bq, bk):
 
 
 def test_tile_counts_closed_forms():
-    _, _, tag = oracle.tile_csr(W.config1(False).slices, 256, 256, 128, 128)
+    _, _, tag = oracle.tile_csr(W.causal_s256(False).slices, 256, 256, 128, 128)
     assert (tag == 1).sum() == 1 and (tag == 2).sum() == 2
-    w3 = W.config3(False)
+    w3 = W.block_sparse_strided_s32768(False)
     _, _, tag = oracle.tile_csr(w3.slices, w3.sq, w3.sk, 128, 128)
     assert (tag == 1).sum() == 4192 and (tag == 2).sum() == 256
-    w5 = W.config5(False)
+    w5 = W.kv_split_q8192(False)
     diag = w5.extra["chunk_slices"][7]
     _, _, tag = oracle.tile_csr(diag, 8192, 8192, 128, 128)
     assert (tag == 1).sum() == 2016 and (tag == 2).sum() == 64

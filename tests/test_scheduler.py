@@ -65,7 +65,7 @@ def _check_plan_schedule(plan):
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_workload_schedules(cfg):
-    w = W.CONFIGS[cfg](with_inputs=False)
+    w = W.WORKLOADS[cfg](with_inputs=False)
     plan = api.plan_from_workload(w, upload=False)
     inf, loads = _check_plan_schedule(plan)
     assert inf["n_splits"] == 0 and inf["n_units"] == inf["n_items"]   # no row needs splitting
