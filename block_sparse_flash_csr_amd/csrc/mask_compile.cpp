@@ -89,109 +89,136 @@ bsfa_status compile_mask(const bsfa_slice *slices, int32_t n_slices, bsfa_plan &
     const int64_t bq = p.bq, bk = p.bk, sq = p.sq, sk = p.sk;
     p.n_qt = (int32_t)((sq + bq - 1) / bq);
     p.n_kt = (int32_t)((sk + bk - 1) / bk);
+    auto live = [&](const bsfa_slice &sl) { return sl.q0 < sl.q1 && sl.k0 < sl.k1; };
+    // Key tiles [kt0, kt1) that slice sl reaches in query tile qt (empty when no row of
+    // the tile admits a key of the slice).
+    auto kt_range = [&](const bsfa_slice &sl, int64_t qt, int64_t &kt0, int64_t &kt1) {
+        const int64_t r1 = std::min((qt + 1) * bq, sq);
+        const int64_t b = std::min<int64_t>(sl.q1, r1);
+        const int64_t diag = sl.type == BSFA_CAUSAL ? (int64_t)sl.k1 - sl.q1 : kDiagFull;
+        const int64_t j_lo = sl.k0, j_hi = row_hi(b - 1, sl.k1, diag);
+        kt0 = j_lo / bk;
+        kt1 = j_lo < j_hi ? (j_hi + bk - 1) / bk : kt0;
+    };
     try {
-        // 1. every (tile, slice) incidence with at least one admitted pair, bucketed by
-        //    query-tile row (slices visit rows in order, so a counting pass suffices)
-        std::vector<int64_t> row_count((size_t)p.n_qt + 1, 0);
-        auto walk = [&](auto &&emit) {
+        // 1. the slices that reach each query tile, in slice order (CSR over query tiles;
+        //    O(n_slices + sum of query tiles per slice))
+        std::vector<int64_t> sptr((size_t)p.n_qt + 1, 0);
+        {
+            std::vector<int64_t> diff((size_t)p.n_qt + 1, 0);
+            for (int32_t s = 0; s < n_slices; ++s) {
+                if (!live(slices[s])) continue;
+                ++diff[(size_t)(slices[s].q0 / bq)];
+                --diff[(size_t)((slices[s].q1 - 1) / bq) + 1];
+            }
+            int64_t run = 0;
+            for (int32_t qt = 0; qt < p.n_qt; ++qt) {
+                run += diff[qt];
+                sptr[(size_t)qt + 1] = sptr[qt] + run;
+            }
+        }
+        std::vector<int32_t> slist((size_t)sptr[p.n_qt]);
+        int64_t bound = 0;   // tiles touched, counted with multiplicity: >= nnz
+        {
+            std::vector<int64_t> fill(sptr.begin(), sptr.end() - 1);
             for (int32_t s = 0; s < n_slices; ++s) {
                 const bsfa_slice &sl = slices[s];
-                if (sl.q0 >= sl.q1 || sl.k0 >= sl.k1) continue;
-                const int64_t diag = sl.type == BSFA_CAUSAL ? (int64_t)sl.k1 - sl.q1 : kDiagFull;
+                if (!live(sl)) continue;
                 for (int64_t qt = sl.q0 / bq; qt * bq < sl.q1; ++qt) {
-                    const int64_t r0 = qt * bq, r1 = std::min(r0 + bq, sq);
-                    const int64_t a = std::max<int64_t>(sl.q0, r0), b = std::min<int64_t>(sl.q1, r1);
-                    const int64_t j_lo = sl.k0, j_hi = row_hi(b - 1, sl.k1, diag);
-                    if (j_lo >= j_hi) continue;
-                    const bool rows_all = a == r0 && b == r1;
-                    for (int64_t kt = j_lo / bk; kt * bk < j_hi; ++kt) {
-                        const int64_t c0 = kt * bk, c1 = std::min(c0 + bk, sk);
-                        const bool covers = rows_all && sl.k0 <= c0 && sl.k1 >= c1 &&
-                                            (c1 - 1) <= r0 + diag;
-                        emit(Touch{(int32_t)qt, (int32_t)kt, s, covers ? 1 : 0});
-                    }
+                    slist[(size_t)fill[qt]++] = s;
+                    int64_t kt0, kt1;
+                    kt_range(sl, qt, kt0, kt1);
+                    bound += kt1 - kt0;
                 }
             }
-        };
-        walk([&](const Touch &t) { ++row_count[(size_t)t.qt + 1]; });
-        for (int32_t qt = 0; qt < p.n_qt; ++qt) row_count[(size_t)qt + 1] += row_count[qt];
-        std::vector<Touch> touches((size_t)row_count[p.n_qt]);
-        {
-            std::vector<int64_t> fill(row_count.begin(), row_count.end() - 1);
-            walk([&](const Touch &t) { touches[(size_t)fill[t.qt]++] = t; });
-        }
-        auto by_col = [](const Touch &x, const Touch &y) {
-            if (x.kt != y.kt) return x.kt < y.kt;
-            return x.slice < y.slice;
-        };
-        for (int32_t qt = 0; qt < p.n_qt; ++qt) {
-            auto b = touches.begin() + row_count[qt], e = touches.begin() + row_count[(size_t)qt + 1];
-            if (!std::is_sorted(b, e, by_col)) std::sort(b, e, by_col);
         }
 
-        // 2. one CSR entry per distinct tile
         p.row_ptr.assign((size_t)p.n_qt + 1, 0);
         p.col.clear();
         p.tag.clear();
         p.piece_ptr.assign(1, 0);
         p.pieces.clear();
-        p.col.reserve(touches.size());
-        p.tag.reserve(touches.size());
-        p.piece_ptr.reserve(touches.size() + 1);
+        p.col.reserve((size_t)bound);
+        p.tag.reserve((size_t)bound);
+        p.piece_ptr.reserve((size_t)bound + 1);
         p.n_full = p.n_partial = p.pairs = 0;
+
+        // 2. per query tile: its (tile, slice) incidences with at least one admitted pair,
+        //    ordered by key tile and then slice, grouped into tiles and classified
+        auto by_col = [](const Touch &x, const Touch &y) {
+            if (x.kt != y.kt) return x.kt < y.kt;
+            return x.slice < y.slice;
+        };
+        std::vector<Touch> row;
         std::vector<Piece> cand;
         std::vector<std::pair<int64_t, int64_t>> ivs;
-        size_t t = 0;
-        while (t < touches.size()) {
-            size_t u = t;
-            bool covered = false;
-            while (u < touches.size() && touches[u].qt == touches[t].qt &&
-                   touches[u].kt == touches[t].kt) {
-                covered |= touches[u].covers != 0;
-                ++u;
-            }
-            const int64_t qt = touches[t].qt, kt = touches[t].kt;
-            const int64_t r0 = qt * bq, r1 = std::min(r0 + bq, sq);
-            const int64_t c0 = kt * bk, c1 = std::min(c0 + bk, sk);
-            const int64_t area = (r1 - r0) * (c1 - c0);
-            bool full = covered;
-            int64_t count = area;
-            if (!covered) {
-                cand.clear();
-                for (size_t x = t; x < u; ++x) {
-                    const bsfa_slice &sl = slices[touches[x].slice];
-                    Piece pc;
-                    pc.q_lo = std::max<int32_t>(sl.q0, (int32_t)r0);
-                    pc.q_hi = std::min<int32_t>(sl.q1, (int32_t)r1);
-                    pc.k_lo = std::max<int32_t>(sl.k0, (int32_t)c0);
-                    pc.k_hi = std::min<int32_t>(sl.k1, (int32_t)c1);
-                    pc.diag = sl.type == BSFA_CAUSAL ? sl.k1 - sl.q1 : kDiagFull;
-                    pc.pad0 = pc.pad1 = pc.pad2 = 0;
-                    cand.push_back(pc);
+        for (int32_t qt = 0; qt < p.n_qt; ++qt) {
+            const int64_t r0 = (int64_t)qt * bq, r1 = std::min(r0 + bq, sq);
+            row.clear();
+            for (int64_t x = sptr[qt]; x < sptr[(size_t)qt + 1]; ++x) {
+                const int32_t s = slist[(size_t)x];
+                const bsfa_slice &sl = slices[s];
+                const int64_t diag = sl.type == BSFA_CAUSAL ? (int64_t)sl.k1 - sl.q1 : kDiagFull;
+                const int64_t a = std::max<int64_t>(sl.q0, r0), b = std::min<int64_t>(sl.q1, r1);
+                const bool rows_all = a == r0 && b == r1;
+                int64_t kt0, kt1;
+                kt_range(sl, qt, kt0, kt1);
+                for (int64_t kt = kt0; kt < kt1; ++kt) {
+                    const int64_t c0 = kt * bk, c1 = std::min(c0 + bk, sk);
+                    const bool covers = rows_all && sl.k0 <= c0 && sl.k1 >= c1 && (c1 - 1) <= r0 + diag;
+                    row.push_back(Touch{qt, (int32_t)kt, s, covers ? 1 : 0});
                 }
-                // one piece that does not cover the tile leaves it partial; several
-                // pieces may still cover it together, which the union count settles
-                count = cand.size() == 1 ? piece_count(cand[0], r0, r1, c0, c1)
-                                         : union_count(cand, r0, r1, c0, c1, ivs);
-                full = count == area;
             }
-            p.col.push_back((int32_t)kt);
-            if (full) {
-                p.tag.push_back(BSFA_TILE_FULL);
-                ++p.n_full;
-            } else {
-                p.tag.push_back(BSFA_TILE_PARTIAL);
-                ++p.n_partial;
-                p.pieces.insert(p.pieces.end(), cand.begin(), cand.end());
+            if (!std::is_sorted(row.begin(), row.end(), by_col)) std::sort(row.begin(), row.end(), by_col);
+
+            size_t t = 0;
+            while (t < row.size()) {
+                size_t u = t;
+                bool covered = false;
+                while (u < row.size() && row[u].kt == row[t].kt) {
+                    covered |= row[u].covers != 0;
+                    ++u;
+                }
+                const int64_t kt = row[t].kt;
+                const int64_t c0 = kt * bk, c1 = std::min(c0 + bk, sk);
+                const int64_t area = (r1 - r0) * (c1 - c0);
+                bool full = covered;
+                int64_t count = area;
+                if (!covered) {
+                    // clipped pieces of the tile, in slice order
+                    cand.clear();
+                    for (size_t x = t; x < u; ++x) {
+                        const bsfa_slice &sl = slices[row[x].slice];
+                        Piece pc;
+                        pc.q_lo = std::max<int32_t>(sl.q0, (int32_t)r0);
+                        pc.q_hi = std::min<int32_t>(sl.q1, (int32_t)r1);
+                        pc.k_lo = std::max<int32_t>(sl.k0, (int32_t)c0);
+                        pc.k_hi = std::min<int32_t>(sl.k1, (int32_t)c1);
+                        pc.diag = sl.type == BSFA_CAUSAL ? sl.k1 - sl.q1 : kDiagFull;
+                        pc.pad0 = pc.pad1 = pc.pad2 = 0;
+                        cand.push_back(pc);
+                    }
+                    // one piece that does not cover the tile leaves it partial; several
+                    // pieces may still cover it together, which the union count settles
+                    count = cand.size() == 1 ? piece_count(cand[0], r0, r1, c0, c1)
+                                             : union_count(cand, r0, r1, c0, c1, ivs);
+                    full = count == area;
+                }
+                p.col.push_back((int32_t)kt);
+                if (full) {
+                    p.tag.push_back(BSFA_TILE_FULL);
+                    ++p.n_full;
+                } else {
+                    p.tag.push_back(BSFA_TILE_PARTIAL);
+                    ++p.n_partial;
+                    p.pieces.insert(p.pieces.end(), cand.begin(), cand.end());
+                }
+                p.piece_ptr.push_back((int32_t)p.pieces.size());
+                p.pairs += count;
+                t = u;
             }
-            p.piece_ptr.push_back((int32_t)p.pieces.size());
-            p.pairs += count;
             p.row_ptr[(size_t)qt + 1] = (int32_t)p.col.size();
-            t = u;
         }
-        // rows with no entry inherit the running count
-        for (int32_t qt = 0; qt < p.n_qt; ++qt)
-            if (p.row_ptr[(size_t)qt + 1] < p.row_ptr[qt]) p.row_ptr[(size_t)qt + 1] = p.row_ptr[qt];
     } catch (const std::bad_alloc &) {
         return BSFA_ERR_OOM;
     }
