@@ -240,6 +240,15 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
             out[w.name].update(mfma_busy_pct=ctr["mfma_busy_pct"], l2_hit_pct=ctr["l2_hit_pct"],
                                hbm_bytes_per_launch=ctr["hbm_bytes_per_launch"],
                                hbm_gbs=ctr["hbm_bytes_per_launch"] / ms * 1e-6)
+        # the same roofline figures as the headline's, for this workload's kernel launch
+        out[w.name]["roofline"] = {
+            "bound": "mfma", "achieved": fl / ms * 1e-9, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": fl / ms * 1e-9 / PEAK_BF16_TFLOPS, "kernel": f"attn_fwd_kernel<{w.d}>", "kernel_ms": ms,
+            "flops_per_launch": fl,
+            "algorithmic_bytes": w.sq * w.hq * (4 * w.d + 4) + w.sk * w.hkv * 4 * w.d,
+            "traffic": None if ctr is None else ctr["hbm_bytes_per_launch"],
+            "traffic_unit": "bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, copy-calibrated; "
+                            "null once the kernel changed since the counters were taken)"}
         log(f"{w.name}: {ms:.3f} ms  {fl / ms * 1e-9:.1f} TFLOPS")
         plan.close()
         del q, k, v, o, lse
@@ -268,10 +277,11 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
     del q, k, v, o, lse
     torch.cuda.empty_cache()
 
-    # Backward at the varlen causal workload: one call runs the dQ kernel (by query tile,
-    # which also forms D = rowsum(dO*O)) and the dK/dV kernel (by key tile).  Algorithmic work is 5
-    # products of 2*d flops per admitted pair (S, dP, dV, dK, dQ); the kernels execute 7
-    # (S and dP are recomputed by both gradient kernels instead of using atomics).
+    # Backward at the varlen causal workload: one call runs the D kernel (D_i = sum_j P_ij
+    # dP_ij by query tile), the dQ kernel (by query tile) and the dK/dV kernel (by key tile).
+    # Algorithmic work is 5 products of 2*d flops per admitted pair (S, dP, dV, dK, dQ); the
+    # kernels execute 9 (S and dP are recomputed by all three kernels instead of storing
+    # P or using atomics).
     w = W.varlen_causal_t16384()
     q, k, v = api.to_device_bf16(w.q), api.to_device_bf16(w.k), api.to_device_bf16(w.v)
     g = api.to_device_bf16(W.random_grad(np.random.default_rng(2002), w.sq, w.hq, w.d))
@@ -283,14 +293,14 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
     dk = torch.empty((w.sk, w.hkv, w.d), dtype=torch.float32, device="cuda")
     dv = torch.empty_like(dk)
     delta = torch.empty_like(lse)
-    f = lambda: api.attn_bwd(q, k, v, o, g, lse, plan, w.scale, dq=dq, dk=dk, dv=dv, delta=delta,
+    f = lambda: api.attn_bwd(q, k, v, g, lse, plan, w.scale, dq=dq, dk=dk, dv=dv, delta=delta,
                              stream=stream)
     sustain(f, warm_s)
     ms = float(np.median(event_times(f, reps * 2, stream)))
     name = w.name + "_backward"
     out[name] = {"kernel_ms": ms, "tflops": fl / ms * 1e-9, "frac_of_peak": fl / ms * 1e-9 / PEAK_BF16_TFLOPS,
                  "flops_per_pair": 10 * w.d, "pairs_per_head": info["pairs"],
-                 "note": "dQ, dK, dV (fp32) from O, LSE and dO; algorithmic flops = 2.5x the forward's"}
+                 "note": "dQ, dK, dV (fp32) from LSE and dO; algorithmic flops = 2.5x the forward's"}
     log(f"{name}: {ms:.3f} ms  {fl / ms * 1e-9:.1f} TFLOPS (algorithmic)")
     plan.close()
     del q, k, v, g, o, lse, dq, dk, dv, delta
@@ -347,7 +357,8 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
     fl = 4.0 * d * info["pairs"] * hq
     o = torch.empty((sq, hq, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((hq, sq), dtype=torch.float32, device="cuda")
-    f = lambda: api.attn_fwd(q, k, v, plan, 1.0 / np.sqrt(d), out=o, lse=lse, stream=stream)
+    ws = api.workspace_for(plan)              # the split rows' partial results
+    f = lambda: api.attn_fwd(q, k, v, plan, 1.0 / np.sqrt(d), out=o, lse=lse, workspace=ws, stream=stream)
     sustain(f, warm_s)
     ms = float(np.median(event_times(f, reps * 2, stream)))
     name = f"prefill_chunk_q{sq}_ctx{sk}_gqa{hq}x{hkv}_d{d}"
@@ -356,7 +367,7 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
                  "note": "not a reference workload; shows the in-call KV split (forward + part merge)"}
     log(f"{name}: {ms:.3f} ms  {fl / ms * 1e-9:.1f} TFLOPS ({info['n_units']} units, {info['n_splits']} split rows)")
     plan.close()
-    del q, k, v, o, lse
+    del q, k, v, o, lse, ws
     torch.cuda.empty_cache()
 
     # KV split: 8 partial forwards over 8192-token KV chunks, then the merge
@@ -447,34 +458,65 @@ def counter_pass(api, W):
         torch.cuda.empty_cache()
 
 
-def cpu_baseline(w, info, target_s):
-    """The fp64 oracle on host cores.  The whole headline workload fits the time budget
-    (~1.8e11 flops), so the sample is all of it unless a first timed slice says otherwise."""
-    import oracle
-    threads = min(os.cpu_count() or 1, 16)
-    rows_all = [(h, i) for h in range(w.hq) for i in range(w.sq)]
-    # time one head first; run everything when the extrapolation fits 2x the target
-    t0 = time.perf_counter()
-    oracle.attn_fwd(w.q, w.k, w.v, w.slices, w.scale, rows=rows_all[:w.sq], n_threads=threads)
-    t_head = time.perf_counter() - t0
-    n_heads = w.hq if t_head * w.hq <= 2 * target_s else max(1, int(target_s / max(t_head, 1e-3)))
-    rows = rows_all[:n_heads * w.sq]
-    t0 = time.perf_counter()
-    oracle.attn_fwd(w.q, w.k, w.v, w.slices, w.scale, rows=rows, n_threads=threads)
-    dt = time.perf_counter() - t0
-    pairs = info["pairs"] * n_heads
-    tflops = 4.0 * w.d * pairs / dt * 1e-12
-    what = "the whole workload" if n_heads == w.hq else f"{n_heads} of {w.hq} heads"
-    model = None
+def _host_cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
-            model = next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), None)
+            return next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), None)
     except OSError:
-        pass
+        return None
+
+
+def cpu_baseline(w, target_s, bq=128):
+    """The fp64 oracle on host cores for workload w (its unsplit mask, every head).  Whole
+    when a first timed query tile extrapolates to within twice target_s; otherwise every
+    k-th query tile (k a power of two chosen from that rate), all heads, extrapolated by
+    admitted-pair count.  TFLOPS = 4 * d * (sampled pairs) / wall time."""
+    import oracle
+    threads = oracle.default_threads()
+    n_qt = (w.sq + bq - 1) // bq
+    row_pairs = {}
+
+    def pairs_of(i):
+        if i not in row_pairs:
+            row_pairs[i] = sum(hi - lo for lo, hi in oracle.row_key_set(w.slices, i))
+        return row_pairs[i]
+
+    def tile_rows(qt):
+        return [(h, i) for h in range(w.hq) for i in range(qt * bq, min((qt + 1) * bq, w.sq))]
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.attn_fwd(w.q, w.k, w.v, w.slices, w.scale, rows=rows, n_threads=threads)
+        return time.perf_counter() - t0
+
+    total_pairs = oracle.pair_count(w.slices, w.sq) * w.hq
+    probe_qt = n_qt - 1                          # the last tile: the most keys in a causal mask
+    probe = tile_rows(probe_qt)
+    probe_pairs = sum(pairs_of(i) for _, i in probe)
+    t_probe = run(probe)
+    rate = probe_pairs / max(t_probe, 1e-6)      # pairs per second
+    k = 1
+    while total_pairs / k / rate > (2 * target_s if k == 1 else target_s) and k < n_qt:
+        k *= 2
+    if k == 1:
+        rows = None
+        pairs = total_pairs
+        dt = run(None) if w.sq * w.hq > len(probe) else t_probe
+        what = f"the whole workload: {w.sq * w.hq} (head, row) outputs"
+    else:
+        qts = list(range(0, n_qt, k))
+        rows = [r for qt in qts for r in tile_rows(qt)]
+        pairs = sum(pairs_of(i) for _, i in rows)
+        dt = run(rows)
+        what = (f"every {k}th query tile of 128 rows ({len(qts)} of {n_qt}), all {w.hq} heads: "
+                f"{len(rows)} (head, row) outputs")
+    tflops = 4.0 * w.d * pairs / dt * 1e-12
     return {"value": tflops, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
-            "host_cpu": model, "host_cpu_count": os.cpu_count(),
-            "sample": f"{what}: {len(rows)} (head, row) outputs, {pairs} unmasked pairs, "
-                      f"{dt:.1f} s wall on {threads} threads"}
+            "host_cpu": _host_cpu_model(), "host_cpu_count": os.cpu_count(),
+            "compiler_flags": " ".join(oracle.CFLAGS),
+            "sample": f"{what}, {pairs} unmasked pairs ({pairs / total_pairs:.3f} of the workload's), "
+                      f"{dt:.1f} s wall on {threads} threads",
+            "workload_s_extrapolated": dt * total_pairs / pairs}
 
 
 def main():
@@ -486,7 +528,10 @@ def main():
     ap.add_argument("--prewarm-s", type=float, default=1.0,
                     help="untimed seconds of headline steps before the warmup steps (GPU clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle time budget for the headline workload")
+    ap.add_argument("--other-cpu-seconds", type=float, default=10.0,
+                    help="oracle time budget for each of the other workloads")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--counter-pass", action="store_true",
@@ -525,7 +570,16 @@ def main():
         f"forward kernel {kernel_ms:.4f} ms "
         f"({achieved:.1f} TFLOPS, {achieved / PEAK_BF16_TFLOPS:.3f} of peak)")
     others = {} if args.quick else other_workloads(api, W, warm_s=0.5 * args.prewarm_s)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, info, args.cpu_seconds)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+    if not args.no_cpu_baseline:
+        # the oracle beside every other workload, after all GPU timing (the GPU is idle)
+        for cfg in (1, 3, 4, 5):
+            wc = W.WORKLOADS[cfg]()
+            if wc.name in others:
+                others[wc.name]["cpu_baseline"] = cpu_baseline(wc, args.other_cpu_seconds)
+                log(f"oracle {wc.name}: {others[wc.name]['cpu_baseline']['value']:.4f} TFLOPS "
+                    f"({others[wc.name]['cpu_baseline']['sample']})")
+            del wc
 
     result = {
         "metric": "effective fwd TFLOPS (unmasked pairs) and % of bf16 MFMA peak, 1 GPU",

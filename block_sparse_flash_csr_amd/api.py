@@ -20,7 +20,8 @@ MERGE_MAX_PARTS = 16
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "shape mismatch", 3: "misaligned pointer or stride",
            4: "unsupported head dim or tile size", 5: "invalid mask", 6: "out of memory",
-           7: "HIP runtime error", 8: "plan not uploaded to the current device"}
+           7: "HIP runtime error", 8: "plan not uploaded to the current device",
+           9: "plan metadata failed its consistency check"}
 
 
 class BsfaError(RuntimeError):
@@ -82,10 +83,10 @@ def library():
     lib.bsfa_lpt_assign.argtypes = [P, I32, I32, P, P]
     lib.bsfa_lpt_assign.restype = ctypes.c_double
     lib.bsfa_attn_fwd.argtypes = [ctypes.POINTER(Tensor)] * 3 + [P, ctypes.c_float,
-                                                                 ctypes.POINTER(Tensor), P, I64, P]
+                                                                 ctypes.POINTER(Tensor), P, I64, P, I64, P]
     lib.bsfa_attn_merge.argtypes = [P, P, I32, I64, I64, I64, I32, I32, I32,
                                     ctypes.POINTER(Tensor), P, P]
-    lib.bsfa_attn_bwd.argtypes = [ctypes.POINTER(Tensor)] * 5 + [P, I64, P, ctypes.c_float,
+    lib.bsfa_attn_bwd.argtypes = [ctypes.POINTER(Tensor)] * 4 + [P, I64, P, ctypes.c_float,
                                                                  P, P, P, P, P]
     lib.bsfa_plan_export_pieces.argtypes = [P, P, P, I64]
     lib.bsfa_dcsr_build.argtypes = [P, I32, I32, I32, I32, I32, P, PP]
@@ -309,8 +310,19 @@ def _tview(t):
     return Tensor(ctypes.c_void_p(t.data_ptr()), t.stride(0), t.stride(1))
 
 
-def attn_fwd(q, k, v, plan: Plan, scale: float, out=None, lse=None, stream=None):
+def workspace_for(plan: Plan, device="cuda"):
+    """Device workspace for the split rows of a plan (None when no row is split)."""
+    import torch
+    n = plan.info()["workspace_bytes"]
+    if n == 0:
+        return None
+    return torch.empty(n // 4, dtype=torch.float32, device=device)
+
+
+def attn_fwd(q, k, v, plan: Plan, scale: float, out=None, lse=None, workspace=None, stream=None):
     """Forward over the plan's mask.  q [sq, hq, d], k/v [sk, hkv, d] bf16 CUDA tensors.
+    workspace: fp32 device tensor of at least the plan's workspace_bytes when a row is
+    split (allocated here when not given).
 
     Returns (O [sq, hq, d] bf16, LSE [hq, sq] fp32)."""
     import torch
@@ -329,27 +341,36 @@ def attn_fwd(q, k, v, plan: Plan, scale: float, out=None, lse=None, stream=None)
     assert q.dtype == k.dtype == v.dtype == out.dtype == torch.bfloat16
     assert tuple(out.shape) == (sq, hq, d)
     assert lse.dtype == torch.float32 and lse.stride(1) == 1 and lse.shape[0] == hq
+    if workspace is None and plan.info()["workspace_bytes"] > 0:
+        workspace = workspace_for(plan, q.device)
+        if stream is not None:
+            # allocated on the current stream, used on `stream`: keep the allocator from
+            # handing the memory out again before that stream's work has run
+            workspace.record_stream(stream)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                            workspace.numel() * workspace.element_size())
     tq, tk, tv, to = _tview(q), _tview(k), _tview(v), _tview(out)
     _check("bsfa_attn_fwd", library().bsfa_attn_fwd(
         ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), plan.handle, float(scale),
-        ctypes.byref(to), ctypes.c_void_p(lse.data_ptr()), lse.stride(0), _stream_handle(stream)))
+        ctypes.byref(to), ctypes.c_void_p(lse.data_ptr()), lse.stride(0), ctypes.c_void_p(ws_ptr),
+        ws_bytes, _stream_handle(stream)))
     return out, lse
 
 
-def attn_bwd(q, k, v, out, dout, lse, plan: Plan, scale: float, dq=None, dk=None, dv=None,
+def attn_bwd(q, k, v, dout, lse, plan: Plan, scale: float, dq=None, dk=None, dv=None,
              delta=None, stream=None):
-    """Gradients of the plan's masked attention.  q/out/dout [sq, hq, d], k/v [sk, hkv, d]
+    """Gradients of the plan's masked attention.  q/dout [sq, hq, d], k/v [sk, hkv, d]
     bf16; lse [hq, >= sq] fp32 from the forward.
 
-    Returns (dQ [sq, hq, d], dK [sk, hkv, d], dV [sk, hkv, d]) fp32; delta (rowsum of
-    dout * out, shaped like lse) is scratch the call fills."""
+    Returns (dQ [sq, hq, d], dK [sk, hkv, d], dV [sk, hkv, d]) fp32; delta (D_i =
+    sum_j P_ij dP_ij, shaped like lse) is scratch the call fills."""
     import torch
     sq, hq, d = q.shape
     psq, psk, phq, phkv, pd = plan.shapes()
     if (sq, hq, d) != (psq, phq, pd):
         raise ValueError(f"q shape {tuple(q.shape)} does not match the plan ({psq}, {phq}, {pd})")
     for name, t, shp in (("k", k, (psk, phkv, pd)), ("v", v, (psk, phkv, pd)),
-                         ("out", out, (psq, phq, pd)), ("dout", dout, (psq, phq, pd))):
+                         ("dout", dout, (psq, phq, pd))):
         if tuple(t.shape) != shp:
             raise ValueError(f"{name} shape {tuple(t.shape)} does not match the plan {shp}")
         assert t.dtype == torch.bfloat16, f"{name} must be bf16"
@@ -367,9 +388,9 @@ def attn_bwd(q, k, v, out, dout, lse, plan: Plan, scale: float, dq=None, dk=None
     for name, t, shp in (("dq", dq, (sq, hq, d)), ("dk", dk, (psk, phkv, d)), ("dv", dv, (psk, phkv, d))):
         assert t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shp, name
     assert delta.dtype == torch.float32 and delta.stride() == lse.stride() and delta.shape == lse.shape
-    tq, tk, tv, to, tg = _tview(q), _tview(k), _tview(v), _tview(out), _tview(dout)
+    tq, tk, tv, tg = _tview(q), _tview(k), _tview(v), _tview(dout)
     _check("bsfa_attn_bwd", library().bsfa_attn_bwd(
-        ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(to), ctypes.byref(tg),
+        ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(tg),
         ctypes.c_void_p(lse.data_ptr()), lse.stride(0), plan.handle, float(scale),
         ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()),
         ctypes.c_void_p(delta.data_ptr()), _stream_handle(stream)))
@@ -383,11 +404,15 @@ def attn_merge(o_parts, lse_parts, out=None, lse=None, stream=None):
     assert n == len(lse_parts) and n >= 1
     t, h, d = o_parts[0].shape
     st = o_parts[0].stride()
+    if st[2] != 1:
+        raise ValueError("partials need a contiguous head dim (stride 1)")
     for p in o_parts:
         assert p.shape == (t, h, d) and p.stride() == st and p.dtype == torch.bfloat16
     lst = lse_parts[0].stride(0)
     for l in lse_parts:
         assert l.shape[0] == h and l.stride(0) == lst and l.stride(1) == 1 and l.dtype == torch.float32
+        if l.shape[1] < t:
+            raise ValueError(f"an LSE part covers {l.shape[1]} tokens, fewer than the {t} merged")
     if out is None:
         out = torch.empty((t, h, d), dtype=torch.bfloat16, device=o_parts[0].device)
     if lse is None:

@@ -5,8 +5,12 @@
 // forward and backward; FlashAttention-T blog, lineage paragraph: the tiled pass
 // recomputes the softmax from the saved log-sum-exp instead of storing it):
 //   P_ij  = 2^(c s_ij - LSE_i log2 e) on admitted pairs, s_ij = q_i . k_j, c = scale log2 e
-//   D_i   = sum_e dO_ie O_ie                       (kernel 2, which also stores it)
-//   dS_ij = P_ij (dO_i . v_j - D_i)
+//   dP_ij = dO_i . v_j
+//   D_i   = sum_j P_ij dP_ij                       (kernel 1: a first pass over the CSR
+//                                                   row; equal to dO_i . O_i for the
+//                                                   exact O, without the bf16 output's
+//                                                   rounding)
+//   dS_ij = P_ij (dP_ij - D_i)
 //   dQ_i  = scale sum_j dS_ij k_j                  (kernel 2: by query tile, CSR row)
 //   dK_j  = scale sum_(h,i) dS_ij q_i,  dV_j = sum_(h,i) P_ij dO_i
 //                                                  (kernel 3: by key tile, CSR column,
@@ -14,6 +18,8 @@
 // No atomics: every output element has one writer, so the result is deterministic.
 //
 // Design (own, for CDNA4):
+//   * Kernels 1 and 2 are one kernel body: kernel 1 forms only S^T and dP^T and sums
+//     P dP per query row; kernel 2 reads that D and adds the dQ product.
 //   * Kernel 2 mirrors the forward's transposed products: S^T = K Q^T and
 //     dP^T = V dO^T with Q and dO held as B operands, so a lane owns one query column
 //     and its LSE_i, D_i are scalars; dQ^T += K^T dS^T takes K^T from the LDS tile with
@@ -27,7 +33,7 @@
 //     XOR-swizzled by the row's low bits so that row reads are conflict-free.
 //   * A row without any admitted key has LSE = -inf and only meets partial tiles, whose
 //     mask gives its scores -inf: its weights come out exactly 0.  Rows past the end are
-//     zero rows (with LSE = D = 0 in kernel 3, -inf in kernel 2) and contribute 0.
+//     zero rows (with LSE = D = 0 in kernel 3, -inf in kernels 1 and 2) and contribute 0.
 #include <climits>
 #include <type_traits>
 
@@ -50,7 +56,7 @@ typedef __attribute__((address_space(3))) void *lds_ptr;
 typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
 
 constexpr int kThreads = 256;
-constexpr int kStep = 64;                 // keys (kernel 2) or queries (kernel 3) per step
+constexpr int kStep = 64;                 // keys (kernels 1, 2) or queries (kernel 3) per step
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int32_t kRsrcWord3 = 0x00020000;
 
@@ -229,7 +235,7 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
-// Operands are read this many products ahead of their MFMA (kernel 3, kernel 2).
+// Operands are read this many products ahead of their MFMA (kernel 3, kernels 1 and 2).
 constexpr int kAheadKv = 2, kAheadQ = 2;
 
 // S += X Y^T and dP += Z W^T over one 64-row LDS tile pair (x_t, z_t) against the register
@@ -258,9 +264,9 @@ __device__ __forceinline__ void score_products(const char *x_t, const char *z_t,
 }
 
 // ---------------------------------------------------------------------------
-// kernel 2: dQ by query tile (one workgroup per (head, query tile), in the plan's launch
-// order), 64-key steps over the CSR row; the K and V tiles of step j + 1 load (LDS
-// double buffer) while step j computes
+// kernels 1 and 2: D, then dQ, by query tile (one workgroup per (head, query tile), in
+// the plan's launch order), 64-key steps over the CSR row; the K and V tiles of step
+// j + 1 load (LDS double buffer) while step j computes
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqTiles {
@@ -325,7 +331,40 @@ __device__ __forceinline__ void dq_step(char *__restrict__ kd, char *__restrict_
     }
 }
 
+// One step of the D pass: issue the next step's K/V loads, then S^T = K Q^T,
+// dP^T = V dO^T and dsum += 2^(c S^T - LSE_i log2 e) dP^T over this lane's keys.
 template <int D>
+__device__ __forceinline__ void delta_step(char *__restrict__ kd, char *__restrict__ vd, const char *__restrict__ kt,
+                                           const char *__restrict__ vt, bool issue, __amdgpu_buffer_rsrc_t rk,
+                                           __amdgpu_buffer_rsrc_t rv, int32_t k_st, int32_t v_st, int wave, int lane,
+                                           const Addr<D> &ad, const bf16x8 (&qf)[BCfg<D>::KS],
+                                           const bf16x8 (&gf)[BCfg<D>::KS], uint64_t m, bool masked_step, float c,
+                                           float nl, float &dsum)
+{
+    if (issue) {
+        tile_dma<D>(rk, k_st, kd, wave, lane);
+        tile_dma<D>(rv, v_st, vd, wave, lane);
+    }
+    if (masked_step && __builtin_amdgcn_ballot_w64(m != 0ull) == 0ull) return;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        s[b] = f32x16{};
+        dp[b] = f32x16{};
+    }
+    __builtin_amdgcn_s_setprio(1);
+    score_products<D, kAheadQ>(kt, vt, qf, gf, ad, s, dp);
+    __builtin_amdgcn_s_setprio(0);
+    if (masked_step) mask_scores(m, s);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            dsum = __builtin_fmaf(__builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, nl)), dp[b][r], dsum);
+}
+
+// DELTA: kernel 1 (D_i = sum_j P_ij dP_ij into `delta`); else kernel 2 (dQ, reading D).
+template <int D, bool DELTA>
 __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
 {
     using C = BCfg<D>;
@@ -349,23 +388,10 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
     // P is 0 whatever the tile holds
     const float lse = qvalid ? a.lse[(int64_t)h * a.lse_sh + qrow] : -INFINITY;
     const float nl = lse == -INFINITY ? -INFINITY : -lse * kLog2e;
-    // D_i = sum_e dO_ie O_ie: this lane holds half of row i's dims of dO (gf) and loads
-    // the same half of O; lanes l and l ^ 32 hold the two halves.  The dK/dV kernel,
-    // launched after this one, reads D from `delta`.
+    // kernel 1: this lane's partial sum of P dP (lanes l and l ^ 32 cover the two halves
+    // of each 64-key step); kernel 2: D_i of this lane's row as kernel 1 stored it
     float dlt = 0.f;
-    {
-        bf16x8 of[C::KS];
-        load_frag<D>((const __bf16 *)a.o + (int64_t)qrow0 * a.o_st + (int64_t)h * a.o_sh, a.o_st, a.sq - qrow0, l32,
-                     hh, of);
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dlt = __builtin_fmaf((float)gf[ks][e], (float)of[ks][e], dlt);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(dlt), __float_as_int(dlt), false, false);
-        dlt = __int_as_float(sw[0]) + __int_as_float(sw[1]);
-        if (qvalid && hh == 0) a.delta[(int64_t)h * a.lse_sh + qrow] = dlt;
-        if (!qvalid) dlt = 0.f;
-    }
+    if constexpr (!DELTA) dlt = qvalid ? a.delta[(int64_t)h * a.lse_sh + qrow] : 0.f;
     f32x16 acc[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
@@ -426,11 +452,21 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
         __builtin_amdgcn_s_waitcnt(0);   // this step's tiles are in LDS (own loads) ...
         __syncthreads();                 // ... for every wave, and the other buffer is free
         char *cur = smem + buf * L::BUF, *nxt = smem + (buf ^ 1) * L::BUF;
-        dq_step<D>(nxt + L::K0, nxt + L::V0, cur + L::K0, cur + L::V0, more, rk, rv, a.k_st, a.v_st, wave, lane,
-                   ad, qf, gf, m, masked_step, a.c, nl, dlt, acc);
+        if constexpr (DELTA)
+            delta_step<D>(nxt + L::K0, nxt + L::V0, cur + L::K0, cur + L::V0, more, rk, rv, a.k_st, a.v_st, wave,
+                          lane, ad, qf, gf, m, masked_step, a.c, nl, dlt);
+        else
+            dq_step<D>(nxt + L::K0, nxt + L::V0, cur + L::K0, cur + L::V0, more, rk, rv, a.k_st, a.v_st, wave, lane,
+                       ad, qf, gf, m, masked_step, a.c, nl, dlt, acc);
         e = ne;
         sub = ns;
         buf ^= 1;
+    }
+    if constexpr (DELTA) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(dlt), __float_as_int(dlt), false, false);
+        const float dsum = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+        if (qvalid && hh == 0) a.delta[(int64_t)h * a.lse_sh + qrow] = dsum;
+        return;
     }
     // lane (query l32, half hh) holds dims 32 db + 8 g4 + 4 hh + 0..3 of its query
     if (qvalid) {
@@ -690,7 +726,10 @@ __global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv2_kernel(const BwdArg
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream)
 {
-    if (a.sq > 0) hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.n_qt * a.hq), dim3(kThreads), 0, stream, a);
+    if (a.sq > 0) {
+        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(a.n_qt * a.hq), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(a.n_qt * a.hq), dim3(kThreads), 0, stream, a);
+    }
     if (a.sk > 0) hipLaunchKernelGGL(bwd_dkdv2_kernel<D>, dim3(a.n_kt * a.hkv), dim3(2 * kThreads), 0, stream, a);
     return hipGetLastError();
 }

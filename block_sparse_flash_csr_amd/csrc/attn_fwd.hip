@@ -679,7 +679,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
         if (slot >= 0) {
             // one part of a split row: normalised fp32 O and its LSE into the workspace
             // slot (rows past the end included; the merge skips them)
-            float *ws = a.meta.ws + (size_t)slot * (kKernelBq * (D + 1));
+            float *ws = a.ws + (size_t)slot * (kKernelBq * (D + 1));
             const int r = wave * 32 + l32;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)

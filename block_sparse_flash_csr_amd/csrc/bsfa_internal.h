@@ -45,6 +45,10 @@ static_assert(sizeof(Split) == 16, "Split is one 16-byte word");
 constexpr int32_t kDiagFull = 1 << 30;
 constexpr int kKernelBq = 128;   // query rows per work item (4 waves x 32)
 constexpr int kKernelBk = 64;    // keys per inner step of the forward kernel
+// The kernels address the entries (16 B each) and the pieces (32 B each) of a plan
+// through 32-bit buffer offsets: a plan whose entry or piece array reaches 2^31 bytes
+// is refused (BSFA_ERR_UNSUPPORTED).
+constexpr size_t kMaxEntries = (size_t)1 << 27, kMaxPieces = (size_t)1 << 26;
 constexpr int kNumXcd = 8;       // MI355X: 8 accelerator complex dies, 32 CUs each
 constexpr int kNumCu = 256;
 
@@ -66,8 +70,6 @@ struct DeviceMeta {
     const int32_t *bin_items = nullptr;   // unit ids in execution order per bin
     const Unit *units = nullptr;
     const Split *splits = nullptr;
-    float *ws = nullptr;                  // partial results of split rows: per slot
-                                          // O [128][d] then LSE [128], fp32
     const int32_t *t_ptr = nullptr;       // transposed CSR: per key tile [n_kt + 1]
     const int32_t *t_list = nullptr;      // (query tile, entry) pairs, ascending query tile
     const int32_t *dq_order = nullptr;    // gradient launch orders: workgroup -> item
@@ -150,12 +152,14 @@ struct FwdArgs {
     int32_t sq, sk, hq, hkv, n_qt, bk_plan;
     float c;  // scale * log2(e)
     DeviceMeta meta;
+    float *ws;                     // partial results of split rows (caller's workspace): per
+                                   // slot O [128][d] then LSE [128], fp32
     int32_t n_bins;
     int32_t n_entries, n_pieces;   // sizes of meta.entries / meta.pieces (bounds of vector loads)
 };
 hipError_t launch_attn_fwd(const FwdArgs &a, int d, hipStream_t stream);
 
-// Merge of split rows: partial results in meta.ws -> O (bf16) and LSE.
+// Merge of split rows: partial results in the workspace -> O (bf16) and LSE.
 struct SplitMergeArgs {
     const float *ws;
     const Split *splits;
@@ -166,14 +170,15 @@ struct SplitMergeArgs {
 };
 hipError_t launch_split_merge(const SplitMergeArgs &a, int d, hipStream_t stream);
 
-// Backward: delta = rowsum(dO * O); dQ per query tile over its CSR row; dK, dV per
-// key tile over its CSR column and the query heads of its key/value head.
+// Backward: delta_i = sum_j P_ij dP_ij per query row (a first pass over the CSR row);
+// dQ per query tile over its CSR row; dK, dV per key tile over its CSR column and the
+// query heads of its key/value head.
 struct BwdArgs {
-    const void *q, *k, *v, *o, *dout;
+    const void *q, *k, *v, *dout;
     const float *lse;
     float *delta;
     float *dq, *dk, *dv;                 // fp32, contiguous [tokens, heads, d]
-    int32_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh, do_st, do_sh, lse_sh;
+    int32_t q_st, q_sh, k_st, k_sh, v_st, v_sh, do_st, do_sh, lse_sh;
     int32_t sq, sk, hq, hkv, n_qt, n_kt, bk_plan;
     float scale, c;                      // c = scale * log2(e)
     DeviceMeta meta;

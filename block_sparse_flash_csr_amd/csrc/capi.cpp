@@ -32,6 +32,72 @@ bsfa_status check_slices(const bsfa_slice *s, int32_t n, int32_t sq, int32_t sk)
     return BSFA_OK;
 }
 
+// Plans past the kernels' addressing limits (kMaxEntries, kMaxPieces) are refused.
+bsfa_status check_plan_limits(size_t nnz, size_t n_pieces)
+{
+    return nnz >= kMaxEntries || n_pieces >= kMaxPieces ? BSFA_ERR_UNSUPPORTED : BSFA_OK;
+}
+
+// Internal consistency of a plan before its metadata reaches a kernel, which trusts it
+// completely: CSR offsets monotone and in range, every entry's key tile and piece range
+// in range (full tiles without pieces, partial tiles with at least one), pieces inside
+// the extents, units inside their query tile's CSR row, every unit in exactly one bin,
+// split slots and the column view and launch orders in range.  Host-only, linear in the
+// plan's size.
+bool plan_consistent(const bsfa_plan &p)
+{
+    const size_t nnz = p.col.size(), npc = p.pieces.size();
+    const int64_t n_items = (int64_t)p.hq * p.n_qt;
+    if (p.row_ptr.size() != (size_t)p.n_qt + 1 || p.tag.size() != nnz || p.piece_ptr.size() != nnz + 1) return false;
+    if (p.row_ptr[0] != 0 || (size_t)p.row_ptr[(size_t)p.n_qt] != nnz) return false;
+    for (int32_t t = 0; t < p.n_qt; ++t)
+        if (p.row_ptr[(size_t)t + 1] < p.row_ptr[(size_t)t]) return false;
+    if (p.piece_ptr[0] != 0 || (size_t)p.piece_ptr[nnz] != npc) return false;
+    for (size_t e = 0; e < nnz; ++e) {
+        const int32_t np = p.piece_ptr[e + 1] - p.piece_ptr[e];
+        if (np < 0 || p.col[e] < 0 || p.col[e] >= p.n_kt) return false;
+        if (p.tag[e] == BSFA_TILE_FULL ? np != 0 : (p.tag[e] != BSFA_TILE_PARTIAL || np < 1)) return false;
+    }
+    for (const Piece &pc : p.pieces)
+        if (pc.q_lo < 0 || pc.q_lo > pc.q_hi || pc.q_hi > p.sq || pc.k_lo < 0 || pc.k_lo > pc.k_hi || pc.k_hi > p.sk)
+            return false;
+    if ((int64_t)p.item_cost.size() != n_items || p.unit_cost.size() != p.units.size()) return false;
+    const size_t n_units = p.units.size();
+    for (const Unit &u : p.units) {
+        if (u.item < 0 || u.item >= n_items || u.slot < -1 || u.slot >= p.n_slots) return false;
+        const int32_t qt = u.item % p.n_qt;
+        if (u.eb < p.row_ptr[(size_t)qt] || u.eb > u.ee || u.ee > p.row_ptr[(size_t)qt + 1]) return false;
+    }
+    if (p.bin_ptr.empty() || p.bin_ptr[0] != 0 || (size_t)p.bin_ptr.back() != p.bin_items.size() ||
+        p.bin_items.size() != n_units)
+        return false;
+    for (size_t b = 0; b + 1 < p.bin_ptr.size(); ++b)
+        if (p.bin_ptr[b + 1] < p.bin_ptr[b]) return false;
+    std::vector<uint8_t> seen(n_units, 0);
+    for (int32_t u : p.bin_items) {
+        if (u < 0 || (size_t)u >= n_units || seen[(size_t)u]) return false;
+        seen[(size_t)u] = 1;
+    }
+    for (const Split &sp : p.splits)
+        if (sp.item < 0 || sp.item >= n_items || sp.first < 0 || sp.parts < 1 || sp.first + sp.parts > p.n_slots)
+            return false;
+    if (p.t_ptr.size() != (size_t)p.n_kt + 1 || p.t_list.size() != 2 * nnz || p.t_ptr[0] != 0 ||
+        (size_t)p.t_ptr[(size_t)p.n_kt] != nnz)
+        return false;
+    for (int32_t t = 0; t < p.n_kt; ++t)
+        if (p.t_ptr[(size_t)t + 1] < p.t_ptr[(size_t)t]) return false;
+    for (size_t i = 0; i < nnz; ++i) {
+        const int32_t qt = p.t_list[2 * i], e = p.t_list[2 * i + 1];
+        if (qt < 0 || qt >= p.n_qt || e < 0 || (size_t)e >= nnz) return false;
+    }
+    if ((int64_t)p.dq_order.size() != n_items || (int64_t)p.dkv_order.size() != (int64_t)p.hkv * p.n_kt) return false;
+    for (int32_t it : p.dq_order)
+        if (it < 0 || it >= n_items) return false;
+    for (int32_t it : p.dkv_order)
+        if (it < 0 || (int64_t)it >= (int64_t)p.hkv * p.n_kt) return false;
+    return true;
+}
+
 // Column view and schedule of a compiled plan.  They read the same CSR and write
 // disjoint fields, so a large plan builds them on two threads (each is a few passes over
 // the entries: tens of milliseconds at millions of tiles); a small one, or a host where
@@ -87,6 +153,7 @@ bsfa_status build_plan(const bsfa_slice *slices, int32_t n_slices, int32_t sq, i
     p->bq = bq;
     p->bk = bk;
     st = compile_mask(slices, n_slices, *p);
+    if (st == BSFA_OK) st = check_plan_limits(p->col.size(), p->pieces.size());
     if (st == BSFA_OK) st = finish_plan(*p);
     if (st != BSFA_OK) {
         delete p;
@@ -383,9 +450,10 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
 {
     if (!p) return BSFA_ERR_ARG;
     if (p->dbuf) return BSFA_ERR_STATE;
+    if (!plan_consistent(*p)) return BSFA_ERR_PLAN;
     hipStream_t s = (hipStream_t)stream;
-    // one image: row_ptr | entries | pieces | bin_ptr | bin_items | units | splits, then
-    // the workspace of split rows (device only, not copied)
+    // one image: row_ptr | entries | pieces | bin_ptr | bin_items | units | splits | column
+    // view | launch orders
     size_t off = 0;
     const size_t nnz = p->col.size();
     const size_t o_row = place<int32_t>(off, p->row_ptr.size());
@@ -400,7 +468,6 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     const size_t o_oq = place<int32_t>(off, p->dq_order.size());
     const size_t o_ok = place<int32_t>(off, p->dkv_order.size());
     const size_t bytes = (off + 255) & ~size_t(255);
-    const size_t ws_bytes = workspace_bytes(*p);
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return BSFA_ERR_HIP;
@@ -426,7 +493,7 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
         std::memcpy(h + o_ok, p->dkv_order.data(), p->dkv_order.size() * sizeof(int32_t));
 
     DevSlot *slot = nullptr;
-    st = dev_acquire(dev, bytes + ws_bytes, &slot);
+    st = dev_acquire(dev, bytes, &slot);
     if (st != BSFA_OK) {
         staging_release_now(stg);
         return st;
@@ -463,7 +530,6 @@ bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
     p->dev.bin_items = (const int32_t *)(base + o_bi);
     p->dev.units = (const Unit *)(base + o_un);
     p->dev.splits = (const Split *)(base + o_sp);
-    p->dev.ws = ws_bytes ? (float *)(base + bytes) : nullptr;
     p->dev.t_ptr = (const int32_t *)(base + o_tp);
     p->dev.t_list = (const int32_t *)(base + o_tl);
     p->dev.dq_order = (const int32_t *)(base + o_oq);
@@ -578,9 +644,16 @@ bsfa_status bsfa_plan_export_units(const bsfa_plan *p, int32_t *units)
 
 bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
                           const bsfa_plan *p, float scale, bsfa_tensor *o, float *lse,
-                          int64_t lse_stride_head, void *stream)
+                          int64_t lse_stride_head, void *workspace, int64_t workspace_bytes_cap,
+                          void *stream)
 {
     if (!q || !k || !v || !p || !o) return BSFA_ERR_ARG;
+    if (workspace_bytes_cap < 0) return BSFA_ERR_ARG;
+    if (p->n_slots > 0) {
+        // split rows: their parts write partial results into the caller's workspace
+        if (!workspace || (size_t)workspace_bytes_cap < workspace_bytes(*p)) return BSFA_ERR_ARG;
+        if (!aligned16(workspace)) return BSFA_ERR_ALIGN;
+    }
     if (!lse && p->sq > 0) return BSFA_ERR_ARG;   // no query: nothing is written
     if (!(scale > 0.f) || !std::isfinite(scale)) return BSFA_ERR_ARG;
     if (p->d != 64 && p->d != 128) return BSFA_ERR_UNSUPPORTED;
@@ -600,7 +673,9 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     for (int t = 0; t < 4; ++t) {
         if (ts[t]->ptr && !aligned16(ts[t]->ptr)) return BSFA_ERR_ALIGN;
         if (!stride_ok(ts[t]->stride_tok) || !stride_ok(ts[t]->stride_head)) return BSFA_ERR_ALIGN;
-        if (n_tok[t] > 1 && ts[t]->stride_tok < p->d) return BSFA_ERR_SHAPE;
+        // the kernels size their buffer ranges as rows x stride_tok: a tensor with a token
+        // needs stride_tok >= d even when it has only one
+        if (n_tok[t] > 0 && ts[t]->stride_tok < p->d) return BSFA_ERR_SHAPE;
         if (n_head[t] > 1 && ts[t]->stride_head < p->d) return BSFA_ERR_SHAPE;
         if (ts[t]->stride_tok > (1 << 24) || ts[t]->stride_head > INT32_MAX) return BSFA_ERR_UNSUPPORTED;
     }
@@ -628,6 +703,7 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     a.bk_plan = p->bk;
     a.c = scale * 1.4426950408889634f;
     a.meta = p->dev;
+    a.ws = p->n_slots > 0 ? (float *)workspace : nullptr;
     a.n_bins = (int32_t)p->bin_ptr.size() - 1;
     a.n_entries = (int32_t)p->col.size();
     a.n_pieces = (int32_t)p->pieces.size();
@@ -649,7 +725,7 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     if (launch_attn_fwd(a, p->d, s) != hipSuccess) return BSFA_ERR_HIP;
     if (!p->splits.empty()) {
         SplitMergeArgs m;
-        m.ws = p->dev.ws;
+        m.ws = a.ws;
         m.splits = p->dev.splits;
         m.n_splits = (int32_t)p->splits.size();
         m.n_qt = p->n_qt;
@@ -665,11 +741,11 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
 }
 
 bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
-                          const bsfa_tensor *o, const bsfa_tensor *dout, const float *lse,
-                          int64_t lse_stride_head, const bsfa_plan *p, float scale, float *dq, float *dk,
-                          float *dv, float *delta, void *stream)
+                          const bsfa_tensor *dout, const float *lse, int64_t lse_stride_head,
+                          const bsfa_plan *p, float scale, float *dq, float *dk, float *dv, float *delta,
+                          void *stream)
 {
-    if (!q || !k || !v || !o || !dout || !p) return BSFA_ERR_ARG;
+    if (!q || !k || !v || !dout || !p) return BSFA_ERR_ARG;
     if (p->sq > 0 && (!lse || !delta)) return BSFA_ERR_ARG;   // no query: neither is read
     if (!(scale > 0.f) || !std::isfinite(scale)) return BSFA_ERR_ARG;
     if (p->d != 64 && p->d != 128) return BSFA_ERR_UNSUPPORTED;
@@ -681,14 +757,14 @@ bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     if (lse_stride_head < p->sq || lse_stride_head > INT32_MAX) return BSFA_ERR_ARG;
     if ((p->sq > 0 && !dq) || (p->sk > 0 && (!dk || !dv))) return BSFA_ERR_ARG;
     if ((int64_t)p->n_kt * p->hkv >= INT32_MAX) return BSFA_ERR_UNSUPPORTED;   // one workgroup each
-    const int32_t n_tok[5] = {p->sq, p->sk, p->sk, p->sq, p->sq};
-    const int32_t n_head[5] = {p->hq, p->hkv, p->hkv, p->hq, p->hq};
-    const bsfa_tensor *ts[5] = {q, k, v, o, dout};
-    for (int t = 0; t < 5; ++t) {
+    const int32_t n_tok[4] = {p->sq, p->sk, p->sk, p->sq};
+    const int32_t n_head[4] = {p->hq, p->hkv, p->hkv, p->hq};
+    const bsfa_tensor *ts[4] = {q, k, v, dout};
+    for (int t = 0; t < 4; ++t) {
         if (n_tok[t] > 0 && !ts[t]->ptr) return BSFA_ERR_ARG;
         if (ts[t]->ptr && !aligned16(ts[t]->ptr)) return BSFA_ERR_ALIGN;
         if (!stride_ok(ts[t]->stride_tok) || !stride_ok(ts[t]->stride_head)) return BSFA_ERR_ALIGN;
-        if (n_tok[t] > 1 && ts[t]->stride_tok < p->d) return BSFA_ERR_SHAPE;
+        if (n_tok[t] > 0 && ts[t]->stride_tok < p->d) return BSFA_ERR_SHAPE;
         if (n_head[t] > 1 && ts[t]->stride_head < p->d) return BSFA_ERR_SHAPE;
         if (ts[t]->stride_tok > (1 << 24) || ts[t]->stride_head > INT32_MAX) return BSFA_ERR_UNSUPPORTED;
     }
@@ -697,7 +773,6 @@ bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     a.q = q->ptr;
     a.k = k->ptr;
     a.v = v->ptr;
-    a.o = o->ptr;
     a.dout = dout->ptr;
     a.lse = lse;
     a.delta = delta;
@@ -710,8 +785,6 @@ bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     a.k_sh = (int32_t)k->stride_head;
     a.v_st = (int32_t)v->stride_tok;
     a.v_sh = (int32_t)v->stride_head;
-    a.o_st = (int32_t)o->stride_tok;
-    a.o_sh = (int32_t)o->stride_head;
     a.do_st = (int32_t)dout->stride_tok;
     a.do_sh = (int32_t)dout->stride_head;
     a.lse_sh = (int32_t)lse_stride_head;
@@ -1016,6 +1089,8 @@ bsfa_status bsfa_plan_from_dcsr(bsfa_dcsr *csr, int32_t hq, int32_t hkv, int32_t
     bsfa_dcsr_view v;
     bsfa_status st = bsfa_dcsr_view_get(csr, &v);
     if (st != BSFA_OK) return st;
+    st = check_plan_limits((size_t)v.nnz, (size_t)v.n_pieces);
+    if (st != BSFA_OK) return st;
     bsfa_plan *p = new (std::nothrow) bsfa_plan;
     if (!p) return BSFA_ERR_OOM;
     p->sq = x->sq;
@@ -1087,6 +1162,7 @@ const char *bsfa_status_str(bsfa_status s)
     case BSFA_ERR_OOM: return "out of memory";
     case BSFA_ERR_HIP: return "HIP runtime error";
     case BSFA_ERR_STATE: return "plan not uploaded to the current device";
+    case BSFA_ERR_PLAN: return "plan metadata failed its consistency check";
     }
     return "unknown status";
 }

@@ -138,9 +138,10 @@ bsfa_status compile_mask(const bsfa_slice *slices, int32_t n_slices, bsfa_plan &
         p.tag.clear();
         p.piece_ptr.assign(1, 0);
         p.pieces.clear();
-        p.col.reserve((size_t)bound);
-        p.tag.reserve((size_t)bound);
-        p.piece_ptr.reserve((size_t)bound + 1);
+        const size_t cap = (size_t)std::min<int64_t>(bound, (int64_t)kMaxEntries);
+        p.col.reserve(cap);
+        p.tag.reserve(cap);
+        p.piece_ptr.reserve(cap + 1);
         p.n_full = p.n_partial = p.pairs = 0;
 
         // 2. per query tile: its (tile, slice) incidences with at least one admitted pair,
@@ -218,6 +219,8 @@ bsfa_status compile_mask(const bsfa_slice *slices, int32_t n_slices, bsfa_plan &
                 t = u;
             }
             p.row_ptr[(size_t)qt + 1] = (int32_t)p.col.size();
+            // past the kernels' addressing limits: stop here instead of compiling the rest
+            if (p.col.size() >= kMaxEntries || p.pieces.size() >= kMaxPieces) return BSFA_ERR_UNSUPPORTED;
         }
     } catch (const std::bad_alloc &) {
         return BSFA_ERR_OOM;

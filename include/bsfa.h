@@ -45,7 +45,8 @@ typedef enum {
     BSFA_ERR_MASK = 5,        /* slice outside [0, S), q1 < q0, k1 < k0, unknown type or code */
     BSFA_ERR_OOM = 6,         /* host or device allocation failed */
     BSFA_ERR_HIP = 7,         /* a HIP runtime call failed (including a sticky earlier fault) */
-    BSFA_ERR_STATE = 8        /* plan not uploaded to the current device */
+    BSFA_ERR_STATE = 8,       /* plan not uploaded to the current device */
+    BSFA_ERR_PLAN = 9         /* plan metadata failed its consistency check (internal error) */
 } bsfa_status;
 
 /* One mask slice ([MA] flexible masks; [UA] 3): the pairs (i, j) with q0 <= i < q1 and
@@ -96,10 +97,14 @@ typedef struct {
  * Dispatch Solver; [UA] 4.1 weights).  Creation is host-only and never touches
  * the GPU.  The kernels need bq == 128 and bk a multiple of 64; other tile sizes
  * build a plan whose CSR can be exported but which bsfa_attn_fwd rejects.
- * A plan is immutable after creation; the caller frees it with bsfa_plan_destroy.
+ * A plan is immutable after creation and may be shared by launches on several streams
+ * at once; the caller frees it with bsfa_plan_destroy.
+ * Limits: fewer than 2^27 non-empty tiles and 2^26 pieces (the kernels address both
+ * arrays with 32-bit byte offsets), e.g. a single causal sequence of up to about 2.9M
+ * tokens at 128 x 128 tiles; larger plans are refused with BSFA_ERR_UNSUPPORTED.
  * Errors: BSFA_ERR_ARG (null out, n_slices < 0, bad sizes), BSFA_ERR_SHAPE
  * (hq % hkv), BSFA_ERR_MASK (slice outside [0,sq) x [0,sk], q1 < q0, k1 < k0, unknown
- * type), BSFA_ERR_OOM. */
+ * type), BSFA_ERR_UNSUPPORTED (the limits above), BSFA_ERR_OOM. */
 bsfa_status bsfa_plan_create(const bsfa_slice *slices, int32_t n_slices, int32_t sq, int32_t sk,
                              int32_t hq, int32_t hkv, int32_t d, int32_t bq, int32_t bk,
                              bsfa_plan **out);
@@ -130,8 +135,10 @@ bsfa_status bsfa_plan_from_blocks(const uint8_t *codes, int32_t nbq, int32_t nbk
  * per-device pool the library owns: buffers are
  * allocated on first need, reused by later plans and held until process exit, so a
  * steady stream of plans allocates nothing and never synchronises.  Must precede
- * bsfa_attn_fwd.  Errors: BSFA_ERR_ARG, BSFA_ERR_STATE (already uploaded),
- * BSFA_ERR_OOM, BSFA_ERR_HIP. */
+ * bsfa_attn_fwd.  Before any device work the plan's metadata is checked on the host
+ * (offsets monotone and in range, every scheduled unit in exactly one bin, ...), since
+ * the kernels trust it.  Errors: BSFA_ERR_ARG, BSFA_ERR_STATE (already uploaded),
+ * BSFA_ERR_PLAN (metadata inconsistent: an internal error), BSFA_ERR_OOM, BSFA_ERR_HIP. */
 bsfa_status bsfa_plan_upload(bsfa_plan *plan, void *stream);
 
 /* Releases host memory and, if uploaded, hands the device buffer back to the pool
@@ -198,37 +205,47 @@ double bsfa_lpt_assign(const float *cost, int32_t n_items, int32_t n_bins, int32
  * Shapes come from the plan, which must be uploaded to the current device.
  * No allocation, no synchronisation; deterministic (no atomics).  The stream is
  * remembered so that bsfa_plan_destroy releases the plan's buffer behind it.
- * A plan with split rows (info.n_splits > 0) runs a second kernel on the same stream
- * that merges the parts; their partial results live in a workspace inside the plan's
- * device buffer, so launches of such a plan must not overlap (order them on one
- * stream).
- * Errors: BSFA_ERR_ARG, BSFA_ERR_ALIGN, BSFA_ERR_UNSUPPORTED (d not 64/128, bq != 128,
- * bk % 64 != 0), BSFA_ERR_STATE (plan not on this device), BSFA_ERR_HIP. */
+ * A plan with split rows (info.n_splits > 0; [UA] 3.2: a key range cut into parts whose
+ * summaries merge exactly) runs a second kernel on the same stream that merges the
+ * parts.  Their partial results go to `workspace`: caller device memory of at least
+ * info.workspace_bytes bytes (16-byte aligned), read and written only by this call's
+ * kernels; NULL (with workspace_bytes 0) is accepted when the plan has no split row.
+ * The plan itself is never written, so launches of one plan may overlap on several
+ * streams as long as each has its own workspace.
+ * Errors: BSFA_ERR_ARG (also a missing or too small workspace), BSFA_ERR_ALIGN,
+ * BSFA_ERR_SHAPE (stride_tok < d for a tensor with a token), BSFA_ERR_UNSUPPORTED (d not
+ * 64/128, bq != 128, bk % 64 != 0), BSFA_ERR_STATE (plan not on this device),
+ * BSFA_ERR_HIP. */
 bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
                           const bsfa_plan *plan, float scale, bsfa_tensor *o, float *lse,
-                          int64_t lse_stride_head, void *stream);
+                          int64_t lse_stride_head, void *workspace, int64_t workspace_bytes,
+                          void *stream);
 
 /* ---- backward ([MA] the same masked attention, forward and backward) ----------
  * Gradients of the forward above for an upstream gradient dO:
  *   P_ij = exp(scale q_i.k_j - LSE_i) on the plan's admitted pairs (0 elsewhere),
- *   D_i = sum_e dO_ie O_ie,  dS_ij = P_ij (dO_i.v_j - D_i),
+ *   dP_ij = dO_i.v_j,  D_i = sum_j P_ij dP_ij,  dS_ij = P_ij (dP_ij - D_i),
  *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_(h,i) dS_ij q_i,
  *   dV_j = sum_(h,i) P_ij dO_i  (h over the query heads of j's key/value head).
- * q, o, dout: bf16 [sq, hq, d]; k, v: bf16 [sk, hkv, d] (strides as bsfa_attn_fwd);
+ * D_i is formed from the recomputed P and dP (it equals dO_i.O_i for the exact O), so
+ * the forward's output is not an input and its bf16 rounding does not enter the
+ * gradients.
+ * q, dout: bf16 [sq, hq, d]; k, v: bf16 [sk, hkv, d] (strides as bsfa_attn_fwd);
  * lse: the forward's fp32 LSE [hq, lse_stride_head].  dq [sq, hq, d], dk and dv
  * [sk, hkv, d]: fp32, contiguous, 16-byte aligned, fully written (rows no key reaches
  * get zeros).  delta: caller scratch of LSE's shape (fp32 [hq, lse_stride_head]),
- * overwritten with D.  With sq == 0, q, o, dout, lse, delta and dq may be NULL; with
+ * overwritten with D.  With sq == 0, q, dout, lse, delta and dq may be NULL; with
  * sk == 0, k, v, dk and dv.  The plan must have bq = 128 and bk = 128 and be uploaded to the
- * current device.  Two kernels on stream: dQ by query tile (which also computes and
- * stores D), then dK/dV by key tile over the query heads of its key/value head (no
+ * current device.  Three kernels on stream: D by query tile over its CSR row, dQ by
+ * query tile, then dK/dV by key tile over the query heads of its key/value head (no
  * atomics, deterministic).  No allocation, no synchronisation.
- * Errors: BSFA_ERR_ARG, BSFA_ERR_ALIGN, BSFA_ERR_SHAPE, BSFA_ERR_UNSUPPORTED (d not 64/
- * 128, tiles not 128 x 128), BSFA_ERR_STATE, BSFA_ERR_HIP. */
+ * Errors: BSFA_ERR_ARG, BSFA_ERR_ALIGN, BSFA_ERR_SHAPE (stride_tok < d for a tensor with
+ * a token), BSFA_ERR_UNSUPPORTED (d not 64/128, tiles not 128 x 128), BSFA_ERR_STATE,
+ * BSFA_ERR_HIP. */
 bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
-                          const bsfa_tensor *o, const bsfa_tensor *dout, const float *lse,
-                          int64_t lse_stride_head, const bsfa_plan *plan, float scale, float *dq,
-                          float *dk, float *dv, float *delta, void *stream);
+                          const bsfa_tensor *dout, const float *lse, int64_t lse_stride_head,
+                          const bsfa_plan *plan, float scale, float *dq, float *dk, float *dv,
+                          float *delta, void *stream);
 
 /* ---- merge of KV-split partials ([UA] 3.2) -----------------------------------
  * For n partial results (O_t, LSE_t) of the same queries over disjoint key sets:

@@ -25,12 +25,23 @@ class _Slice(ctypes.Structure):
                 ("k1", ctypes.c_int32), ("type", ctypes.c_int32)]
 
 
+# -O3 at the x86-64-v3 level (AVX2, FMA): the library is compiled on one host and may be
+# run on another x86 host (-march=native would bind it to the first one's CPU);
+# -ffp-contract=off keeps every multiply and add rounded separately, as the C source
+# reads.
+CFLAGS = ["-O3", "-march=x86-64-v3", "-ffp-contract=off", "-std=c99", "-fPIC", "-shared", "-pthread"]
+MAX_THREADS = 16       # worker threads by default: at most the host's cores, at most 16
+
+
+def default_threads() -> int:
+    return max(1, min(os.cpu_count() or 1, MAX_THREADS))
+
+
 def build(force: bool = True) -> str:
     """Compile liboracle.so with gcc (host only)."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", _SRC,
-                               "-o", tmp, "-lm"])
+        subprocess.check_call(["gcc"] + CFLAGS + [_SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -124,7 +135,7 @@ def attn_fwd(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, slices,
     sk, hkv, d2 = k_bits.shape
     assert d2 == d and v_bits.shape == k_bits.shape
     if n_threads is None:
-        n_threads = os.cpu_count() or 1
+        n_threads = default_threads()
     if rows is None:
         o = np.zeros((sq, hq, d), np.float64)
         lse = np.zeros((hq, sq), np.float64)
@@ -169,7 +180,7 @@ def attn_bwd(q_bits, k_bits, v_bits, do_bits, slices, scale: float, n_threads: i
     dk = np.zeros((sk, hkv, d), np.float64)
     dv = np.zeros((sk, hkv, d), np.float64)
     if n_threads is None:
-        n_threads = os.cpu_count() or 1
+        n_threads = default_threads()
     rc = _load().oracle_attn_bwd(_ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(do_bits), sq, sk, hq, hkv,
                                  d, _slices(slices), len(slices), float(scale), _ptr(dq), _ptr(dk),
                                  _ptr(dv), int(n_threads))
@@ -192,7 +203,7 @@ def attn_bwd_sampled(q_bits, k_bits, v_bits, do_bits, slices, scale: float, rows
     dk = np.zeros((keys_arr.shape[0], d), np.float64)
     dv = np.zeros((keys_arr.shape[0], d), np.float64)
     if n_threads is None:
-        n_threads = os.cpu_count() or 1
+        n_threads = default_threads()
     rc = _load().oracle_attn_bwd_sampled(
         _ptr(q_bits), _ptr(k_bits), _ptr(v_bits), _ptr(do_bits), sq, sk, hq, hkv, d, _slices(slices),
         len(slices), float(scale), _ptr(rows_arr), rows_arr.shape[0], _ptr(dq), _ptr(keys_arr),

@@ -96,10 +96,10 @@ int main(int argc, char **argv)
     /* not yet uploaded: rejected */
     bsfa_tensor tq = {dq, (int64_t)hq * d, d}, tk = {dk, (int64_t)hkv * d, d}, tv = {dv, (int64_t)hkv * d, d};
     bsfa_tensor to = {dO, (int64_t)hq * d, d};
-    if (bsfa_attn_fwd(&tq, &tk, &tv, plan, scale, &to, (float *)dl, sq, NULL) != BSFA_ERR_STATE)
+    if (bsfa_attn_fwd(&tq, &tk, &tv, plan, scale, &to, (float *)dl, sq, NULL, 0, NULL) != BSFA_ERR_STATE)
         return fail("status", "a plan not uploaded must give BSFA_ERR_STATE");
     if ((st = bsfa_plan_upload(plan, NULL)) != BSFA_OK) return fail("bsfa_plan_upload", bsfa_status_str(st));
-    if ((st = bsfa_attn_fwd(&tq, &tk, &tv, plan, scale, &to, (float *)dl, sq, NULL)) != BSFA_OK)
+    if ((st = bsfa_attn_fwd(&tq, &tk, &tv, plan, scale, &to, (float *)dl, sq, NULL, 0, NULL)) != BSFA_OK)
         return fail("bsfa_attn_fwd", bsfa_status_str(st));
     if (hipDeviceSynchronize() != hipSuccess) return fail("hipDeviceSynchronize", "forward");
 

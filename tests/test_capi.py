@@ -92,19 +92,93 @@ def test_forward_rejects_unuploaded_and_unsupported():
     t = api.Tensor(ctypes.c_void_p(16), 8, 8)
     lse = ctypes.c_void_p(16)
     st = lib.bsfa_attn_fwd(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), p.handle, 0.1,
-                           ctypes.byref(t), lse, 64, None)
+                           ctypes.byref(t), lse, 64, None, 0, None)
     assert st == 4  # bq != 128
     p = api.Plan.from_slices([(0, 64, 0, 64, 1)], 64, 64, 1, 1, 96)
     st = lib.bsfa_attn_fwd(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), p.handle, 0.1,
-                           ctypes.byref(t), lse, 64, None)
+                           ctypes.byref(t), lse, 64, None, 0, None)
     assert st == 4  # d = 96
     p = api.Plan.from_slices([(0, 64, 0, 64, 1)], 64, 64, 1, 1, 128)
     st = lib.bsfa_attn_fwd(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), p.handle, 0.1,
-                           ctypes.byref(t), lse, 64, None)
+                           ctypes.byref(t), lse, 64, None, 0, None)
     assert st == 8  # not uploaded
     st = lib.bsfa_attn_fwd(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), p.handle, -1.0,
-                           ctypes.byref(t), lse, 64, None)
+                           ctypes.byref(t), lse, 64, None, 0, None)
     assert st == 1  # non-positive scale
+
+
+def test_forward_requires_a_workspace_for_split_rows():
+    """A plan with split rows needs caller workspace of at least info.workspace_bytes (the
+    plan itself holds none, so launches of one plan may overlap on several streams)."""
+    lib = api.library()
+    p = api.Plan.from_slices([(0, 128, 0, 65536, 1)], 128, 65536, 32, 8, 128)
+    info = p.info()
+    assert info["n_splits"] > 0 and info["workspace_bytes"] == info["n_units"] * 128 * 129 * 4
+    t = api.Tensor(ctypes.c_void_p(16), 1024, 128)
+    lse = ctypes.c_void_p(16)
+
+    def call(ws, nbytes):
+        return lib.bsfa_attn_fwd(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), p.handle, 0.1,
+                                 ctypes.byref(t), lse, 128, ws, nbytes, None)
+
+    assert call(None, 0) == 1                                        # no workspace
+    assert call(ctypes.c_void_p(16), info["workspace_bytes"] - 16) == 1   # too small
+    assert call(ctypes.c_void_p(24), info["workspace_bytes"]) == 3        # misaligned
+    assert call(ctypes.c_void_p(16), -1) == 1
+    assert call(ctypes.c_void_p(16), info["workspace_bytes"]) == 8        # then: not uploaded
+    # a plan without split rows needs none
+    q = api.Plan.from_slices([(0, 256, 0, 256, 1)], 256, 256, 2, 2, 128)
+    assert q.info()["workspace_bytes"] == 0
+    assert lib.bsfa_attn_fwd(ctypes.byref(t), ctypes.byref(t), ctypes.byref(t), q.handle, 0.1,
+                             ctypes.byref(t), lse, 256, None, 0, None) == 8
+
+
+def test_plans_past_the_addressing_limit_are_refused():
+    """The kernels address entries (16 B) and pieces (32 B) with 32-bit byte offsets: a plan
+    that reaches 2^27 non-empty tiles is refused rather than built and run wrong."""
+    lib = api.library()
+    h = ctypes.c_void_p()
+    s = 16 * 16384            # causal at 16 x 16 tiles: 16384 * 16385 / 2 > 2^27 tiles
+    one = (api.Slice * 1)(api.Slice(0, s, 0, s, 1))
+    assert lib.bsfa_plan_create(one, 1, s, s, 1, 1, 128, 16, 16, ctypes.byref(h)) == 4
+    assert not h.value
+    s = 16 * 16383            # 16383 * 16384 / 2 = 134,209,536 < 2^27 tiles: accepted
+    n_ok = 16383 * 16384 // 2
+    assert n_ok < 1 << 27
+    one = (api.Slice * 1)(api.Slice(0, s, 0, s, 1))
+    assert lib.bsfa_plan_create(one, 1, s, s, 1, 1, 128, 16, 16, ctypes.byref(h)) == 0
+    inf = api.PlanInfo()
+    assert lib.bsfa_plan_get_info(h, ctypes.byref(inf)) == 0 and inf.nnz == n_ok
+    lib.bsfa_plan_destroy(h)
+
+
+def test_corrupted_plans_are_refused_before_upload():
+    """tests/c_abi/plan_check (built by build()) corrupts one plan field at a time through
+    the library's internal layout; the upload's host-side check must refuse each plan
+    with BSFA_ERR_PLAN before any device work, and pass the intact plans."""
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "plan_check")
+    if not os.path.exists(exe):
+        pytest.fail(f"{exe} is missing: run build() first")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    print(r.stdout)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert sum(line.startswith("ok") for line in r.stdout.splitlines()) == 18
+
+
+def test_merge_binding_rejects_strided_head_dim_and_short_lse():
+    """The merge kernel reads partials with a contiguous head dim and LSE rows covering
+    every merged token; the binding refuses other views before any device call."""
+    import torch
+    base = torch.zeros((8, 2, 256), dtype=torch.bfloat16)
+    parts = [base[..., ::2], base[..., ::2]]          # head dim stride 2
+    lses = [torch.zeros((2, 8)), torch.zeros((2, 8))]
+    with pytest.raises(ValueError):
+        api.attn_merge(parts, lses)
+    parts = [torch.zeros((8, 2, 128), dtype=torch.bfloat16)] * 2
+    short = [torch.zeros((2, 16))[:, :4]] * 2         # 4 tokens of LSE for 8 merged tokens
+    with pytest.raises(ValueError):
+        api.attn_merge(parts, short)
 
 
 def test_merge_rejects_bad_arguments():
@@ -137,7 +211,7 @@ def test_backward_rejects_bad_arguments():
     lib = api.library()
     t = api.Tensor(ctypes.c_void_p(16), 8, 8)
     buf = ctypes.c_void_p(16)
-    tp = [ctypes.byref(t)] * 5
+    tp = [ctypes.byref(t)] * 4
 
     def call(plan, scale=0.1, lse=buf, dq=buf, delta=buf):
         return lib.bsfa_attn_bwd(*tp, lse, 64, plan.handle, scale, dq, buf, buf, delta, None)

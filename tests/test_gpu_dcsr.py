@@ -122,8 +122,8 @@ def test_plan_from_device_csr_equals_host_plan(cfg):
     oh, lh = api.attn_fwd(q, k, v, host, w.scale)
     od, ld = api.attn_fwd(q, k, v, dev, w.scale)
     g = api.to_device_bf16(W.random_grad(np.random.default_rng(cfg), w.sq, w.hq, w.d))
-    gh = api.attn_bwd(q, k, v, oh, g, lh, host, w.scale)
-    gd = api.attn_bwd(q, k, v, od, g, ld, dev, w.scale)
+    gh = api.attn_bwd(q, k, v, g, lh, host, w.scale)
+    gd = api.attn_bwd(q, k, v, g, ld, dev, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(oh.view(torch.int16), od.view(torch.int16)) and torch.equal(lh, ld)
     for x, y in zip(gh, gd):

@@ -73,13 +73,13 @@ def test_backward_packed_inputs_equal_contiguous():
     qc, kc, vc = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
     o, lse = api.attn_fwd(qc, kc, vc, plan, 1.0 / np.sqrt(d))
     g = dev_bf16(gb)
-    ref = api.attn_bwd(qc, kc, vc, o, g, lse, plan, 1.0 / np.sqrt(d))
+    ref = api.attn_bwd(qc, kc, vc, g, lse, plan, 1.0 / np.sqrt(d))
     _, q, k, v = _packed(qb, kb, vb)
-    # O and dO as views of one [T, 2 hq, d] buffer, LSE inside a wider one
+    # dO as a view into a [T, 2 hq, d] buffer (beside O), LSE inside a wider one
     og = torch.cat([o, g], dim=1)
     l_big = torch.full((hq, s + 24), 3.0, dtype=torch.float32, device="cuda")
     l_big[:, :s] = lse
-    got = api.attn_bwd(q, k, v, og[:, :hq], og[:, hq:], l_big[:, :s], plan, 1.0 / np.sqrt(d),
+    got = api.attn_bwd(q, k, v, og[:, hq:], l_big[:, :s], plan, 1.0 / np.sqrt(d),
                        delta=torch.empty_like(l_big)[:, :s])
     torch.cuda.synchronize()
     for name, a, b in zip(("dQ", "dK", "dV"), got, ref):

@@ -71,7 +71,7 @@ def test_max_size_backward(setup):
     g = W.device_normal_bf16((S, HQ, D), 95)
     o, lse = api.attn_fwd(q, k, v, plan, SCALE)
     say("max size backward: launching")
-    dq, dk, dv = api.attn_bwd(q, k, v, o, g, lse, plan, SCALE)
+    dq, dk, dv = api.attn_bwd(q, k, v, g, lse, plan, SCALE)
     torch.cuda.synchronize()
     for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
         assert torch.isfinite(t).all().item(), f"non-finite {name}"
@@ -116,9 +116,9 @@ def test_large_plan_column_view_built_beside_the_schedule():
     q, k, v, g = (api.to_device_bf16(x) for x in (qb, kb, vb, gb))
     say(f"large plan: S={s} nnz={plan.info()['nnz']}: forward + backward")
     o, lse = api.attn_fwd(q, k, v, plan, scale)
-    dq, dk, dv = api.attn_bwd(q, k, v, o, g, lse, plan, scale)
+    dq, dk, dv = api.attn_bwd(q, k, v, g, lse, plan, scale)
     again = api.Plan.from_slices(slices, s, s, hq, hkv, d).upload()
-    dq2, dk2, dv2 = api.attn_bwd(q, k, v, o, g, lse, again, scale)
+    dq2, dk2, dv2 = api.attn_bwd(q, k, v, g, lse, again, scale)
     torch.cuda.synchronize()
     for name, a, b in (("dQ", dq, dq2), ("dK", dk, dk2), ("dV", dv, dv2)):
         assert torch.isfinite(a).all().item(), f"non-finite {name}"

@@ -157,19 +157,27 @@ def sampled_check(w, plan, rows, what):
     return o, lse
 
 
-def test_varlen_causal_t16384_sampled():
-    w = W.varlen_causal_t16384()
+def workload_full_check(w, what):
+    """Every (head, row) output of a full-size workload, on the plan the benchmark times."""
+    import torch
     plan = api.plan_from_workload(w)
-    cu = w.cu_seqlens
-    extra = list(cu[:-1]) + list(cu[:-1] + 1) + list(cu[1:] - 1) + list(cu[1:] - 2)
-    sampled_check(w, plan, sample_rows(w, 256, 2, extra), "varlen causal t16384")
+    q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    say(f"{what}: launching forward ({w.sq} rows x {w.hq} heads)")
+    o, lse = api.attn_fwd(q, k, v, plan, w.scale)
+    torch.cuda.synchronize()
+    o_gpu, l_gpu = W.bf16_to_f32(host_bits(o)), lse.cpu().numpy()
+    plan.close()
+    say(f"{what}: oracle on every row")
+    o_ref, lse_ref = oracle.attn_fwd(w.q, w.k, w.v, w.slices, w.scale)
+    compare(o_gpu, l_gpu.T, o_ref, lse_ref.T, what)
 
 
-def test_block_sparse_strided_s32768_sampled():
-    w = W.block_sparse_strided_s32768()
-    plan = api.plan_from_workload(w)
-    extra = [128 * 8 * t + o for t in range(0, 32, 5) for o in (0, 1, 127)]
-    sampled_check(w, plan, sample_rows(w, 256, 3, extra), "block-sparse strided s32768")
+def test_varlen_causal_t16384_full():
+    workload_full_check(W.varlen_causal_t16384(), "varlen causal t16384, every output")
+
+
+def test_block_sparse_strided_s32768_full():
+    workload_full_check(W.block_sparse_strided_s32768(), "block-sparse strided s32768, every output")
 
 
 def test_range_slices_s65536_sampled():
@@ -338,6 +346,69 @@ def test_split_rows_full(seed, sq, sk, hq, hkv, d, kind):
     full_check(qb, kb, vb, slices, 1.0 / np.sqrt(d), f"split rows {kind}")
 
 
+def test_split_plan_shared_by_two_streams_at_once():
+    """One plan with split rows launched on two streams with no ordering between them,
+    each launch with its own workspace: the plan holds no per-launch state, so both
+    outputs equal the oracle's (and each other, bit for bit)."""
+    import torch
+    sq, sk, hq, hkv, d = 256, 12000, 2, 1, 128
+    rng = np.random.default_rng(37)
+    slices = [(0, sq, 0, sk, 1), (0, 40, 5000, 5100, 0)]
+    qb, kb, vb = W.random_inputs(rng, sq, sk, hq, hkv, d)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    plan = api.Plan.from_slices(slices, sq, sk, hq, hkv, d).upload()
+    inf = plan.info()
+    assert inf["n_splits"] > 0 and inf["workspace_bytes"] > 0, inf
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [api.workspace_for(plan) for _ in streams]
+    outs = [[(torch.empty((sq, hq, d), dtype=torch.bfloat16, device="cuda"),
+              torch.empty((hq, sq), dtype=torch.float32, device="cuda")) for _ in range(6)] for _ in streams]
+    torch.cuda.synchronize()
+    say(f"split plan on two streams at once: units={inf['n_units']} splits={inf['n_splits']}")
+    for i in range(6):
+        for s_i, s in enumerate(streams):
+            o, l = outs[s_i][i]
+            api.attn_fwd(q, k, v, plan, 1.0 / np.sqrt(d), out=o, lse=l, workspace=wss[s_i], stream=s)
+    torch.cuda.synchronize()
+    plan.close()
+    o_ref, lse_ref = oracle.attn_fwd(qb, kb, vb, slices, 1.0 / np.sqrt(d))
+    o0, l0 = outs[0][0]
+    compare(W.bf16_to_f32(host_bits(o0)), l0.cpu().numpy().T, o_ref, lse_ref.T, "split plan, two streams")
+    for s_i in range(2):
+        for i in range(6):
+            o, l = outs[s_i][i]
+            assert torch.equal(o, o0) and torch.equal(l, l0), (s_i, i)
+
+
+def test_one_token_tensors_need_a_full_row_stride():
+    """A tensor with a single token still needs stride_tok >= d (the kernels size their
+    buffer ranges as rows x stride): a smaller stride is refused, not read short."""
+    import ctypes
+    import torch
+    d = 128
+    plan = api.Plan.from_slices([(0, 1, 0, 50, 0)], 1, 50, 2, 1, d).upload()
+    lib = api.library()
+    q = torch.zeros((1, 2, d), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((50, 1, d), dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros((1, 2, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((2, 1), dtype=torch.float32, device="cuda")
+    tq_bad = api.Tensor(ctypes.c_void_p(q.data_ptr()), 8, d)
+    tq = api.Tensor(ctypes.c_void_p(q.data_ptr()), 2 * d, d)
+    tkv = api.Tensor(ctypes.c_void_p(kv.data_ptr()), d, d)
+    to = api.Tensor(ctypes.c_void_p(o.data_ptr()), 2 * d, d)
+
+    def call(tq_, to_):
+        return lib.bsfa_attn_fwd(ctypes.byref(tq_), ctypes.byref(tkv), ctypes.byref(tkv), plan.handle, 0.1,
+                                 ctypes.byref(to_), ctypes.c_void_p(lse.data_ptr()), 1, None, 0,
+                                 api._stream_handle())
+
+    assert call(tq_bad, to) == 2
+    assert call(tq, api.Tensor(ctypes.c_void_p(o.data_ptr()), 0, d)) == 2
+    assert call(tq, to) == 0
+    torch.cuda.synchronize()
+    plan.close()
+
+
 def test_plans_from_several_host_threads():
     """Four host threads build, upload, launch and destroy plans at the same time, each on
     its own stream (the plan pools, the staging images and the copy ordering are shared
@@ -423,14 +494,14 @@ def test_zero_length_extents():
     torch.cuda.synchronize()
     assert o0.numel() == 0
     # backward without queries: every key's gradient is zero
-    dq, dk, dv = api.attn_bwd(q0, kv, kv, o0, q0, l0, plan, 0.1)
+    dq, dk, dv = api.attn_bwd(q0, kv, kv, q0, l0, plan, 0.1)
     torch.cuda.synchronize()
     assert dq.numel() == 0 and bool((dk == 0).all()) and bool((dv == 0).all())
     plan.close()
     # backward without keys: dQ is zero
     plan = api.Plan.from_slices([], 100, 0, 2, 1, d).upload()
     g = dev_bf16(W.random_grad(rng, 100, 2, d))
-    dq, dk, dv = api.attn_bwd(q, k, k, o, g, lse, plan, 0.1)
+    dq, dk, dv = api.attn_bwd(q, k, k, g, lse, plan, 0.1)
     torch.cuda.synchronize()
     assert bool((dq == 0).all()) and dk.numel() == 0 and dv.numel() == 0
     plan.close()
