@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libbsfa.so")
 BSFA_FULL, BSFA_CAUSAL = 0, 1
 TILE_FULL, TILE_PARTIAL = 1, 2
 MERGE_MAX_PARTS = 16
+STATIC_WORKSPACE_BYTES = 32 << 20     # bsfa_attn_fwd_noalloc's per-GPU workspace
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "shape mismatch", 3: "misaligned pointer or stride",
            4: "unsupported head dim or tile size", 5: "invalid mask", 6: "out of memory",
@@ -84,6 +85,8 @@ def library():
     lib.bsfa_lpt_assign.restype = ctypes.c_double
     lib.bsfa_attn_fwd.argtypes = [ctypes.POINTER(Tensor)] * 3 + [P, ctypes.c_float,
                                                                  ctypes.POINTER(Tensor), P, I64, P, I64, P]
+    lib.bsfa_attn_fwd_noalloc.argtypes = [ctypes.POINTER(Tensor)] * 3 + [P, ctypes.c_float,
+                                                                         ctypes.POINTER(Tensor), P, I64, P]
     lib.bsfa_attn_merge.argtypes = [P, P, I32, I64, I64, I64, I32, I32, I32,
                                     ctypes.POINTER(Tensor), P, P]
     lib.bsfa_attn_bwd.argtypes = [ctypes.POINTER(Tensor)] * 4 + [P, I64, P, ctypes.c_float,
@@ -100,6 +103,7 @@ def library():
     for name in ("bsfa_plan_create", "bsfa_plan_from_varlen", "bsfa_plan_from_blocks",
                  "bsfa_plan_upload", "bsfa_plan_get_info", "bsfa_plan_export_csr",
                  "bsfa_plan_export_schedule", "bsfa_plan_export_units", "bsfa_attn_fwd",
+                 "bsfa_attn_fwd_noalloc",
                  "bsfa_attn_merge", "bsfa_attn_bwd", "bsfa_plan_export_pieces", "bsfa_dcsr_build",
                  "bsfa_dcsr_view_get", "bsfa_dcsr_export", "bsfa_plan_from_dcsr"):
         getattr(lib, name).restype = I32

@@ -724,6 +724,35 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
 
 }  // namespace
 
+// Static workspace for the split rows' partial results of bsfa_attn_fwd_noalloc (callers
+// that cannot allocate device memory).  One copy per GPU, held until the process ends;
+// every call on a GPU shares it (overlapping calls on one GPU race), and it keeps the
+// last call's contents: each part writes all of its slot before the merge reads it, so
+// nothing needs clearing.  Host code uses the per-device address from
+// hipGetSymbolAddress, never the array's name (a host-side stand-in).
+static __device__ __align__(256) float scratch[kStaticWorkspaceBytes / sizeof(float)];
+
+hipError_t static_workspace(float **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        // once per device, with that device current (it is: the caller's)
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = (float *)p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
 hipError_t launch_attn_fwd(const FwdArgs &a, int d, hipStream_t stream)
 {
     if (a.n_bins <= 0) return hipSuccess;

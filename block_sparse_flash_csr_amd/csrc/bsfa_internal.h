@@ -159,6 +159,11 @@ struct FwdArgs {
 };
 hipError_t launch_attn_fwd(const FwdArgs &a, int d, hipStream_t stream);
 
+// Size of the static device workspace of bsfa_attn_fwd_noalloc, and its address on the
+// current device (looked up once per device).
+constexpr size_t kStaticWorkspaceBytes = (size_t)32 << 20;
+hipError_t static_workspace(float **ptr);
+
 // Merge of split rows: partial results in the workspace -> O (bf16) and LSE.
 struct SplitMergeArgs {
     const float *ws;

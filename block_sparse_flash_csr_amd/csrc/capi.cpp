@@ -740,6 +740,19 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     return BSFA_OK;
 }
 
+static_assert(kStaticWorkspaceBytes == (size_t)BSFA_STATIC_WORKSPACE_BYTES, "one static workspace size");
+
+bsfa_status bsfa_attn_fwd_noalloc(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
+                                  const bsfa_plan *p, float scale, bsfa_tensor *o, float *lse,
+                                  int64_t lse_stride_head, void *stream)
+{
+    if (!p) return BSFA_ERR_ARG;
+    if (workspace_bytes(*p) > kStaticWorkspaceBytes) return BSFA_ERR_UNSUPPORTED;
+    float *ws = nullptr;
+    if (static_workspace(&ws) != hipSuccess) return BSFA_ERR_HIP;
+    return bsfa_attn_fwd(q, k, v, p, scale, o, lse, lse_stride_head, ws, (int64_t)kStaticWorkspaceBytes, stream);
+}
+
 bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
                           const bsfa_tensor *dout, const float *lse, int64_t lse_stride_head,
                           const bsfa_plan *p, float scale, float *dq, float *dk, float *dv, float *delta,

@@ -221,6 +221,24 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
                           int64_t lse_stride_head, void *workspace, int64_t workspace_bytes,
                           void *stream);
 
+/* ---- forward without allocation ------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): bsfa_attn_fwd with the split rows'
+ * partial results in a static device workspace of the library instead of a caller
+ * buffer.  The workspace is BSFA_STATIC_WORKSPACE_BYTES (32 MiB) per GPU, held from the
+ * library's first use on that GPU until the process ends, and shared by every call on
+ * that GPU: calls that overlap on one GPU (on different streams, or from several host
+ * threads) race on it and must be ordered by the caller.  Plans whose
+ * info.workspace_bytes exceeds it are refused with BSFA_ERR_UNSUPPORTED (about 500
+ * split-row parts at d = 128); plans without split rows never touch it.  Arguments,
+ * results and every other error as bsfa_attn_fwd; no allocation, no synchronisation.
+ * The workspace's address is looked up once per GPU, on the first call with that GPU
+ * current. */
+enum { BSFA_STATIC_WORKSPACE_BYTES = 32 << 20 };
+bsfa_status bsfa_attn_fwd_noalloc(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
+                                  const bsfa_plan *plan, float scale, bsfa_tensor *o, float *lse,
+                                  int64_t lse_stride_head, void *stream);
+
 /* ---- backward ([MA] the same masked attention, forward and backward) ----------
  * Gradients of the forward above for an upstream gradient dO:
  *   P_ij = exp(scale q_i.k_j - LSE_i) on the plan's admitted pairs (0 elsewhere),
