@@ -40,7 +40,10 @@
 //     the direct loads in flight into the other two tiles.
 //   * Softmax in base 2 with a single FMA for scale and shift, and conditional
 //     rescaling (FlashAttention-4 article: rescale only when needed): a row's running
-//     max moves only when its tile max exceeds it by more than tau = 8.
+//     max moves only when its tile max exceeds it by more than tau = 8.  At head dim 64,
+//     where the vector work binds, the tile max itself is skipped: a step's weights are
+//     taken against the running max and checked afterwards (their sum over a lane's keys
+//     at most 2^tau), with a recomputation only for the rare step that fails.
 //   * The per-element mask runs only on partial tiles and on the key tail
 //     (MagiAttention news: flexible masks at small cost; cheap boundary predicates):
 //     each lane turns the tile's slice pieces into key intervals for its query row.
@@ -73,9 +76,18 @@ typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
 constexpr int kThreads = 256;
 constexpr int kBkS = kKernelBk;          // keys per step
 constexpr float kTau = 8.0f;             // rescale threshold, log2 units
+constexpr float kRescaleSum = 256.0f;    // 2^kTau: bound on a lane's weight sum per step (lazy max)
 constexpr float kMFloor = -1.0e30f;      // finite start of the running max
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int32_t kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
+
+// Head dim 64 runs the vector-bound form of the softmax step ("lazy max"): no tile max of
+// the next step's scores; each step's weights are taken against the running max and only
+// a lane whose weights exceed 2^tau (or overflowed) sends the wave through a recomputation
+// with the true max.  At head dim 128 the extra branch costs more registers than the saved
+// maxima are worth.
+template <int D>
+constexpr bool kLazyMax = D == 64;
 
 template <int D>
 struct Cfg {
@@ -467,6 +479,25 @@ __device__ __forceinline__ void step_body(char *__restrict__ k_dst, char *__rest
         asm volatile("" : "+v"(e0), "+v"(e1));
         __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (kLazyMax<D>) {
+        // Conditional rescale after the fact (FlashAttention-4 article: rescale only when
+        // needed): the weights were taken against the running max; only when one of them
+        // (conservatively: their sum over this lane's keys) exceeds 2^tau, or overflowed,
+        // does the step take its true max, rescale the rows whose max moved by more than
+        // tau and take its weights again.  Both halves of a query row see the same max.
+        if (__builtin_amdgcn_ballot_w64(!(e0 + e1 <= kRescaleSum)) != 0) {
+            rescale_for<D>(tile_max(cur, c), acc);
+            const float nm2 = -acc.m;
+#pragma unroll
+            for (int v = 0; v < 32; ++v) {
+                const int j = v >> 3, r = v & 7;
+                pf[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[j >> 1][(j & 1) * 8 + r], c, nm2));
+                float &ex = (r & 1) ? e1 : e0;
+                ex = v < 2 ? pf[r] : ex + pf[r];
+                if (r == 7) pb[j] = __builtin_convertvector(pf, bf16x8);
+            }
+        }
+    }
     acc.l += e0 + e1;
 
     // Phase 2 also takes the unmasked tile max of the new scores (block 0 once its
@@ -487,16 +518,22 @@ __device__ __forceinline__ void step_body(char *__restrict__ k_dst, char *__rest
         }
         // max over 16 scores of one block: a 3-way max per group on groups B0.. (block 0)
         // and B1.. (block 1), the last element folded in at the end
-        if (i >= B0 && i < B0 + MG) mx0 = max3_step(nxt[0], i - B0, mx0);
-        if (i >= B1 && i < B1 + MG) mx1 = max3_step(nxt[1], i - B1, mx1);
+        if constexpr (!kLazyMax<D>) {
+            if (i >= B0 && i < B0 + MG) mx0 = max3_step(nxt[0], i - B0, mx0);
+            if (i >= B1 && i < B1 + MG) mx1 = max3_step(nxt[1], i - B1, mx1);
+        }
         asm volatile("" : "+v"(s0), "+v"(s1), "+v"(mx0), "+v"(mx1));
         __builtin_amdgcn_sched_barrier(0);
     }
     acc.lb += s0 + s1;
-    if (B1 == NP)
+    if constexpr (kLazyMax<D>) {
+        mx_raw = 0.f;   // not used
+    } else {
+        if (B1 == NP)
 #pragma unroll
-        for (int q = 0; q < MG; ++q) mx1 = max3_step(nxt[1], q, mx1);
-    mx_raw = vmax(vmax(mx0, nxt[0][15]), vmax(mx1, nxt[1][15]));
+            for (int q = 0; q < MG; ++q) mx1 = max3_step(nxt[1], q, mx1);
+        mx_raw = vmax(vmax(mx0, nxt[0][15]), vmax(mx1, nxt[1][15]));
+    }
 }
 
 template <int D>
@@ -635,7 +672,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
                                   min(kBkS, sj2.kv_end - sj2.kv0)};
                 const TileSrc vld{(const __bf16 *)a.v + (int64_t)g * a.v_sh + (int64_t)sj1.kv0 * a.v_st, a.v_st,
                                   min(kBkS, sj1.kv_end - sj1.kv0)};
-                rescale_for<D>(mx_cur, acc);   // needs only step j's tile max
+                if constexpr (!kLazyMax<D>) rescale_for<D>(mx_cur, acc);   // needs only step j's tile max
                 __builtin_amdgcn_sched_barrier(0);
                 // The score products run unconditionally so the block stays straight-line;
                 // on the last step they read a stale (valid) tile and are discarded.
@@ -645,7 +682,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
                 float mx_raw;
                 step_body<D>(smem + K_FREE, smem + V_NEXT, smem + K_NEXT, smem + V_CUR, kld, has2, vld, has1, ln,
                              wave, qf, cur, c, acc, nxt, mx_raw);
-                if (m1) {
+                if constexpr (kLazyMax<D>) {
+                    if (m1) apply_bits(bits, nxt);   // the maxima are taken only when needed
+                } else if (m1) {
                     apply_bits(bits, nxt);
                     mx_nxt = tile_max(nxt, c);
                 } else if (has1) {

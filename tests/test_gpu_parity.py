@@ -7,7 +7,7 @@ import oracle
 from block_sparse_flash_csr_amd import api
 from block_sparse_flash_csr_amd import workloads as W
 
-from gpu_helpers import compare, dev_bf16, host_bits, say, sample_rows
+from gpu_helpers import bf16_floor, compare, dev_bf16, host_bits, say, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -88,20 +88,65 @@ def test_bk64_plan():
     full_check(qb, kb, vb, slices, 1.0 / np.sqrt(128), "plan bk=64", bk=64)
 
 
-def test_large_logits_exercise_rescale():
-    """Q scaled x8: tile maxima jump by more than the rescale threshold."""
+def _large_logit_inputs(d):
     rng = np.random.default_rng(9)
     sq = sk = 512
-    qf = rng.standard_normal((sq, 2, 128), dtype=np.float32) * 8.0
+    qf = rng.standard_normal((sq, 2, d), dtype=np.float32) * 8.0
     qb = W.bf16_bits(qf)
-    _, kb, vb = W.random_inputs(rng, sq, sk, 2, 2, 128)
-    full_check(qb, kb, vb, [(0, sq, 0, sk, 1)], 1.0 / np.sqrt(128), "Q x8 causal")
+    _, kb, vb = W.random_inputs(rng, sq, sk, 2, 2, d)
+    return qb, kb, vb
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_large_logits_exercise_rescale(d):
+    """Tile maxima that jump by more than the rescale threshold (at d = 64 the weights
+    are checked after the fact, so these steps take the recomputation path)."""
+    qb, kb, vb = _large_logit_inputs(d)
+    sq = sk = qb.shape[0]
+    if d == 128:
+        full_check(qb, kb, vb, [(0, sq, 0, sk, 1)], 1.0 / np.sqrt(d), f"Q x8 causal d={d}")
     # increasing scores along keys: the max moves on every tile
     kf = W.bf16_to_f32(kb).copy()
     kf += np.linspace(0, 6, sk, dtype=np.float32)[:, None, None] * np.sign(
         W.bf16_to_f32(qb).mean(axis=0, keepdims=True))
-    full_check(qb, W.bf16_bits(kf), vb, [(0, sq, 0, sk, 0)], 1.0 / np.sqrt(128),
-               "growing max full")
+    full_check(qb, W.bf16_bits(kf), vb, [(0, sq, 0, sk, 0)], 1.0 / np.sqrt(d),
+               f"growing max full d={d}")
+    # scores that grow by tens of log2 units within one tile: the first weights taken
+    # against the running max overflow to infinity and must be recomputed
+    kf2 = W.bf16_to_f32(kb).copy()
+    kf2 += np.linspace(0, 40, sk, dtype=np.float32)[:, None, None] * np.sign(
+        W.bf16_to_f32(qb).mean(axis=0, keepdims=True))
+    full_check(qb, W.bf16_bits(kf2), vb, [(0, sq, 0, sk, 0)], 1.0 / np.sqrt(d),
+               f"steep max full d={d}")
+
+
+class OutputFormatBreach(AssertionError):
+    """The 1e-2 bar fails only by the bf16 output format: rounding the exact O to bf16
+    alone already exceeds it."""
+
+
+@pytest.mark.xfail(raises=OutputFormatBreach, strict=False,
+                   reason="rows nearly one-hot with |O| >= 4: rounding the exact output to bf16 alone "
+                          "gives 0.0129 > 1e-2")
+def test_one_hot_rows_d64():
+    """Q x8 causal at d = 64: some rows are nearly one-hot with |O| in [4, 8), where bf16
+    output rounding alone reaches 0.0156.  The kernel's error must be that rounding plus
+    at most the bf16 weights' share (2^-9 of |O|); the 1e-2 bar itself is a known breach."""
+    d = 64
+    qb, kb, vb = _large_logit_inputs(d)
+    sq = sk = qb.shape[0]
+    sl = [(0, sq, 0, sk, 1)]
+    say("Q x8 causal d=64 (nearly one-hot rows)")
+    o, lse = run_fwd(qb, kb, vb, sl, 1.0 / np.sqrt(d), sq, sk, 2, 2, d)
+    o_ref, lse_ref = oracle.attn_fwd(qb, kb, vb, sl, 1.0 / np.sqrt(d))
+    floor = bf16_floor(o_ref)
+    err = float(np.max(np.abs(o.astype(np.float64) - o_ref)))
+    dl = float(np.max(np.abs(lse.T - lse_ref.T)))
+    say(f"Q x8 causal d=64: max|dO| {err:.3e} (bf16 output floor {floor:.3e}), max|dLSE| {dl:.3e}")
+    assert not np.isnan(o).any() and dl <= 1e-3
+    assert err <= floor + 2.0 ** -9 * float(np.max(np.abs(o_ref))), (err, floor)
+    if err > 1e-2:
+        raise OutputFormatBreach(f"max|dO| {err} > 1e-2 with a bf16 output floor of {floor}")
 
 
 def test_fully_masked_rows_and_empty_tiles():
