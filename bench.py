@@ -332,9 +332,11 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
         v = dc.view()
         dev_ms = (time.perf_counter() - t0) * 1e3
         assert v["nnz"] == nnz
-        # a full plan (column view and schedule too) from the device CSR
+        # a full plan (column view and schedule too) from the device CSR, until its device
+        # image is complete
         t0 = time.perf_counter()
         dp = dc.plan(16, 16, 128)
+        torch.cuda.synchronize()
         dplan_ms = dev_ms + (time.perf_counter() - t0) * 1e3
         dp.close()
         mc[name] = {"slices": len(sl), "nnz": nnz, "touches": v["touches"], "host_plan_ms": host_ms,

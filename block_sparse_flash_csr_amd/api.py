@@ -98,6 +98,10 @@ def library():
     lib.bsfa_dcsr_destroy.argtypes = [P]
     lib.bsfa_plan_from_dcsr.argtypes = [P, I32, I32, I32, PP]
     lib.bsfa_dcsr_destroy.restype = None
+    lib.bsfa_set_rescale_threshold.argtypes = [ctypes.c_float]
+    lib.bsfa_set_rescale_threshold.restype = I32
+    lib.bsfa_get_rescale_threshold.argtypes = []
+    lib.bsfa_get_rescale_threshold.restype = ctypes.c_float
     lib.bsfa_status_str.argtypes = [I32]
     lib.bsfa_status_str.restype = ctypes.c_char_p
     for name in ("bsfa_plan_create", "bsfa_plan_from_varlen", "bsfa_plan_from_blocks",
@@ -175,8 +179,9 @@ class DeviceCsr:
         return row_ptr, col[:v["nnz"]], tag[:v["nnz"]], piece_ptr, pieces[:v["n_pieces"]]
 
     def plan(self, hq, hkv, d) -> "Plan":
-        """A (not yet uploaded) plan over this CSR: the same plan Plan.from_slices builds
-        for the same slices and tile sizes (bsfa_plan_from_dcsr)."""
+        """The plan over this CSR, built on the device and resident there (upload() only
+        records a stream): the same plan Plan.from_slices builds for the same slices and
+        tile sizes (bsfa_plan_from_dcsr)."""
         h = ctypes.c_void_p()
         _check("bsfa_plan_from_dcsr", library().bsfa_plan_from_dcsr(self._h, hq, hkv, d, ctypes.byref(h)))
         return Plan(h)
@@ -429,6 +434,15 @@ def attn_merge(o_parts, lse_parts, out=None, lse=None, stream=None):
         optrs, lptrs, n, st[0], st[1], lst, t, h, d, ctypes.byref(to),
         ctypes.c_void_p(lse.data_ptr()), _stream_handle(stream)))
     return out, lse[:, :t]
+
+
+def set_rescale_threshold(tau_log2: float):
+    """Conditional-rescale threshold of the forward (log2 units, default 8; process-wide)."""
+    _check("bsfa_set_rescale_threshold", library().bsfa_set_rescale_threshold(float(tau_log2)))
+
+
+def rescale_threshold() -> float:
+    return float(library().bsfa_get_rescale_threshold())
 
 
 def lpt_assign(costs, n_bins):

@@ -40,7 +40,7 @@
 //     the direct loads in flight into the other two tiles.
 //   * Softmax in base 2 with a single FMA for scale and shift, and conditional
 //     rescaling (FlashAttention-4 article: rescale only when needed): a row's running
-//     max moves only when its tile max exceeds it by more than tau = 8.  At head dim 64,
+//     max moves only when its tile max exceeds it by more than tau (8 unless set).  At head dim 64,
 //     where the vector work binds, the tile max itself is skipped: a step's weights are
 //     taken against the running max and checked afterwards (their sum over a lane's keys
 //     at most 2^tau), with a recomputation only for the rare step that fails.
@@ -75,8 +75,6 @@ typedef __attribute__((address_space(3))) i16x4 *lds_i16x4;
 
 constexpr int kThreads = 256;
 constexpr int kBkS = kKernelBk;          // keys per step
-constexpr float kTau = 8.0f;             // rescale threshold, log2 units
-constexpr float kRescaleSum = 256.0f;    // 2^kTau: bound on a lane's weight sum per step (lazy max)
 constexpr float kMFloor = -1.0e30f;      // finite start of the running max
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int32_t kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
@@ -371,6 +369,7 @@ template <int D>
 struct Acc {
     f32x16 o[Cfg<D>::DB];
     float m, l, lb;   // running max, fp32 weight sum (LSE), bf16-weight sum (O's normaliser)
+    float tau, rsum;  // rescale threshold (log2 units) and 2^tau (the lazy max's bound)
 };
 
 // Conditional rescale before step j (FlashAttention-4 article): each row moves its
@@ -379,7 +378,7 @@ struct Acc {
 template <int D>
 __device__ __forceinline__ void rescale_for(float mx, Acc<D> &acc)
 {
-    const bool need = mx > acc.m + kTau;
+    const bool need = mx > acc.m + acc.tau;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
         const float m_new = need ? fmaxf(acc.m, mx) : acc.m;
         const float alpha = __builtin_amdgcn_exp2f(acc.m - m_new);
@@ -485,7 +484,7 @@ __device__ __forceinline__ void step_body(char *__restrict__ k_dst, char *__rest
         // (conservatively: their sum over this lane's keys) exceeds 2^tau, or overflowed,
         // does the step take its true max, rescale the rows whose max moved by more than
         // tau and take its weights again.  Both halves of a query row see the same max.
-        if (__builtin_amdgcn_ballot_w64(!(e0 + e1 <= kRescaleSum)) != 0) {
+        if (__builtin_amdgcn_ballot_w64(!(e0 + e1 <= acc.rsum)) != 0) {
             rescale_for<D>(tile_max(cur, c), acc);
             const float nm2 = -acc.m;
 #pragma unroll
@@ -602,6 +601,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
         acc.m = kMFloor;
         acc.l = 0.f;
         acc.lb = 0.f;
+        acc.tau = a.tau;
+        acc.rsum = a.rsum;
 
         const int e0 = un[1], e1 = un[2];
         const int spe = a.bk_plan / kBkS;     // steps per CSR entry

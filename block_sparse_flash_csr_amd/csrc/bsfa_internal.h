@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <functional>
 #include <mutex>
 #include <vector>
 
@@ -81,6 +82,14 @@ struct DeviceMeta {
 struct bsfa_plan {
     int32_t sq = 0, sk = 0, hq = 0, hkv = 0, d = 0, bq = 0, bk = 0;
     int32_t n_qt = 0, n_kt = 0;
+    // A plan built over a device-compiled CSR keeps its CSR arrays (col, tag, piece_ptr,
+    // pieces, t_list) only in its device image, assembled on the device; the host holds
+    // row_ptr, t_ptr, the schedule and the launch orders.
+    bool device_built = false;
+    int64_t dev_nnz = 0, dev_npieces = 0;
+    size_t off_entries = 0, off_pieces = 0;   // byte offsets of those sections in dbuf
+    size_t nnz() const { return device_built ? (size_t)dev_nnz : col.size(); }
+    size_t npieces() const { return device_built ? (size_t)dev_npieces : pieces.size(); }
     // tile CSR
     std::vector<int32_t> row_ptr;
     std::vector<int32_t> col;
@@ -135,8 +144,20 @@ bsfa_status compile_mask(const bsfa_slice *slices, int32_t n_slices, bsfa_plan &
 // Column view of the tile CSR (for the key/value gradients) and the launch orders of the
 // gradient kernels.
 void build_transpose(bsfa_plan &p);
-// Scheduler: items, costs and the per-bin lists.
-void build_schedule(bsfa_plan &p, int n_bins_max);
+// Launch orders of the gradient kernels from row_ptr and t_ptr.
+void build_orders(bsfa_plan &p);
+// Scheduler: items, costs and the per-bin lists.  A row's cost is the per-item constant
+// plus its full and partial 64-key steps (RowSteps, per query tile); the entries' own
+// costs (EntryCosts: entries [e0, e1) of one row) are asked for only for rows that are
+// split into parts.
+struct RowSteps {
+    std::vector<int64_t> full, partial;
+};
+using EntryCosts = std::function<void(int32_t e0, int32_t e1, std::vector<double> &out)>;
+int64_t entry_steps(const bsfa_plan &p, int32_t col);
+void row_steps_host(const bsfa_plan &p, RowSteps &rs);
+void entry_costs_host(const bsfa_plan &p, int32_t e0, int32_t e1, std::vector<double> &out);
+void build_schedule(bsfa_plan &p, int n_bins_max, const RowSteps &rs, const EntryCosts &entry_costs);
 // Min-heap greedy (LPT) of the given items onto the given bins; appends (bin, item)
 // pairs in assignment order and updates the loads.
 void lpt(const std::vector<int32_t> &items, const std::vector<float> &cost,
@@ -151,6 +172,7 @@ struct FwdArgs {
     int32_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh, lse_sh;
     int32_t sq, sk, hq, hkv, n_qt, bk_plan;
     float c;  // scale * log2(e)
+    float tau, rsum;               // rescale threshold (log2 units) and 2^tau
     DeviceMeta meta;
     float *ws;                     // partial results of split rows (caller's workspace): per
                                    // slot O [128][d] then LSE [128], fp32
@@ -214,6 +236,27 @@ struct DcsrArgs {
 };
 size_t dcsr_sort_temp_bytes(int64_t n, int32_t end_bit);
 hipError_t launch_dcsr(const DcsrArgs &a, hipStream_t stream);
+
+// Device part of a plan over a device-compiled CSR (plan_dev.hip): per-row full and
+// partial 64-key steps and per-key-tile entry counts (launch_plan_counts), then the
+// entry records and the column view (launch_plan_image: a stable radix sort of the
+// entries' key tiles; end_bit covers n_kt).
+struct DevPlanArgs {
+    const int32_t *row_ptr, *col, *piece_ptr;   // the compiled CSR
+    const uint8_t *tag;
+    int32_t n_qt, n_kt, bk, sk, end_bit;
+    int64_t nnz;
+    int64_t *row_full, *row_partial;           // [n_qt]
+    int32_t *col_count;                        // [n_kt]
+    Entry *entries;                            // [nnz], in the plan's device image
+    int32_t *t_list;                           // [2 nnz], in the plan's device image
+    int32_t *iota, *keys_out, *sorted_e, *row_of;   // [nnz] scratch
+    void *temp;
+    size_t temp_bytes;
+};
+hipError_t launch_plan_counts(const DevPlanArgs &a, hipStream_t stream);
+size_t plan_sort_temp_bytes(int64_t nnz, int32_t end_bit);
+hipError_t launch_plan_image(const DevPlanArgs &a, hipStream_t stream);
 
 struct MergeArgs {
     const void *o_parts[BSFA_MERGE_MAX_PARTS];

@@ -18,6 +18,9 @@ namespace {
 
 constexpr int kBinsPerCu = 2;  // forward workgroups resident per CU (LDS and VGPR budget)
 
+// Conditional-rescale threshold of the forward's online softmax, log2 units (process-wide).
+std::atomic<float> g_rescale_tau{8.0f};
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool stride_ok(int64_t s) { return s >= 0 && (s & 7) == 0; }
 
@@ -46,21 +49,26 @@ bsfa_status check_plan_limits(size_t nnz, size_t n_pieces)
 // plan's size.
 bool plan_consistent(const bsfa_plan &p)
 {
-    const size_t nnz = p.col.size(), npc = p.pieces.size();
+    const size_t nnz = p.nnz(), npc = p.npieces();
     const int64_t n_items = (int64_t)p.hq * p.n_qt;
-    if (p.row_ptr.size() != (size_t)p.n_qt + 1 || p.tag.size() != nnz || p.piece_ptr.size() != nnz + 1) return false;
+    if (p.row_ptr.size() != (size_t)p.n_qt + 1) return false;
     if (p.row_ptr[0] != 0 || (size_t)p.row_ptr[(size_t)p.n_qt] != nnz) return false;
     for (int32_t t = 0; t < p.n_qt; ++t)
         if (p.row_ptr[(size_t)t + 1] < p.row_ptr[(size_t)t]) return false;
-    if (p.piece_ptr[0] != 0 || (size_t)p.piece_ptr[nnz] != npc) return false;
-    for (size_t e = 0; e < nnz; ++e) {
-        const int32_t np = p.piece_ptr[e + 1] - p.piece_ptr[e];
-        if (np < 0 || p.col[e] < 0 || p.col[e] >= p.n_kt) return false;
-        if (p.tag[e] == BSFA_TILE_FULL ? np != 0 : (p.tag[e] != BSFA_TILE_PARTIAL || np < 1)) return false;
+    if (!p.device_built) {
+        // the CSR arrays (a device-built plan has them only in its device image)
+        if (p.tag.size() != nnz || p.piece_ptr.size() != nnz + 1) return false;
+        if (p.piece_ptr[0] != 0 || (size_t)p.piece_ptr[nnz] != npc) return false;
+        for (size_t e = 0; e < nnz; ++e) {
+            const int32_t np = p.piece_ptr[e + 1] - p.piece_ptr[e];
+            if (np < 0 || p.col[e] < 0 || p.col[e] >= p.n_kt) return false;
+            if (p.tag[e] == BSFA_TILE_FULL ? np != 0 : (p.tag[e] != BSFA_TILE_PARTIAL || np < 1)) return false;
+        }
+        for (const Piece &pc : p.pieces)
+            if (pc.q_lo < 0 || pc.q_lo > pc.q_hi || pc.q_hi > p.sq || pc.k_lo < 0 || pc.k_lo > pc.k_hi ||
+                pc.k_hi > p.sk)
+                return false;
     }
-    for (const Piece &pc : p.pieces)
-        if (pc.q_lo < 0 || pc.q_lo > pc.q_hi || pc.q_hi > p.sq || pc.k_lo < 0 || pc.k_lo > pc.k_hi || pc.k_hi > p.sk)
-            return false;
     if ((int64_t)p.item_cost.size() != n_items || p.unit_cost.size() != p.units.size()) return false;
     const size_t n_units = p.units.size();
     for (const Unit &u : p.units) {
@@ -81,14 +89,16 @@ bool plan_consistent(const bsfa_plan &p)
     for (const Split &sp : p.splits)
         if (sp.item < 0 || sp.item >= n_items || sp.first < 0 || sp.parts < 1 || sp.first + sp.parts > p.n_slots)
             return false;
-    if (p.t_ptr.size() != (size_t)p.n_kt + 1 || p.t_list.size() != 2 * nnz || p.t_ptr[0] != 0 ||
-        (size_t)p.t_ptr[(size_t)p.n_kt] != nnz)
+    if (p.t_ptr.size() != (size_t)p.n_kt + 1 || p.t_ptr[0] != 0 || (size_t)p.t_ptr[(size_t)p.n_kt] != nnz)
         return false;
     for (int32_t t = 0; t < p.n_kt; ++t)
         if (p.t_ptr[(size_t)t + 1] < p.t_ptr[(size_t)t]) return false;
-    for (size_t i = 0; i < nnz; ++i) {
-        const int32_t qt = p.t_list[2 * i], e = p.t_list[2 * i + 1];
-        if (qt < 0 || qt >= p.n_qt || e < 0 || (size_t)e >= nnz) return false;
+    if (!p.device_built) {
+        if (p.t_list.size() != 2 * nnz) return false;
+        for (size_t i = 0; i < nnz; ++i) {
+            const int32_t qt = p.t_list[2 * i], e = p.t_list[2 * i + 1];
+            if (qt < 0 || qt >= p.n_qt || e < 0 || (size_t)e >= nnz) return false;
+        }
     }
     if ((int64_t)p.dq_order.size() != n_items || (int64_t)p.dkv_order.size() != (int64_t)p.hkv * p.n_kt) return false;
     for (int32_t it : p.dq_order)
@@ -123,7 +133,10 @@ bsfa_status finish_plan(bsfa_plan &p)
     bool oom = false;
     try {
         if (!tr.joinable()) build_transpose(p);
-        build_schedule(p, kNumCu * kBinsPerCu);
+        RowSteps rs;
+        row_steps_host(p, rs);
+        build_schedule(p, kNumCu * kBinsPerCu, rs,
+                       [&p](int32_t e0, int32_t e1, std::vector<double> &out) { entry_costs_host(p, e0, e1, out); });
     } catch (const std::bad_alloc &) {
         oom = true;
     }
@@ -174,6 +187,32 @@ size_t place(size_t &off, size_t count)
     const size_t at = off;
     off += count * sizeof(T);
     return at;
+}
+
+// Byte offsets of the sections of a plan's device image (256-byte aligned): row_ptr |
+// entries | pieces | bin_ptr | bin_items | units | splits | t_ptr | t_list | dq_order |
+// dkv_order.
+struct ImageLayout {
+    size_t row, ent, pc, bp, bi, un, sp, tp, tl, oq, ok, bytes;
+};
+
+ImageLayout image_layout(const bsfa_plan &p)
+{
+    ImageLayout L;
+    size_t off = 0;
+    L.row = place<int32_t>(off, p.row_ptr.size());
+    L.ent = place<Entry>(off, p.nnz());
+    L.pc = place<Piece>(off, p.npieces());
+    L.bp = place<int32_t>(off, p.bin_ptr.size());
+    L.bi = place<int32_t>(off, p.bin_items.size());
+    L.un = place<Unit>(off, p.units.size());
+    L.sp = place<Split>(off, p.splits.size());
+    L.tp = place<int32_t>(off, p.t_ptr.size());
+    L.tl = place<int32_t>(off, 2 * p.nnz());
+    L.oq = place<int32_t>(off, p.dq_order.size());
+    L.ok = place<int32_t>(off, p.dkv_order.size());
+    L.bytes = (off + 255) & ~size_t(255);
+    return L;
 }
 
 // Pinned host images of plan metadata, reused across uploads.  An image is taken by
@@ -449,25 +488,32 @@ bsfa_status bsfa_plan_from_blocks(const uint8_t *codes, int32_t nbq, int32_t nbk
 bsfa_status bsfa_plan_upload(bsfa_plan *p, void *stream)
 {
     if (!p) return BSFA_ERR_ARG;
+    if (p->device_built) {
+        // built on the device and resident there: nothing to copy; the stream is only
+        // remembered as one to release the buffer behind
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return BSFA_ERR_HIP;
+        if (cur != p->device) return BSFA_ERR_STATE;
+        const hipStream_t s = (hipStream_t)stream;
+        std::lock_guard<std::mutex> lk(p->streams_mu);
+        if (s != p->ustream && std::find(p->used_streams.begin(), p->used_streams.end(), s) == p->used_streams.end()) {
+            try {
+                p->used_streams.push_back(s);
+            } catch (const std::bad_alloc &) {
+                return BSFA_ERR_OOM;
+            }
+        }
+        return BSFA_OK;
+    }
     if (p->dbuf) return BSFA_ERR_STATE;
     if (!plan_consistent(*p)) return BSFA_ERR_PLAN;
     hipStream_t s = (hipStream_t)stream;
     // one image: row_ptr | entries | pieces | bin_ptr | bin_items | units | splits | column
     // view | launch orders
-    size_t off = 0;
     const size_t nnz = p->col.size();
-    const size_t o_row = place<int32_t>(off, p->row_ptr.size());
-    const size_t o_ent = place<Entry>(off, nnz);
-    const size_t o_pc = place<Piece>(off, p->pieces.size());
-    const size_t o_bp = place<int32_t>(off, p->bin_ptr.size());
-    const size_t o_bi = place<int32_t>(off, p->bin_items.size());
-    const size_t o_un = place<Unit>(off, p->units.size());
-    const size_t o_sp = place<Split>(off, p->splits.size());
-    const size_t o_tp = place<int32_t>(off, p->t_ptr.size());
-    const size_t o_tl = place<int32_t>(off, p->t_list.size());
-    const size_t o_oq = place<int32_t>(off, p->dq_order.size());
-    const size_t o_ok = place<int32_t>(off, p->dkv_order.size());
-    const size_t bytes = (off + 255) & ~size_t(255);
+    const ImageLayout L = image_layout(*p);
+    const size_t o_row = L.row, o_ent = L.ent, o_pc = L.pc, o_bp = L.bp, o_bi = L.bi, o_un = L.un, o_sp = L.sp,
+                 o_tp = L.tp, o_tl = L.tl, o_oq = L.oq, o_ok = L.ok, bytes = L.bytes;
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return BSFA_ERR_HIP;
@@ -574,10 +620,10 @@ bsfa_status bsfa_plan_get_info(const bsfa_plan *p, bsfa_plan_info *info)
     info->bk = p->bk;
     info->n_qtiles = p->n_qt;
     info->n_ktiles = p->n_kt;
-    info->nnz = (int64_t)p->col.size();
+    info->nnz = (int64_t)p->nnz();
     info->n_full = p->n_full;
     info->n_partial = p->n_partial;
-    info->n_pieces = (int64_t)p->pieces.size();
+    info->n_pieces = (int64_t)p->npieces();
     info->pairs = p->pairs;
     info->n_items = (int32_t)p->item_cost.size();
     info->n_bins = (int32_t)p->bin_ptr.size() - 1;
@@ -590,29 +636,74 @@ bsfa_status bsfa_plan_get_info(const bsfa_plan *p, bsfa_plan_info *info)
     return BSFA_OK;
 }
 
+// Entry records (and pieces) of a device-built plan, copied back from its device image
+// once the image is complete.
+static bsfa_status device_entries(const bsfa_plan &p, std::vector<Entry> &ent, std::vector<Piece> *pcs)
+{
+    try {
+        ent.resize(p.nnz());
+        if (pcs) pcs->resize(p.npieces());
+    } catch (const std::bad_alloc &) {
+        return BSFA_ERR_OOM;
+    }
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return BSFA_ERR_HIP;
+    if (cur != p.device && hipSetDevice(p.device) != hipSuccess) return BSFA_ERR_HIP;
+    bool ok = hipEventSynchronize(((DevSlot *)p.slot)->ready) == hipSuccess;
+    const uint8_t *base = (const uint8_t *)p.dbuf;
+    if (ok && !ent.empty())
+        ok = hipMemcpy(ent.data(), base + p.off_entries, ent.size() * sizeof(Entry), hipMemcpyDeviceToHost) ==
+             hipSuccess;
+    if (ok && pcs && !pcs->empty())
+        ok = hipMemcpy(pcs->data(), base + p.off_pieces, pcs->size() * sizeof(Piece), hipMemcpyDeviceToHost) ==
+             hipSuccess;
+    if (cur != p.device) (void)hipSetDevice(cur);
+    return ok ? BSFA_OK : BSFA_ERR_HIP;
+}
+
 bsfa_status bsfa_plan_export_csr(const bsfa_plan *p, int32_t *row_ptr, int32_t *col, uint8_t *tag,
                                  int64_t cap, int64_t *nnz)
 {
     if (!p || !nnz) return BSFA_ERR_ARG;
-    *nnz = (int64_t)p->col.size();
+    *nnz = (int64_t)p->nnz();
     if (cap < *nnz) return BSFA_ERR_ARG;
     if (!row_ptr || (*nnz > 0 && (!col || !tag))) return BSFA_ERR_ARG;
     std::memcpy(row_ptr, p->row_ptr.data(), p->row_ptr.size() * sizeof(int32_t));
-    if (*nnz > 0) {
-        std::memcpy(col, p->col.data(), p->col.size() * sizeof(int32_t));
-        std::memcpy(tag, p->tag.data(), p->tag.size());
+    if (*nnz == 0) return BSFA_OK;
+    if (p->device_built) {
+        std::vector<Entry> ent;
+        const bsfa_status st = device_entries(*p, ent, nullptr);
+        if (st != BSFA_OK) return st;
+        for (size_t e = 0; e < ent.size(); ++e) {
+            col[e] = ent[e].col;
+            tag[e] = (uint8_t)ent[e].tag;
+        }
+        return BSFA_OK;
     }
+    std::memcpy(col, p->col.data(), p->col.size() * sizeof(int32_t));
+    std::memcpy(tag, p->tag.data(), p->tag.size());
     return BSFA_OK;
 }
 
 bsfa_status bsfa_plan_export_pieces(const bsfa_plan *p, int32_t *piece_ptr, int32_t *pieces, int64_t cap)
 {
     if (!p || !piece_ptr) return BSFA_ERR_ARG;
-    const int64_t n = (int64_t)p->pieces.size();
+    const int64_t n = (int64_t)p->npieces();
     if (cap < n || (n > 0 && !pieces)) return BSFA_ERR_ARG;
-    std::memcpy(piece_ptr, p->piece_ptr.data(), p->piece_ptr.size() * sizeof(int32_t));
+    const Piece *src = p->pieces.data();
+    std::vector<Entry> ent;
+    std::vector<Piece> pcs;
+    if (p->device_built) {
+        const bsfa_status st = device_entries(*p, ent, &pcs);
+        if (st != BSFA_OK) return st;
+        for (size_t e = 0; e < ent.size(); ++e) piece_ptr[e] = ent[e].piece_begin;
+        piece_ptr[ent.size()] = (int32_t)n;
+        src = pcs.data();
+    } else {
+        std::memcpy(piece_ptr, p->piece_ptr.data(), p->piece_ptr.size() * sizeof(int32_t));
+    }
     for (int64_t t = 0; t < n; ++t) {
-        const Piece &pc = p->pieces[(size_t)t];
+        const Piece &pc = src[(size_t)t];
         int32_t *o = pieces + 5 * t;
         o[0] = pc.q_lo;
         o[1] = pc.q_hi;
@@ -702,11 +793,13 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     a.n_qt = p->n_qt;
     a.bk_plan = p->bk;
     a.c = scale * 1.4426950408889634f;
+    a.tau = g_rescale_tau.load(std::memory_order_relaxed);
+    a.rsum = std::exp2(a.tau);
     a.meta = p->dev;
     a.ws = p->n_slots > 0 ? (float *)workspace : nullptr;
     a.n_bins = (int32_t)p->bin_ptr.size() - 1;
-    a.n_entries = (int32_t)p->col.size();
-    a.n_pieces = (int32_t)p->pieces.size();
+    a.n_entries = (int32_t)p->nnz();
+    a.n_pieces = (int32_t)p->npieces();
     if (p->sq == 0) return BSFA_OK;
     const hipStream_t s = (hipStream_t)stream;
     if (s != p->ustream) {
@@ -811,8 +904,8 @@ bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     a.scale = scale;
     a.c = scale * 1.4426950408889634f;
     a.meta = p->dev;
-    a.n_entries = (int32_t)p->col.size();
-    a.n_pieces = (int32_t)p->pieces.size();
+    a.n_entries = (int32_t)p->nnz();
+    a.n_pieces = (int32_t)p->npieces();
     const hipStream_t s = (hipStream_t)stream;
     if (s != p->ustream) {
         std::lock_guard<std::mutex> lk(p->streams_mu);
@@ -1096,14 +1189,16 @@ bsfa_status bsfa_plan_from_dcsr(bsfa_dcsr *csr, int32_t hq, int32_t hkv, int32_t
     if (hq % hkv != 0) return BSFA_ERR_SHAPE;
     const DcsrEx *x = static_cast<const DcsrEx *>(csr);
     if ((int64_t)hq * x->n_qt >= (int64_t)1 << 31) return BSFA_ERR_ARG;
-    int cur = 0;
-    if (hipGetDevice(&cur) != hipSuccess) return BSFA_ERR_HIP;
-    if (cur != x->device) return BSFA_ERR_STATE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BSFA_ERR_HIP;
+    if (dev != x->device) return BSFA_ERR_STATE;
     bsfa_dcsr_view v;
-    bsfa_status st = bsfa_dcsr_view_get(csr, &v);
+    bsfa_status st = bsfa_dcsr_view_get(csr, &v);   // waits for the compile
     if (st != BSFA_OK) return st;
     st = check_plan_limits((size_t)v.nnz, (size_t)v.n_pieces);
     if (st != BSFA_OK) return st;
+    const hipStream_t cs = copy_stream(dev);
+    if (!cs) return BSFA_ERR_HIP;
     bsfa_plan *p = new (std::nothrow) bsfa_plan;
     if (!p) return BSFA_ERR_OOM;
     p->sq = x->sq;
@@ -1115,38 +1210,181 @@ bsfa_status bsfa_plan_from_dcsr(bsfa_dcsr *csr, int32_t hq, int32_t hkv, int32_t
     p->bk = x->bk;
     p->n_qt = x->n_qt;
     p->n_kt = x->n_kt;
-    try {
-        p->row_ptr.resize((size_t)p->n_qt + 1);
-        p->col.resize((size_t)v.nnz);
-        p->tag.resize((size_t)v.nnz);
-        p->piece_ptr.resize((size_t)v.nnz + 1);
-        p->pieces.resize((size_t)v.n_pieces);
-    } catch (const std::bad_alloc &) {
-        delete p;
-        return BSFA_ERR_OOM;
-    }
-    // the device arrays are laid out as the host compiler's (Piece is the same 32-byte record)
-    bool ok = hipMemcpy(p->row_ptr.data(), v.row_ptr, p->row_ptr.size() * 4, hipMemcpyDeviceToHost) == hipSuccess;
-    ok = ok && hipMemcpy(p->piece_ptr.data(), v.piece_ptr, p->piece_ptr.size() * 4, hipMemcpyDeviceToHost) ==
-                   hipSuccess;
-    if (v.nnz > 0) {
-        ok = ok && hipMemcpy(p->col.data(), v.col, p->col.size() * 4, hipMemcpyDeviceToHost) == hipSuccess;
-        ok = ok && hipMemcpy(p->tag.data(), v.tag, p->tag.size(), hipMemcpyDeviceToHost) == hipSuccess;
-    }
-    if (v.n_pieces > 0)
-        ok = ok && hipMemcpy(p->pieces.data(), v.pieces, p->pieces.size() * sizeof(Piece), hipMemcpyDeviceToHost) ==
-                       hipSuccess;
-    if (!ok) {
-        delete p;
-        return BSFA_ERR_HIP;
-    }
+    p->device_built = true;
+    p->dev_nnz = v.nnz;
+    p->dev_npieces = v.n_pieces;
     p->n_full = v.n_full;
     p->n_partial = v.n_partial;
     p->pairs = v.pairs;
-    st = finish_plan(*p);
-    if (st != BSFA_OK) {
+    const int64_t nnz = v.nnz;
+    int end_bit = 1;
+    while ((1ll << end_bit) < (int64_t)std::max(p->n_kt, 1)) ++end_bit;
+
+    // device scratch (stream-ordered, freed behind the image's kernels): per-row steps,
+    // per-key-tile counts, then the sort's arrays
+    const size_t sort_temp = nnz > 0 ? plan_sort_temp_bytes(nnz, end_bit) : 0;
+    size_t off = 0;
+    const size_t o_full = place<int64_t>(off, (size_t)p->n_qt), o_part = place<int64_t>(off, (size_t)p->n_qt);
+    const size_t o_cnt = place<int32_t>(off, (size_t)p->n_kt);
+    const size_t o_iota = place<int32_t>(off, (size_t)nnz), o_keys = place<int32_t>(off, (size_t)nnz);
+    const size_t o_sorted = place<int32_t>(off, (size_t)nnz), o_rowof = place<int32_t>(off, (size_t)nnz);
+    const size_t o_temp = place<uint8_t>(off, sort_temp);
+    const size_t scratch_bytes = off + 256;
+    void *scratch = nullptr;
+    if (hipMallocAsync(&scratch, scratch_bytes, cs) != hipSuccess) {
         delete p;
-        return st;
+        return BSFA_ERR_OOM;
+    }
+    uint8_t *sb = (uint8_t *)scratch;
+    DevPlanArgs a{};
+    a.row_ptr = v.row_ptr;
+    a.col = v.col;
+    a.piece_ptr = v.piece_ptr;
+    a.tag = v.tag;
+    a.n_qt = p->n_qt;
+    a.n_kt = p->n_kt;
+    a.bk = p->bk;
+    a.sk = p->sk;
+    a.end_bit = end_bit;
+    a.nnz = nnz;
+    a.row_full = (int64_t *)(sb + o_full);
+    a.row_partial = (int64_t *)(sb + o_part);
+    a.col_count = (int32_t *)(sb + o_cnt);
+    a.iota = (int32_t *)(sb + o_iota);
+    a.keys_out = (int32_t *)(sb + o_keys);
+    a.sorted_e = (int32_t *)(sb + o_sorted);
+    a.row_of = (int32_t *)(sb + o_rowof);
+    a.temp = sb + o_temp;
+    a.temp_bytes = sort_temp;
+    auto fail = [&](bsfa_status code) {
+        (void)hipFreeAsync(scratch, cs);
+        delete p;
+        return code;
+    };
+
+    // 1. counts on the device; the host receives row_ptr and n_qt + n_kt counts
+    RowSteps rs;
+    std::vector<int32_t> col_count;
+    try {
+        p->row_ptr.resize((size_t)p->n_qt + 1);
+        rs.full.resize((size_t)p->n_qt);
+        rs.partial.resize((size_t)p->n_qt);
+        col_count.resize((size_t)p->n_kt);
+    } catch (const std::bad_alloc &) {
+        return fail(BSFA_ERR_OOM);
+    }
+    bool ok = launch_plan_counts(a, cs) == hipSuccess;
+    ok = ok && hipMemcpyAsync(p->row_ptr.data(), v.row_ptr, p->row_ptr.size() * 4, hipMemcpyDeviceToHost, cs) ==
+                   hipSuccess;
+    if (p->n_qt > 0) {
+        ok = ok && hipMemcpyAsync(rs.full.data(), a.row_full, rs.full.size() * 8, hipMemcpyDeviceToHost, cs) ==
+                       hipSuccess;
+        ok = ok && hipMemcpyAsync(rs.partial.data(), a.row_partial, rs.partial.size() * 8, hipMemcpyDeviceToHost,
+                                  cs) == hipSuccess;
+    }
+    if (p->n_kt > 0)
+        ok = ok && hipMemcpyAsync(col_count.data(), a.col_count, col_count.size() * 4, hipMemcpyDeviceToHost, cs) ==
+                       hipSuccess;
+    ok = ok && hipStreamSynchronize(cs) == hipSuccess;
+    if (!ok) return fail(BSFA_ERR_HIP);
+
+    // 2. column offsets, schedule and launch orders on the host (sizes n_qt, n_kt, items);
+    //    a split row's entry costs come from its CSR entries (copied for that row only)
+    try {
+        p->t_ptr.assign((size_t)p->n_kt + 1, 0);
+        for (int32_t kt = 0; kt < p->n_kt; ++kt) p->t_ptr[(size_t)kt + 1] = p->t_ptr[kt] + col_count[kt];
+        bool copy_ok = true;
+        build_schedule(*p, kNumCu * kBinsPerCu, rs, [&](int32_t e0, int32_t e1, std::vector<double> &outc) {
+            std::vector<int32_t> c((size_t)(e1 - e0));
+            std::vector<uint8_t> t((size_t)(e1 - e0));
+            copy_ok = copy_ok && hipMemcpy(c.data(), v.col + e0, c.size() * 4, hipMemcpyDeviceToHost) == hipSuccess &&
+                      hipMemcpy(t.data(), v.tag + e0, t.size(), hipMemcpyDeviceToHost) == hipSuccess;
+            outc.resize(c.size());
+            for (size_t i = 0; i < c.size(); ++i)
+                outc[i] = (double)entry_steps(*p, c[i]) * bsfa_tile_cost(t[i], kCostPartial);
+        });
+        if (!copy_ok) return fail(BSFA_ERR_HIP);
+        build_orders(*p);
+    } catch (const std::bad_alloc &) {
+        return fail(BSFA_ERR_OOM);
+    }
+
+    // 3. the device image: the host-built sections go through one compact pinned image,
+    //    the CSR sections (entries, pieces, column view) are written on the device
+    const ImageLayout L = image_layout(*p);
+    struct Sec {
+        size_t at;          // offset in the device image
+        const void *src;
+        size_t bytes;
+        size_t staged = 0;  // offset in the compact host image
+    };
+    Sec secs[] = {{L.row, p->row_ptr.data(), p->row_ptr.size() * 4},
+                  {L.bp, p->bin_ptr.data(), p->bin_ptr.size() * 4},
+                  {L.bi, p->bin_items.data(), p->bin_items.size() * 4},
+                  {L.un, p->units.data(), p->units.size() * sizeof(Unit)},
+                  {L.sp, p->splits.data(), p->splits.size() * sizeof(Split)},
+                  {L.tp, p->t_ptr.data(), p->t_ptr.size() * 4},
+                  {L.oq, p->dq_order.data(), p->dq_order.size() * 4},
+                  {L.ok, p->dkv_order.data(), p->dkv_order.size() * 4}};
+    size_t staged = 0;
+    for (Sec &x : secs) x.staged = place<uint8_t>(staged, x.bytes);
+    Staging *stg = nullptr;
+    st = staging_acquire(dev, staged + 256, &stg);
+    if (st != BSFA_OK) return fail(st);
+    uint8_t *h = (uint8_t *)stg->host;
+    for (const Sec &x : secs)
+        if (x.bytes) std::memcpy(h + x.staged, x.src, x.bytes);
+    DevSlot *slot = nullptr;
+    st = dev_acquire(dev, L.bytes, &slot);
+    if (st != BSFA_OK) {
+        staging_release_now(stg);
+        return fail(st);
+    }
+    uint8_t *base = (uint8_t *)slot->ptr;
+    for (const Sec &x : secs)
+        ok = ok && (x.bytes == 0 ||
+                    hipMemcpyAsync(base + x.at, h + x.staged, x.bytes, hipMemcpyHostToDevice, cs) == hipSuccess);
+    if (ok && v.n_pieces > 0)
+        ok = hipMemcpyAsync(base + L.pc, v.pieces, (size_t)v.n_pieces * sizeof(Piece), hipMemcpyDeviceToDevice, cs) ==
+             hipSuccess;
+    a.entries = (Entry *)(base + L.ent);
+    a.t_list = (int32_t *)(base + L.tl);
+    ok = ok && launch_plan_image(a, cs) == hipSuccess;
+    ok = ok && hipEventRecord(stg->copied, cs) == hipSuccess && hipEventRecord(slot->ready, cs) == hipSuccess;
+    // the image's kernels and copies read the compiled CSR's buffer: its completion event
+    // now stands behind them, so destroying the CSR waits for them
+    ok = ok && hipEventRecord(csr->done, cs) == hipSuccess;
+    (void)hipFreeAsync(scratch, cs);
+    if (!ok) {
+        (void)hipStreamSynchronize(cs);
+        std::vector<hipStream_t> rel{cs};
+        dev_release(slot, rel);
+        staging_release_now(stg);
+        delete p;
+        return BSFA_ERR_HIP;
+    }
+    staging_in_flight(stg);
+    p->dev.row_ptr = (const int32_t *)(base + L.row);
+    p->dev.entries = (const Entry *)(base + L.ent);
+    p->dev.pieces = (const Piece *)(base + L.pc);
+    p->dev.bin_ptr = (const int32_t *)(base + L.bp);
+    p->dev.bin_items = (const int32_t *)(base + L.bi);
+    p->dev.units = (const Unit *)(base + L.un);
+    p->dev.splits = (const Split *)(base + L.sp);
+    p->dev.t_ptr = (const int32_t *)(base + L.tp);
+    p->dev.t_list = (const int32_t *)(base + L.tl);
+    p->dev.dq_order = (const int32_t *)(base + L.oq);
+    p->dev.dkv_order = (const int32_t *)(base + L.ok);
+    p->off_entries = L.ent;
+    p->off_pieces = L.pc;
+    p->dbuf = base;
+    p->slot = slot;
+    p->device = dev;
+    p->ustream = cs;
+    if (!plan_consistent(*p)) {
+        // an internal error: the metadata must never reach a kernel
+        bsfa_plan_destroy(p);
+        return BSFA_ERR_PLAN;
     }
     *out = p;
     return BSFA_OK;
@@ -1162,6 +1400,15 @@ void bsfa_dcsr_destroy(bsfa_dcsr *c)
     if (c->buf) (void)hipFree(c->buf);
     delete static_cast<DcsrEx *>(c);
 }
+
+bsfa_status bsfa_set_rescale_threshold(float tau_log2)
+{
+    if (!(tau_log2 >= 0.f && tau_log2 <= 64.f)) return BSFA_ERR_ARG;
+    g_rescale_tau.store(tau_log2, std::memory_order_relaxed);
+    return BSFA_OK;
+}
+
+float bsfa_get_rescale_threshold(void) { return g_rescale_tau.load(std::memory_order_relaxed); }
 
 const char *bsfa_status_str(bsfa_status s)
 {

@@ -243,7 +243,11 @@ void build_transpose(bsfa_plan &p)
             p.t_list[2 * (size_t)at] = qt;
             p.t_list[2 * (size_t)at + 1] = e;
         }
+    build_orders(p);
+}
 
+void build_orders(bsfa_plan &p)
+{
     // Launch orders of the gradient kernels.  A workgroup's work is about its number of
     // CSR entries (times the query heads of a key/value head for dK/dV), so items run
     // longest first ([MA] Dispatch Solver: greedy, heaviest first).  The hardware hands

@@ -75,25 +75,38 @@ void lpt(const std::vector<int32_t> &items, const std::vector<float> &cost,
     lpt_sorted(order, cost, bins, assign, load);
 }
 
-void build_schedule(bsfa_plan &p, int n_bins_max)
+// 64-key steps of an entry of key tile col.
+int64_t entry_steps(const bsfa_plan &p, int32_t col)
+{
+    const int64_t c0 = (int64_t)col * p.bk;
+    const int64_t keys = std::min<int64_t>(c0 + p.bk, p.sk) - c0;
+    return (keys + kKernelBk - 1) / kKernelBk;
+}
+
+void row_steps_host(const bsfa_plan &p, RowSteps &rs)
+{
+    rs.full.assign((size_t)p.n_qt, 0);
+    rs.partial.assign((size_t)p.n_qt, 0);
+    for (int32_t qt = 0; qt < p.n_qt; ++qt)
+        for (int32_t e = p.row_ptr[qt]; e < p.row_ptr[(size_t)qt + 1]; ++e)
+            (p.tag[e] == BSFA_TILE_FULL ? rs.full : rs.partial)[qt] += entry_steps(p, p.col[e]);
+}
+
+void entry_costs_host(const bsfa_plan &p, int32_t e0, int32_t e1, std::vector<double> &out)
+{
+    out.resize((size_t)(e1 - e0));
+    for (int32_t e = e0; e < e1; ++e)
+        out[(size_t)(e - e0)] = (double)entry_steps(p, p.col[e]) * bsfa_tile_cost(p.tag[e], kCostPartial);
+}
+
+void build_schedule(bsfa_plan &p, int n_bins_max, const RowSteps &rs, const EntryCosts &entry_costs)
 {
     const int32_t n_items = p.hq * p.n_qt;
-    const size_t nnz = p.col.size();
-    // cost of each entry: its 64-key steps weighted by tag; of a row: the per-item
-    // constant plus its entries (the same for every head)
-    std::vector<double> ecost(nnz);
-    for (size_t e = 0; e < nnz; ++e) {
-        const int64_t c0 = (int64_t)p.col[e] * p.bk;
-        const int64_t keys = std::min<int64_t>(c0 + p.bk, p.sk) - c0;
-        const double steps = (double)((keys + kKernelBk - 1) / kKernelBk);
-        ecost[e] = steps * bsfa_tile_cost(p.tag[e], kCostPartial);
-    }
+    // cost of a row: the per-item constant plus its 64-key steps weighted by tag (the
+    // same for every head); entries' own costs are needed only to cut split rows
     std::vector<double> row_cost((size_t)p.n_qt, 0.0);
-    for (int32_t qt = 0; qt < p.n_qt; ++qt) {
-        double c = kCostItem;
-        for (int32_t e = p.row_ptr[qt]; e < p.row_ptr[(size_t)qt + 1]; ++e) c += ecost[e];
-        row_cost[qt] = c;
-    }
+    for (int32_t qt = 0; qt < p.n_qt; ++qt)
+        row_cost[qt] = kCostItem + (double)rs.full[qt] + (double)rs.partial[qt] * kCostPartial;
     p.item_cost.assign((size_t)n_items, 0.f);
     double total = 0.0;
     for (int32_t h = 0; h < p.hq; ++h)
@@ -110,7 +123,8 @@ void build_schedule(bsfa_plan &p, int n_bins_max)
     std::vector<int32_t> parts((size_t)p.n_qt, 1);
     std::vector<int32_t> cut_ptr((size_t)p.n_qt + 1, 0);   // into cuts
     std::vector<int32_t> cuts;                               // entry boundaries per row
-    std::vector<double> part_cost;                           // per (row, part)
+    std::vector<double> ec;                                  // entry costs of one split row
+    std::vector<std::pair<int32_t, std::vector<double>>> split_costs;   // (row, its entry costs)
     for (int32_t qt = 0; qt < p.n_qt; ++qt) {
         const int32_t e0 = p.row_ptr[qt], e1 = p.row_ptr[(size_t)qt + 1];
         int32_t np = 1;
@@ -119,16 +133,20 @@ void build_schedule(bsfa_plan &p, int n_bins_max)
         parts[qt] = np;
         cut_ptr[(size_t)qt + 1] = cut_ptr[qt] + np;
         cuts.push_back(e0);
-        const double work = row_cost[qt] - kCostItem;
-        double acc = 0.0;
-        int32_t e = e0;
-        for (int32_t k = 1; k < np; ++k) {
-            // end of part k-1: first entry where the running cost reaches k/np of the
-            // row, leaving at least one entry for each later part
-            const double goal = work * k / np;
-            while (e < e1 - (np - k) && acc + ecost[e] * 0.5 < goal) acc += ecost[e++];
-            if (e == cuts.back()) acc += ecost[e++];
-            cuts.push_back(e);
+        if (np > 1) {
+            entry_costs(e0, e1, ec);
+            const double work = row_cost[qt] - kCostItem;
+            double acc = 0.0;
+            int32_t e = e0;
+            for (int32_t k = 1; k < np; ++k) {
+                // end of part k-1: first entry where the running cost reaches k/np of the
+                // row, leaving at least one entry for each later part
+                const double goal = work * k / np;
+                while (e < e1 - (np - k) && acc + ec[(size_t)(e - e0)] * 0.5 < goal) acc += ec[(size_t)(e++ - e0)];
+                if (e == cuts.back()) acc += ec[(size_t)(e++ - e0)];
+                cuts.push_back(e);
+            }
+            split_costs.emplace_back(qt, ec);
         }
         cuts.push_back(e1);
     }
@@ -156,13 +174,23 @@ void build_schedule(bsfa_plan &p, int n_bins_max)
     p.unit_cost.assign((size_t)n_units, 0.f);
     p.splits.clear();
     std::vector<float> rk_cost((size_t)upr);   // cost of (row, part) = of its unit in any head
-    for (int32_t qt = 0; qt < p.n_qt; ++qt)
-        for (int32_t k = 0; k < parts[qt]; ++k) {
-            const int32_t eb = cuts[(size_t)cut_ptr[qt] + k], ee = cuts[(size_t)cut_ptr[qt] + k + 1];
-            double c = kCostItem;
-            for (int32_t e = eb; e < ee; ++e) c += ecost[e];
-            rk_cost[(size_t)row_base[qt] + k] = (float)c;
+    {
+        size_t si = 0;
+        for (int32_t qt = 0; qt < p.n_qt; ++qt) {
+            if (parts[qt] == 1) {
+                rk_cost[(size_t)row_base[qt]] = (float)row_cost[qt];
+                continue;
+            }
+            const std::vector<double> &rc = split_costs[si++].second;
+            const int32_t e0 = p.row_ptr[qt];
+            for (int32_t k = 0; k < parts[qt]; ++k) {
+                const int32_t eb = cuts[(size_t)cut_ptr[qt] + k], ee = cuts[(size_t)cut_ptr[qt] + k + 1];
+                double c = kCostItem;
+                for (int32_t e = eb; e < ee; ++e) c += rc[(size_t)(e - e0)];
+                rk_cost[(size_t)row_base[qt] + k] = (float)c;
+            }
         }
+    }
     for (int32_t h = 0; h < p.hq; ++h)
         for (int32_t qt = 0; qt < p.n_qt; ++qt) {
             const int32_t item = h * p.n_qt + qt;

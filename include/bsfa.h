@@ -332,15 +332,35 @@ bsfa_status bsfa_dcsr_export(bsfa_dcsr *csr, int32_t *row_ptr, int32_t *col, uin
 void bsfa_dcsr_destroy(bsfa_dcsr *csr);
 
 /* A plan over a device-compiled tile CSR ([MA]: block-sparse mask generation without a
- * dense mask, CSR mask metadata driving the kernels): waits for the compile, copies its
- * CSR to the host and builds the column view and the schedule exactly as
- * bsfa_plan_create does from the same slices and tile sizes, so the plan (CSR, pieces,
- * schedule, launch orders) equals that plan field for field.  hq, hkv, d as for
- * bsfa_plan_create; the extents and tile sizes are those csr was compiled with.  csr
- * stays owned by the caller and may be destroyed afterwards.  The current device must
- * be the one csr was built on.  Errors: BSFA_ERR_ARG, BSFA_ERR_SHAPE (hq % hkv),
- * BSFA_ERR_STATE (another current device), BSFA_ERR_OOM, BSFA_ERR_HIP. */
+ * dense mask, CSR mask metadata driving the kernels), built where the CSR is: the GPU
+ * counts each query tile's full and partial steps and each key tile's entries, the host
+ * receives only those n_qtiles + n_ktiles counts (and row_ptr) and builds the min-heap
+ * schedule and the gradient launch orders from them (a row split into parts also has its
+ * own entries copied back), and the plan's device image (entry records, pieces, the
+ * column view by a stable sort of the entries' key tiles) is assembled on the GPU.  The
+ * plan equals the one bsfa_plan_create builds from the same slices and tile sizes field
+ * for field (CSR, pieces, schedule, units, launch orders), so the forward and backward
+ * outputs are bit-identical.  It is resident on the current device from the start:
+ * bsfa_plan_upload on it copies nothing and only records its stream as one to release the
+ * buffer behind; launches are ordered after the image's assembly (an internal stream) as
+ * after an upload.  The exports copy its CSR back from the device image.  hq, hkv, d as
+ * for bsfa_plan_create; the extents and tile sizes are those csr was compiled with.  csr
+ * stays owned by the caller and may be destroyed afterwards.  The current device must be
+ * the one csr was built on.  Errors: BSFA_ERR_ARG, BSFA_ERR_SHAPE (hq % hkv),
+ * BSFA_ERR_STATE (another current device), BSFA_ERR_UNSUPPORTED (plan limits),
+ * BSFA_ERR_OOM, BSFA_ERR_HIP, BSFA_ERR_PLAN (internal inconsistency). */
 bsfa_status bsfa_plan_from_dcsr(bsfa_dcsr *csr, int32_t hq, int32_t hkv, int32_t d, bsfa_plan **out);
+
+/* Threshold of the forward's conditional rescaling ([F4] "three techniques": rescale the
+ * running sums only when needed): a row's running max moves only when a tile's maximum
+ * scaled score exceeds it by more than tau_log2 (log2 units); until then the tile's
+ * weights are taken against the old max and may reach 2^tau.  Results equal those of any
+ * other threshold up to rounding; 0 moves the max whenever it grows.  Default 8.
+ * Process-wide, read when a forward launch is enqueued (launches already enqueued keep
+ * theirs).  Errors: BSFA_ERR_ARG unless 0 <= tau_log2 <= 64 (weights up to 2^64 keep the
+ * fp32 sums finite). */
+bsfa_status bsfa_set_rescale_threshold(float tau_log2);
+float bsfa_get_rescale_threshold(void);
 
 const char *bsfa_status_str(bsfa_status status);
 

@@ -181,6 +181,22 @@ def test_merge_binding_rejects_strided_head_dim_and_short_lse():
         api.attn_merge(parts, short)
 
 
+def test_rescale_threshold_setting():
+    """The conditional-rescale threshold accepts 0..64 (log2 units) and refuses the rest."""
+    lib = api.library()
+    assert api.rescale_threshold() == 8.0
+    try:
+        for bad in (-0.5, 64.5, float("nan"), float("inf")):
+            assert lib.bsfa_set_rescale_threshold(bad) == 1
+        assert api.rescale_threshold() == 8.0
+        api.set_rescale_threshold(0.0)
+        assert api.rescale_threshold() == 0.0
+        api.set_rescale_threshold(64.0)
+        assert api.rescale_threshold() == 64.0
+    finally:
+        api.set_rescale_threshold(8.0)
+
+
 def test_merge_rejects_bad_arguments():
     lib = api.library()
     t = api.Tensor(ctypes.c_void_p(16), 1024, 128)

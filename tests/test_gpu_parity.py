@@ -120,6 +120,35 @@ def test_large_logits_exercise_rescale(d):
                f"steep max full d={d}")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_rescale_threshold_zero_equals_default(d):
+    """The conditional rescale changes only rounding: with tau = 0 (the max moves whenever
+    it grows) and the default tau = 8 the outputs both meet the oracle's tolerance and
+    agree with each other to a few bf16 units."""
+    import torch
+    rng = np.random.default_rng(90 + d)
+    sq, sk = 600, 700
+    slices = W.random_slices(rng, sq, sk, 5) + [(0, sq, 0, sk, 1)]
+    qb, kb, vb = W.random_inputs(rng, sq, sk, 3, 1, d)
+    kf = W.bf16_to_f32(kb).copy()      # maxima that grow along the keys
+    kf += np.linspace(0, 10, sk, dtype=np.float32)[:, None, None] * np.sign(
+        W.bf16_to_f32(qb).mean(axis=0, keepdims=True)[:, :1])
+    kb = W.bf16_bits(kf)
+    o_ref, lse_ref = oracle.attn_fwd(qb, kb, vb, slices, 1.0 / np.sqrt(d))
+    outs = {}
+    try:
+        for tau in (0.0, 8.0):
+            api.set_rescale_threshold(tau)
+            o, lse = run_fwd(qb, kb, vb, slices, 1.0 / np.sqrt(d), sq, sk, 3, 1, d)
+            compare(o, lse.T, o_ref, lse_ref.T, f"tau={tau} d={d}")
+            outs[tau] = (o, lse)
+    finally:
+        api.set_rescale_threshold(8.0)
+    assert float(np.max(np.abs(outs[0.0][0] - outs[8.0][0]))) <= 1.6e-2
+    fin = np.isfinite(outs[8.0][1])
+    assert float(np.max(np.abs(outs[0.0][1][fin] - outs[8.0][1][fin]))) <= 1e-4
+
+
 class OutputFormatBreach(AssertionError):
     """The 1e-2 bar fails only by the bf16 output format: rounding the exact O to bf16
     alone already exceeds it."""
