@@ -425,8 +425,9 @@ COUNTER_ORDER = ((1, 20), (2, 20), (3, 20), (4, 5), (5, 5))
 def counter_pass(api, W):
     """Fixed launch sequence for hardware-counter runs: for each workload in
     COUNTER_ORDER, its forward launched that many times back to back (workload 5: the
-    8 chunk forwards and the merge, repeated).  No other forward or merge kernel runs,
-    so a counter file maps onto workloads by dispatch order and kernel name."""
+    8 chunk forwards and the merge, repeated), and after workload 2 its backward 5 times.
+    No other forward or merge kernel runs, so a counter file maps onto workloads by
+    dispatch order and kernel name."""
     import torch
     stream = torch.cuda.current_stream()
     for cfg, reps in COUNTER_ORDER:
@@ -454,6 +455,14 @@ def counter_pass(api, W):
                 api.attn_fwd(q, k, v, plans[0], w.scale, out=o, lse=lse, stream=stream)
         torch.cuda.synchronize()
         log(f"counter pass: workload {cfg} ({w.name}) x {reps}")
+        if cfg == 2:
+            # the backward of the headline workload (D, dQ and dK/dV kernels) x 5
+            g = api.to_device_bf16(W.random_grad(np.random.default_rng(2002), w.sq, w.hq, w.d))
+            for _ in range(5):
+                api.attn_bwd(q, k, v, g, lse, plans[0], w.scale, stream=stream)
+            torch.cuda.synchronize()
+            log(f"counter pass: backward of workload {cfg} x 5")
+            del g
         for p in plans:
             p.close()
         del q, k, v
