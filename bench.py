@@ -322,7 +322,9 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
         host_ms = (time.perf_counter() - t0) * 1e3
         nnz = hp.info()["nnz"]
         hp.close()
-        api.DeviceCsr(sl, s_, s_).close()      # warm (first-use costs)
+        wc = api.DeviceCsr(sl, s_, s_)          # warm (first-use costs: module loads, pools)
+        wc.plan(16, 16, 128).close()
+        wc.close()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
