@@ -233,11 +233,15 @@ inline unsigned grid_of(int64_t n) { return (unsigned)((n + kThreadsDev - 1) / k
 
 size_t dcsr_sort_temp_bytes(int64_t n, int32_t end_bit)
 {
-    size_t a = 0, b = 0, c = 0;
-    hipcub::DeviceRadixSort::SortKeys(nullptr, a, (const uint64_t *)nullptr, (uint64_t *)nullptr, (int)n, 0, end_bit);
-    hipcub::DeviceScan::ExclusiveSum(nullptr, b, (const int32_t *)nullptr, (int32_t *)nullptr, (int)n);
-    c = std::max(a, b);
-    return c;
+    // a failed query leaves 0: the sort or scan itself then fails and is reported
+    size_t a = 0, b = 0;
+    if (hipcub::DeviceRadixSort::SortKeys(nullptr, a, (const uint64_t *)nullptr, (uint64_t *)nullptr, (int)n, 0,
+                                          end_bit) != hipSuccess)
+        return 0;
+    if (hipcub::DeviceScan::ExclusiveSum(nullptr, b, (const int32_t *)nullptr, (int32_t *)nullptr, (int)n) !=
+        hipSuccess)
+        return 0;
+    return std::max(a, b);
 }
 
 hipError_t launch_dcsr(const DcsrArgs &a, hipStream_t stream)

@@ -115,9 +115,12 @@ hipError_t launch_plan_counts(const DevPlanArgs &a, hipStream_t stream)
 
 size_t plan_sort_temp_bytes(int64_t nnz, int32_t end_bit)
 {
+    // a failed query leaves 0: the sort itself then fails and is reported
     size_t t = 0;
-    hipcub::DeviceRadixSort::SortPairs(nullptr, t, (const int32_t *)nullptr, (int32_t *)nullptr,
-                                       (const int32_t *)nullptr, (int32_t *)nullptr, (int)nnz, 0, end_bit);
+    if (hipcub::DeviceRadixSort::SortPairs(nullptr, t, (const int32_t *)nullptr, (int32_t *)nullptr,
+                                           (const int32_t *)nullptr, (int32_t *)nullptr, (int)nnz, 0, end_bit) !=
+        hipSuccess)
+        return 0;
     return t;
 }
 
