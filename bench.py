@@ -347,6 +347,32 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
         log(f"mask compile {name}: host plan {host_ms:.1f} ms, device CSR {dev_ms:.2f} ms "
             f"(stream {e0.elapsed_time(e1):.2f} ms), plan from device CSR {dplan_ms:.1f} ms, nnz {nnz}")
         dc.close()
+        if name.startswith("strided_blocks"):
+            # the same mask as its block-code map (blocks = tiles), compiled on the device
+            # without slices, and the host plan from the map
+            codes = W.strided_block_codes(s_ // 128, 8)
+            t0 = time.perf_counter()
+            api.Plan.from_blocks(codes, 128, 128, s_, s_, 16, 16, 128).close()
+            host_b_ms = (time.perf_counter() - t0) * 1e3
+            wc = api.DeviceCsr.from_blocks(codes, s_, s_)
+            wc.plan(16, 16, 128).close()
+            wc.close()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            dc = api.DeviceCsr.from_blocks(codes, s_, s_, stream=stream)
+            v = dc.view()
+            dev_b_ms = (time.perf_counter() - t0) * 1e3
+            assert v["nnz"] == nnz
+            t0 = time.perf_counter()
+            dp = dc.plan(16, 16, 128)
+            torch.cuda.synchronize()
+            dplan_b_ms = dev_b_ms + (time.perf_counter() - t0) * 1e3
+            dp.close()
+            dc.close()
+            mc[name].update({"host_plan_from_block_map_ms": host_b_ms, "device_csr_from_block_map_ms": dev_b_ms,
+                             "plan_from_device_block_map_ms": dplan_b_ms})
+            log(f"mask compile {name} as a {codes.shape[0]}x{codes.shape[1]} block map: host plan {host_b_ms:.1f} ms, "
+                f"device CSR {dev_b_ms:.2f} ms, plan from it {dplan_b_ms:.1f} ms")
     out["mask_compile"] = mc
 
     # Few query rows against a long context (a prefill chunk): 1 query tile x 32 heads is

@@ -93,6 +93,7 @@ def library():
                                                                  P, P, P, P, P]
     lib.bsfa_plan_export_pieces.argtypes = [P, P, P, I64]
     lib.bsfa_dcsr_build.argtypes = [P, I32, I32, I32, I32, I32, P, PP]
+    lib.bsfa_dcsr_build_blocks.argtypes = [P, I32, I32, I32, I32, I32, I32, P, PP]
     lib.bsfa_dcsr_view_get.argtypes = [P, ctypes.POINTER(DcsrView)]
     lib.bsfa_dcsr_export.argtypes = [P, P, P, P, P, P, I64, I64]
     lib.bsfa_dcsr_destroy.argtypes = [P]
@@ -109,7 +110,7 @@ def library():
                  "bsfa_plan_export_schedule", "bsfa_plan_export_units", "bsfa_attn_fwd",
                  "bsfa_attn_fwd_noalloc",
                  "bsfa_attn_merge", "bsfa_attn_bwd", "bsfa_plan_export_pieces", "bsfa_dcsr_build",
-                 "bsfa_dcsr_view_get", "bsfa_dcsr_export", "bsfa_plan_from_dcsr"):
+                 "bsfa_dcsr_build_blocks", "bsfa_dcsr_view_get", "bsfa_dcsr_export", "bsfa_plan_from_dcsr"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -159,6 +160,20 @@ class DeviceCsr:
         _check("bsfa_dcsr_build", library().bsfa_dcsr_build(_ptr(arr), len(arr), sq, sk, bq, bk,
                                                              _stream_handle(stream), ctypes.byref(h)))
         self._h = h
+
+    @classmethod
+    def from_blocks(cls, codes, sq, sk, bq=128, bk=128, stream=None) -> "DeviceCsr":
+        """Tile CSR of a block-code map over (bq x bk) blocks (0 empty, 1 full, 2 causal),
+        compiled on the GPU (bsfa_dcsr_build_blocks): the CSR Plan.from_blocks builds
+        with blocks equal to tiles."""
+        c = np.ascontiguousarray(codes, dtype=np.uint8)
+        assert c.ndim == 2
+        h = ctypes.c_void_p()
+        _check("bsfa_dcsr_build_blocks", library().bsfa_dcsr_build_blocks(
+            _ptr(c), c.shape[0], c.shape[1], sq, sk, bq, bk, _stream_handle(stream), ctypes.byref(h)))
+        obj = cls.__new__(cls)
+        obj._h = h
+        return obj
 
     def view(self) -> dict:
         v = DcsrView()

@@ -1127,6 +1127,142 @@ bsfa_status bsfa_dcsr_build(const bsfa_slice *slices, int32_t n_slices, int32_t 
     return BSFA_OK;
 }
 
+bsfa_status bsfa_dcsr_build_blocks(const uint8_t *codes, int32_t nbq, int32_t nbk, int32_t sq, int32_t sk,
+                                   int32_t bq, int32_t bk, void *stream, bsfa_dcsr **out)
+{
+    if (!out) return BSFA_ERR_ARG;
+    *out = nullptr;
+    if (nbq < 0 || nbk < 0 || sq < 0 || sk < 0 || bq <= 0 || bk <= 0 || sq >= (1 << 30) || sk >= (1 << 30))
+        return BSFA_ERR_ARG;
+    const int64_t n_codes = (int64_t)nbq * nbk;
+    if (n_codes > 0 && !codes) return BSFA_ERR_ARG;
+    const int32_t n_qt = (int32_t)(((int64_t)sq + bq - 1) / bq), n_kt = (int32_t)(((int64_t)sk + bk - 1) / bk);
+    // codes must be 0, 1 or 2 everywhere (as for bsfa_plan_from_blocks); entries and pieces
+    // are counted over the blocks that exist, so the buffers are sized exactly
+    const int32_t rq = std::min(nbq, n_qt), rk = std::min(nbk, n_kt);
+    uint8_t worst = 0;
+    int64_t nnz = 0, n_pieces = 0;
+    for (int32_t i = 0; i < nbq; ++i) {
+        const uint8_t *r = codes + (int64_t)i * nbk;
+        const int32_t jc = i < rq ? rk : 0;   // blocks of this row that exist
+        int64_t nz = 0, n2 = 0;
+        // byte-wide counters over chunks of 255 blocks (they cannot wrap), so that the
+        // compiler keeps the loop in vector registers
+        for (int32_t j0 = 0; j0 < jc; j0 += 255) {
+            const int32_t j1 = std::min(j0 + 255, jc);
+            uint8_t cz = 0, c2 = 0, mx = 0;
+            for (int32_t j = j0; j < j1; ++j) {
+                cz += r[j] != 0;
+                c2 += r[j] == 2;
+                mx = std::max(mx, r[j]);
+            }
+            nz += cz;
+            n2 += c2;
+            worst = std::max(worst, mx);
+        }
+        for (int32_t j = jc; j < nbk; ++j) worst = std::max(worst, r[j]);
+        nnz += nz;
+        if (std::min<int64_t>((int64_t)i * bq + bq, sq) - (int64_t)i * bq > 1) n_pieces += n2;
+    }
+    if (worst > 2) return BSFA_ERR_MASK;
+    if (nnz >= INT32_MAX || n_pieces >= INT32_MAX) return BSFA_ERR_UNSUPPORTED;
+    size_t off = 0;
+    auto place = [&](size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return at;
+    };
+    const size_t o_codes = place((size_t)std::max<int64_t>(n_codes, 1));
+    const size_t image_bytes = off;
+    const size_t rows = (size_t)n_qt + 1;
+    const size_t o_rc = place(rows * 4), o_rp = place(rows * 4), o_row = place(rows * 4), o_po = place(rows * 4);
+    const size_t nn = (size_t)std::max<int64_t>(nnz, 1);
+    const size_t o_col = place(nn * 4), o_tag = place(nn), o_pp = place((nn + 1) * 4);
+    const size_t o_pc = place((size_t)std::max<int64_t>(n_pieces, 1) * sizeof(Piece));
+    const size_t o_tot = place(8 * sizeof(unsigned long long));
+    const size_t temp = dcsr_blocks_scan_temp_bytes(n_qt + 1);
+    const size_t o_tmp = place(std::max<size_t>(temp, 1));
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BSFA_ERR_HIP;
+    Staging *stg = nullptr;
+    bsfa_status sst = staging_acquire(dev, image_bytes, &stg);
+    if (sst != BSFA_OK) return sst;
+    if (n_codes > 0) std::memcpy((uint8_t *)stg->host + o_codes, codes, (size_t)n_codes);
+    DcsrEx *c = new (std::nothrow) DcsrEx;
+    if (!c) {
+        staging_release_now(stg);
+        return BSFA_ERR_OOM;
+    }
+    c->device = dev;
+    c->sq = sq;
+    c->sk = sk;
+    c->bq = bq;
+    c->bk = bk;
+    c->n_qt = n_qt;
+    c->n_kt = n_kt;
+    c->n_touch = nnz;   // one (tile, block) incidence per entry
+    void *buf = nullptr;
+    if (hipMalloc(&buf, off) != hipSuccess) {
+        (void)hipGetLastError();
+        staging_release_now(stg);
+        delete c;
+        return BSFA_ERR_OOM;
+    }
+    c->buf = buf;
+    char *b = (char *)buf;
+    if (hipEventCreateWithFlags(&c->done, hipEventDisableTiming) != hipSuccess) {
+        staging_release_now(stg);
+        bsfa_dcsr_destroy(c);
+        return BSFA_ERR_HIP;
+    }
+    const hipStream_t s = (hipStream_t)stream;
+    DcsrBlockArgs a{};
+    a.sq = sq;
+    a.sk = sk;
+    a.bq = bq;
+    a.bk = bk;
+    a.n_qt = n_qt;
+    a.n_kt = n_kt;
+    a.nbq = nbq;
+    a.nbk = nbk;
+    a.codes = (const uint8_t *)(b + o_codes);
+    a.row_cnt = (int32_t *)(b + o_rc);
+    a.row_pcnt = (int32_t *)(b + o_rp);
+    a.row_ptr = (int32_t *)(b + o_row);
+    a.row_poff = (int32_t *)(b + o_po);
+    a.temp = b + o_tmp;
+    a.temp_bytes = temp;
+    a.col = (int32_t *)(b + o_col);
+    a.tag = (uint8_t *)(b + o_tag);
+    a.piece_ptr = (int32_t *)(b + o_pp);
+    a.pieces = (Piece *)(b + o_pc);
+    a.totals = (unsigned long long *)(b + o_tot);
+    c->row_ptr = a.row_ptr;
+    c->col = a.col;
+    c->tag = a.tag;
+    c->piece_ptr = a.piece_ptr;
+    c->pieces = (const int32_t *)a.pieces;
+    c->totals_dev = a.totals;
+    // the pinned image stays reserved until the copy recorded behind it has run
+    const bool copied = hipMemcpyAsync(b, stg->host, image_bytes, hipMemcpyHostToDevice, s) == hipSuccess;
+    bool ok = copied && hipEventRecord(stg->copied, s) == hipSuccess;
+    if (ok) {
+        staging_in_flight(stg);
+    } else {
+        if (copied) (void)hipStreamSynchronize(s);   // error path: the copy may still read the image
+        staging_release_now(stg);
+    }
+    ok = ok && launch_dcsr_blocks(a, s) == hipSuccess;
+    ok = ok && hipEventRecord(c->done, s) == hipSuccess;
+    if (!ok) {
+        (void)hipGetLastError();
+        bsfa_dcsr_destroy(c);
+        return BSFA_ERR_HIP;
+    }
+    *out = c;
+    return BSFA_OK;
+}
+
 bsfa_status bsfa_dcsr_view_get(bsfa_dcsr *c, bsfa_dcsr_view *v)
 {
     if (!c || !v) return BSFA_ERR_ARG;

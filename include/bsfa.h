@@ -321,6 +321,20 @@ typedef struct {
 
 bsfa_status bsfa_dcsr_build(const bsfa_slice *slices, int32_t n_slices, int32_t sq, int32_t sk,
                             int32_t bq, int32_t bk, void *stream, bsfa_dcsr **out);
+/* The same device CSR from a block-code map whose blocks are the tiles ([MA] "Blackwell
+ * adaptation": block-sparse mask generation on the device; [UA] 3 Full / Causal / Empty
+ * blocks): codes is a host uint8 [nbq, nbk] row-major map over (bq x bk) blocks, 0 =
+ * empty, 1 = full, 2 = causal inside the block, blocks clipped to [0, sq) x [0, sk) --
+ * the mask bsfa_plan_from_blocks builds with block_q = bq, block_k = bk.  The arrays
+ * equal, entry for entry, those of that plan: each non-empty block in range is one
+ * entry, full for code 1 (and for a causal block of one row), else partial with the
+ * block itself as its one piece (diag = k1 - q1 of the clipped block).  The host checks
+ * the codes and counts the entries (one pass over the map), copies the map to the
+ * device and enqueues the compile on stream (no wait); touches = nnz.  Errors:
+ * BSFA_ERR_ARG, BSFA_ERR_MASK (a code above 2), BSFA_ERR_UNSUPPORTED (2^31 entries or
+ * pieces or more), BSFA_ERR_OOM, BSFA_ERR_HIP. */
+bsfa_status bsfa_dcsr_build_blocks(const uint8_t *codes, int32_t nbq, int32_t nbk, int32_t sq, int32_t sk,
+                                   int32_t bq, int32_t bk, void *stream, bsfa_dcsr **out);
 bsfa_status bsfa_dcsr_view_get(bsfa_dcsr *csr, bsfa_dcsr_view *view);
 /* Waits for the compile and copies its arrays to host memory in the layouts of
  * bsfa_plan_export_csr and bsfa_plan_export_pieces: row_ptr [n_qtiles + 1], col and tag

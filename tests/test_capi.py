@@ -258,3 +258,22 @@ def test_device_compiler_rejects_bad_arguments():
     assert lib.bsfa_dcsr_build(None, 1, 10, 10, 128, 128, None, ctypes.byref(h)) == 1  # no slices
     assert lib.bsfa_plan_from_dcsr(None, 2, 1, 128, ctypes.byref(h)) == 1              # no csr
     assert lib.bsfa_plan_from_dcsr(None, 2, 1, 128, None) == 1                         # no out
+
+
+def test_block_code_device_compiler_rejects_bad_arguments():
+    """Checks of bsfa_dcsr_build_blocks that fail before any HIP call."""
+    lib = api.library()
+    h = ctypes.c_void_p()
+    codes = np.zeros((3, 3), np.uint8)
+    codes[2, 2] = 3
+    assert lib.bsfa_dcsr_build_blocks(api._ptr(codes), 3, 3, 384, 384, 128, 128, None, ctypes.byref(h)) == 5
+    codes[2, 2] = 1
+    assert lib.bsfa_dcsr_build_blocks(api._ptr(codes), 3, 3, 384, 384, 0, 128, None, ctypes.byref(h)) == 1
+    assert lib.bsfa_dcsr_build_blocks(api._ptr(codes), 3, 3, -1, 384, 128, 128, None, ctypes.byref(h)) == 1
+    assert lib.bsfa_dcsr_build_blocks(None, 3, 3, 384, 384, 128, 128, None, ctypes.byref(h)) == 1
+    assert lib.bsfa_dcsr_build_blocks(api._ptr(codes), 3, 3, 384, 384, 128, 128, None, None) == 1
+    # a code above 2 outside the tile grid is refused too (as bsfa_plan_from_blocks does)
+    big = np.zeros((5, 5), np.uint8)
+    big[4, 4] = 7
+    assert lib.bsfa_dcsr_build_blocks(api._ptr(big), 5, 5, 100, 100, 128, 128, None, ctypes.byref(h)) == 5
+    assert not h.value

@@ -224,3 +224,85 @@ def test_device_compiles_from_several_host_threads():
         th.join()
     torch.cuda.synchronize()
     assert not errors, errors
+
+
+def check_blocks(codes, sq, sk, bq, bk, what):
+    """bsfa_dcsr_build_blocks against the host plan of the same block map (blocks = tiles)."""
+    plan = api.Plan.from_blocks(codes, bq, bk, sq, sk, 1, 1, 64, bq=bq, bk=bk)
+    dc = api.DeviceCsr.from_blocks(codes, sq, sk, bq=bq, bk=bk)
+    v = dc.view()
+    rp, col, tag, pp, pcs = dc.export()
+    hrp, hcol, htag = plan.csr()
+    hpp, hpcs = plan.pieces()
+    inf = plan.info()
+    assert np.array_equal(rp, hrp), f"{what}: row_ptr"
+    assert np.array_equal(col, hcol), f"{what}: col"
+    assert np.array_equal(tag, htag), f"{what}: tag"
+    assert np.array_equal(pp, hpp), f"{what}: piece_ptr"
+    assert np.array_equal(pcs, hpcs), f"{what}: pieces"
+    for k in ("nnz", "n_full", "n_partial", "n_pieces", "pairs"):
+        assert v[k] == inf[k], f"{what}: {k} {v[k]} != {inf[k]}"
+    assert v["touches"] == v["nnz"]
+    dc.close()
+    plan.close()
+    return v
+
+
+@pytest.mark.parametrize("bq,bk", [(128, 128), (64, 128), (128, 64), (128, 256), (16, 48), (1, 7)])
+def test_block_codes_compiled_on_the_device(bq, bk):
+    """Random code maps (densities 0 to 1, every code), maps shorter, exactly as long and
+    longer than the tile grid, ragged last rows and columns, single-row blocks."""
+    rng = np.random.default_rng(bq * 7919 + bk)
+    for t in range(24):
+        sq, sk = int(rng.integers(1, 1200)), int(rng.integers(1, 1200))
+        nqt, nkt = -(-sq // bq), -(-sk // bk)
+        nbq = max(0, nqt + int(rng.integers(-2, 3)))
+        nbk = max(0, nkt + int(rng.integers(-2, 3)))
+        dens = float(rng.uniform(0, 1))
+        codes = np.where(rng.random((nbq, nbk)) < dens, rng.integers(1, 3, (nbq, nbk)), 0).astype(np.uint8)
+        check_blocks(codes, sq, sk, bq, bk, f"blocks bq={bq} bk={bk} sq={sq} sk={sk} map {nbq}x{nbk}")
+
+
+def test_block_codes_edge_cases():
+    check_blocks(np.zeros((0, 0), np.uint8), 300, 200, 128, 128, "empty map")
+    check_blocks(np.zeros((3, 2), np.uint8), 300, 200, 128, 128, "all-empty map")
+    check_blocks(np.full((1, 1), 2, np.uint8), 1, 1, 128, 128, "one causal pair")
+    check_blocks(np.full((4, 4), 2, np.uint8), 385, 390, 128, 128, "causal, ragged last row of one token")
+    check_blocks(np.full((2, 2), 1, np.uint8), 0, 0, 128, 128, "no rows, no keys")
+
+
+def test_block_codes_refuse_a_code_above_2():
+    codes = np.zeros((3, 3), np.uint8)
+    codes[2, 1] = 3
+    with pytest.raises(api.BsfaError) as e:
+        api.DeviceCsr.from_blocks(codes, 384, 384)
+    assert e.value.status == 5
+
+
+def test_strided_blocks_device_plan_and_forward():
+    """The strided workload's code map compiled on the device: its plan equals the host
+    plan built from the same map, and the forward over it is bit-identical."""
+    import torch
+    w = W.block_sparse_strided_s32768()
+    codes = W.strided_block_codes(w.sq // 128, 8)
+    check_blocks(codes, w.sq, w.sk, 128, 128, "strided s32768")
+    hp = api.Plan.from_blocks(codes, 128, 128, w.sq, w.sk, w.hq, w.hkv, w.d).upload()
+    dc = api.DeviceCsr.from_blocks(codes, w.sq, w.sk)
+    dp = dc.plan(w.hq, w.hkv, w.d)
+    dc.close()
+    _same_plan(dp, hp, "strided s32768 from blocks")
+    q, k, v = api.to_device_bf16(w.q), api.to_device_bf16(w.k), api.to_device_bf16(w.v)
+    o1, l1 = api.attn_fwd(q, k, v, hp, w.scale)
+    o2, l2 = api.attn_fwd(q, k, v, dp.upload(), w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    say("strided s32768: device plan from the block map equals the host plan; forward bit-identical")
+    hp.close()
+    dp.close()
+
+
+def test_block_codes_524288():
+    """The benchmark's strided map at 524,288 tokens (4096 x 4096 blocks)."""
+    S = 524288
+    v = check_blocks(W.strided_block_codes(S // 128, 8), S, S, 128, 128, "strided blocks s524288")
+    say(f"strided blocks s{S}: nnz {v['nnz']} ({v['n_full']} F + {v['n_partial']} P)")
