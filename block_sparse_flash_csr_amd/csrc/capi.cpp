@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "bsfa_internal.h"
+#include "dcsr_blocks.h"
 
 using namespace bsfa;
 

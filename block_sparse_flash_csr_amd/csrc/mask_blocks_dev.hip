@@ -17,7 +17,7 @@
 // slot).
 #include <hipcub/hipcub.hpp>
 
-#include "bsfa_internal.h"
+#include "dcsr_blocks.h"
 
 namespace bsfa {
 namespace {
