@@ -289,7 +289,7 @@ __device__ __forceinline__ uint64_t range_bits(int lo, int hi)
     return upto_hi & ~((1ull << lo) - 1ull);
 }
 
-// One score through the mask: bit off of w keeps it, else -inf (v_bfe_i32 + v_bfi_b32).
+// One score through the mask: bit off of w keeps it, else -inf.
 __device__ __forceinline__ float masked(float x, int32_t w, int off)
 {
     const int32_t keep = (w << (31 - off)) >> 31;
@@ -328,9 +328,8 @@ __device__ __forceinline__ uint64_t mask_bits_pf(const Step &cur, const PiecePai
     return m & range_bits(0, tail);
 }
 
-// Rejected scores become -inf: bit off of the mask word, sign-extended to a full
-// word (v_bfe_i32), selects between the score and -inf bit by bit (v_bfi_b32).
-// off(kb, r) = kb*32 + 8*(r>>2) + (r&3) is the offset of accumulator register r of
+// Rejected scores become -inf: bit off of the mask word selects between the score and
+// -inf.  off(kb, r) = kb*32 + 8*(r>>2) + (r&3) is the offset of accumulator register r of
 // block kb from base.
 __device__ __forceinline__ void apply_bits(uint64_t m, f32x16 (&s)[2])
 {
