@@ -442,6 +442,32 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
                            forward_hbm_gbs=nc * ctr["hbm_bytes_per_launch"] / fwd_ms * 1e-6)
     log(f"{w.name}: fwd {fwd_ms:.3f} ms ({fl / fwd_ms * 1e-9:.1f} TFLOPS), merge {merge_ms:.3f} ms "
         f"({merge_bytes / merge_ms * 1e-6:.0f} GB/s)")
+    # the same split with fp32 partial outputs (the chunk forwards write fp32 O, the merge
+    # reads fp32 partials and writes the bf16 result)
+    torch.cuda.synchronize()
+    del os_
+    os32 = [torch.empty((c, w.hq, w.d), dtype=torch.float32, device="cuda") for _ in range(nc)]
+
+    def fwd_all32():
+        for t in range(nc):
+            api.attn_fwd(q, k[t * c:(t + 1) * c], v[t * c:(t + 1) * c], plans[t], w.scale,
+                         out=os32[t], lse=ls_[t], stream=stream)
+
+    def merge32():
+        api.attn_merge(os32, ls_, out=om, lse=lm, stream=stream)
+
+    sustain(lambda: (fwd_all32(), merge32()), warm_s)
+    fwd32_ms = float(np.median(event_times(fwd_all32, reps, stream)))
+    merge32_ms = float(np.median(event_times(merge32, reps * 2, stream)))
+    merge32_bytes = nc * c * w.hq * (4 * w.d + 4) + c * w.hq * (2 * w.d + 4)
+    out[w.name]["fp32_partials"] = {
+        "forward_ms": fwd32_ms, "forward_tflops": fl / fwd32_ms * 1e-9, "merge_ms": merge32_ms,
+        "merge_bytes": merge32_bytes, "merge_gbs": merge32_bytes / merge32_ms * 1e-6,
+        "merge_frac_of_hbm_peak": merge32_bytes / merge32_ms * 1e-6 / PEAK_HBM_GBS}
+    log(f"{w.name} with fp32 partials: fwd {fwd32_ms:.3f} ms ({fl / fwd32_ms * 1e-9:.1f} TFLOPS), merge "
+        f"{merge32_ms:.3f} ms ({merge32_bytes / merge32_ms * 1e-6:.0f} GB/s)")
+    torch.cuda.synchronize()
+    del os32
     for p in plans:
         p.close()
     return out

@@ -89,6 +89,11 @@ def library():
                                                                          ctypes.POINTER(Tensor), P, I64, P]
     lib.bsfa_attn_merge.argtypes = [P, P, I32, I64, I64, I64, I32, I32, I32,
                                     ctypes.POINTER(Tensor), P, P]
+    lib.bsfa_attn_fwd_typed.argtypes = [ctypes.POINTER(Tensor)] * 3 + [P, ctypes.c_float,
+                                                                       ctypes.POINTER(Tensor), I32, P, I64, P,
+                                                                       I64, P]
+    lib.bsfa_attn_merge_typed.argtypes = [P, I32, P, I32, I64, I64, I64, I32, I32, I32,
+                                          ctypes.POINTER(Tensor), I32, P, P]
     lib.bsfa_attn_bwd.argtypes = [ctypes.POINTER(Tensor)] * 4 + [P, I64, P, ctypes.c_float,
                                                                  P, P, P, P, P]
     lib.bsfa_plan_export_pieces.argtypes = [P, P, P, I64]
@@ -108,7 +113,7 @@ def library():
     for name in ("bsfa_plan_create", "bsfa_plan_from_varlen", "bsfa_plan_from_blocks",
                  "bsfa_plan_upload", "bsfa_plan_get_info", "bsfa_plan_export_csr",
                  "bsfa_plan_export_schedule", "bsfa_plan_export_units", "bsfa_attn_fwd",
-                 "bsfa_attn_fwd_noalloc",
+                 "bsfa_attn_fwd_noalloc", "bsfa_attn_fwd_typed", "bsfa_attn_merge_typed",
                  "bsfa_attn_merge", "bsfa_attn_bwd", "bsfa_plan_export_pieces", "bsfa_dcsr_build",
                  "bsfa_dcsr_build_blocks", "bsfa_dcsr_view_get", "bsfa_dcsr_export", "bsfa_plan_from_dcsr"):
         getattr(lib, name).restype = I32
@@ -343,12 +348,26 @@ def workspace_for(plan: Plan, device="cuda"):
     return torch.empty(n // 4, dtype=torch.float32, device=device)
 
 
-def attn_fwd(q, k, v, plan: Plan, scale: float, out=None, lse=None, workspace=None, stream=None):
+DTYPE_BF16, DTYPE_F32 = 0, 1   # element types of O for the typed entry points
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise ValueError(f"O must be bf16 or fp32, got {t.dtype}")
+
+
+def attn_fwd(q, k, v, plan: Plan, scale: float, out=None, lse=None, workspace=None, stream=None,
+             out_dtype=None):
     """Forward over the plan's mask.  q [sq, hq, d], k/v [sk, hkv, d] bf16 CUDA tensors.
     workspace: fp32 device tensor of at least the plan's workspace_bytes when a row is
-    split (allocated here when not given).
+    split (allocated here when not given).  O is bf16 unless `out` is an fp32 tensor or
+    out_dtype is torch.float32 (the fp32 value the bf16 output is rounded from).
 
-    Returns (O [sq, hq, d] bf16, LSE [hq, sq] fp32)."""
+    Returns (O [sq, hq, d], LSE [hq, sq] fp32)."""
     import torch
     sq, hq, d = q.shape
     psq, psk, phq, phkv, pd = plan.shapes()
@@ -359,10 +378,12 @@ def attn_fwd(q, k, v, plan: Plan, scale: float, out=None, lse=None, workspace=No
             raise ValueError(f"{name} shape {tuple(t.shape)} does not match the plan "
                              f"({psk}, {phkv}, {pd})")
     if out is None:
-        out = torch.empty((sq, hq, d), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((sq, hq, d), dtype=out_dtype or torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((hq, sq), dtype=torch.float32, device=q.device)
-    assert q.dtype == k.dtype == v.dtype == out.dtype == torch.bfloat16
+    assert q.dtype == k.dtype == v.dtype == torch.bfloat16
+    o_code = _dtype_code(out)
+    assert out_dtype is None or out.dtype == out_dtype
     assert tuple(out.shape) == (sq, hq, d)
     assert lse.dtype == torch.float32 and lse.stride(1) == 1 and lse.shape[0] == hq
     if workspace is None and plan.info()["workspace_bytes"] > 0:
@@ -374,10 +395,16 @@ def attn_fwd(q, k, v, plan: Plan, scale: float, out=None, lse=None, workspace=No
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
     tq, tk, tv, to = _tview(q), _tview(k), _tview(v), _tview(out)
-    _check("bsfa_attn_fwd", library().bsfa_attn_fwd(
-        ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), plan.handle, float(scale),
-        ctypes.byref(to), ctypes.c_void_p(lse.data_ptr()), lse.stride(0), ctypes.c_void_p(ws_ptr),
-        ws_bytes, _stream_handle(stream)))
+    if o_code == DTYPE_BF16:
+        _check("bsfa_attn_fwd", library().bsfa_attn_fwd(
+            ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), plan.handle, float(scale),
+            ctypes.byref(to), ctypes.c_void_p(lse.data_ptr()), lse.stride(0), ctypes.c_void_p(ws_ptr),
+            ws_bytes, _stream_handle(stream)))
+    else:
+        _check("bsfa_attn_fwd_typed", library().bsfa_attn_fwd_typed(
+            ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), plan.handle, float(scale),
+            ctypes.byref(to), o_code, ctypes.c_void_p(lse.data_ptr()), lse.stride(0), ctypes.c_void_p(ws_ptr),
+            ws_bytes, _stream_handle(stream)))
     return out, lse
 
 
@@ -421,8 +448,10 @@ def attn_bwd(q, k, v, dout, lse, plan: Plan, scale: float, dq=None, dk=None, dv=
     return dq, dk, dv
 
 
-def attn_merge(o_parts, lse_parts, out=None, lse=None, stream=None):
-    """Merge n partials: o_parts list of [T, H, d] bf16 (same strides), lse_parts list of [H, T] fp32."""
+def attn_merge(o_parts, lse_parts, out=None, lse=None, stream=None, out_dtype=None):
+    """Merge n partials: o_parts list of [T, H, d] tensors of one dtype, bf16 or fp32 (same
+    strides), lse_parts list of [H, T] fp32.  The result O is bf16 unless `out` is fp32 or
+    out_dtype is torch.float32."""
     import torch
     n = len(o_parts)
     assert n == len(lse_parts) and n >= 1
@@ -430,24 +459,32 @@ def attn_merge(o_parts, lse_parts, out=None, lse=None, stream=None):
     st = o_parts[0].stride()
     if st[2] != 1:
         raise ValueError("partials need a contiguous head dim (stride 1)")
+    p_code = _dtype_code(o_parts[0])
     for p in o_parts:
-        assert p.shape == (t, h, d) and p.stride() == st and p.dtype == torch.bfloat16
+        assert p.shape == (t, h, d) and p.stride() == st and p.dtype == o_parts[0].dtype
     lst = lse_parts[0].stride(0)
     for l in lse_parts:
         assert l.shape[0] == h and l.stride(0) == lst and l.stride(1) == 1 and l.dtype == torch.float32
         if l.shape[1] < t:
             raise ValueError(f"an LSE part covers {l.shape[1]} tokens, fewer than the {t} merged")
     if out is None:
-        out = torch.empty((t, h, d), dtype=torch.bfloat16, device=o_parts[0].device)
+        out = torch.empty((t, h, d), dtype=out_dtype or torch.bfloat16, device=o_parts[0].device)
+    o_code = _dtype_code(out)
+    assert out_dtype is None or out.dtype == out_dtype
     if lse is None:
         lse = torch.empty((h, lst), dtype=torch.float32, device=o_parts[0].device)
     assert lse.stride(0) == lst
     optrs = (ctypes.c_void_p * n)(*[p.data_ptr() for p in o_parts])
     lptrs = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lse_parts])
     to = _tview(out)
-    _check("bsfa_attn_merge", library().bsfa_attn_merge(
-        optrs, lptrs, n, st[0], st[1], lst, t, h, d, ctypes.byref(to),
-        ctypes.c_void_p(lse.data_ptr()), _stream_handle(stream)))
+    if p_code == DTYPE_BF16 and o_code == DTYPE_BF16:
+        _check("bsfa_attn_merge", library().bsfa_attn_merge(
+            optrs, lptrs, n, st[0], st[1], lst, t, h, d, ctypes.byref(to),
+            ctypes.c_void_p(lse.data_ptr()), _stream_handle(stream)))
+    else:
+        _check("bsfa_attn_merge_typed", library().bsfa_attn_merge_typed(
+            optrs, p_code, lptrs, n, st[0], st[1], lst, t, h, d, ctypes.byref(to), o_code,
+            ctypes.c_void_p(lse.data_ptr()), _stream_handle(stream)))
     return out, lse[:, :t]
 
 

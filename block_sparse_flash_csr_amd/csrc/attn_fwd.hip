@@ -534,8 +534,10 @@ __device__ __forceinline__ void step_body(char *__restrict__ k_dst, char *__rest
     }
 }
 
-template <int D>
-__global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
+// The kernel body; OUT_F32 selects the type of O (bf16, or the fp32 value it is rounded
+// from).
+template <int D, bool OUT_F32>
+__device__ __forceinline__ void attn_fwd_body(const FwdArgs &a)
 {
     using C = Cfg<D>;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_B];
@@ -732,7 +734,22 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
             if (hh == 0) ws[kKernelBq * D + r] = lse_v;
             continue;
         }
-        {
+        if constexpr (OUT_F32) {
+            // fp32 O: the same products the bf16 output is rounded from, stored straight
+            // from the lane's registers (4 head dims of its query row per store)
+            if (qvalid) {
+                float *orow = (float *)a.o + (int64_t)qrow * a.o_st + (int64_t)h * a.o_sh;
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        f32x4 w;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) w[t] = acc.o[db][g4 * 4 + t] * inv;
+                        *(f32x4 *)(orow + db * 32 + 8 * g4 + 4 * hh) = w;
+                    }
+            }
+        } else {
             constexpr int ESH = D == 128 ? 0 : 1;
             constexpr int RPI = 1024 / C::ROWB;   // rows per 16-byte-per-lane read
             char *stage = smem + wave * 32 * C::ROWB;
@@ -759,6 +776,18 @@ __global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
         }
         if (qvalid && hh == 0) a.lse[(int64_t)h * a.lse_sh + qrow] = lse_v;
     }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2) attn_fwd_kernel(const FwdArgs a)
+{
+    attn_fwd_body<D, false>(a);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2) attn_fwd_o32_kernel(const FwdArgs a)
+{
+    attn_fwd_body<D, true>(a);
 }
 
 }  // namespace
@@ -795,10 +824,16 @@ hipError_t static_workspace(float **ptr)
 hipError_t launch_attn_fwd(const FwdArgs &a, int d, hipStream_t stream)
 {
     if (a.n_bins <= 0) return hipSuccess;
-    if (d == 128)
+    if (a.o_f32) {
+        if (d == 128)
+            hipLaunchKernelGGL(attn_fwd_o32_kernel<128>, dim3(a.n_bins), dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL(attn_fwd_o32_kernel<64>, dim3(a.n_bins), dim3(kThreads), 0, stream, a);
+    } else if (d == 128) {
         hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(a.n_bins), dim3(kThreads), 0, stream, a);
-    else
+    } else {
         hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(a.n_bins), dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ namespace bsfa {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
@@ -27,10 +28,13 @@ constexpr float kLn2 = 0.693147180559945309f;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-template <int D>
-__global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a)
+// One lane: EPL head dims (16 bytes of a partial row) of one (token, head) row.
+// IN32 / OUT32: the partials / the result are fp32 (else bf16).
+template <int D, bool IN32, bool OUT32>
+__device__ __forceinline__ void merge_body(const MergeArgs &a)
 {
-    constexpr int TPR = D / 8;               // lanes per row (16 bytes each)
+    constexpr int EPL = IN32 ? 4 : 8;        // head dims per lane (16-byte loads)
+    constexpr int TPR = D / EPL;             // lanes per row
     constexpr int RPB = kThreads / TPR;      // rows per workgroup
     const int tid = threadIdx.x;
     // heads vary fastest across workgroups: the workgroups running together read whole
@@ -43,12 +47,14 @@ __global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a)
     float lse[BSFA_MERGE_MAX_PARTS];
     u32x4 ov[BSFA_MERGE_MAX_PARTS];
     const int64_t lse_off = (int64_t)h * a.lse_sh + t;
-    const int64_t o_off = (int64_t)t * a.p_st + (int64_t)h * a.p_sh + chunk * 8;
+    const int64_t o_off = (int64_t)t * a.p_st + (int64_t)h * a.p_sh + chunk * EPL;
 #pragma unroll
     for (int i = 0; i < BSFA_MERGE_MAX_PARTS; ++i) {
         if (i < a.n) {
             lse[i] = a.lse_parts[i][lse_off];
-            ov[i] = __builtin_nontemporal_load((const u32x4 *)((const __bf16 *)a.o_parts[i] + o_off));
+            const u32x4 *src = IN32 ? (const u32x4 *)((const float *)a.o_parts[i] + o_off)
+                                    : (const u32x4 *)((const __bf16 *)a.o_parts[i] + o_off);
+            ov[i] = __builtin_nontemporal_load(src);
         }
     }
     float m = -INFINITY;
@@ -56,7 +62,9 @@ __global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a)
     for (int i = 0; i < BSFA_MERGE_MAX_PARTS; ++i)
         if (i < a.n) m = fmaxf(m, lse[i]);
 
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float acc[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
     float out_lse = -INFINITY;
     if (m != -INFINITY) {
         float w[BSFA_MERGE_MAX_PARTS];
@@ -75,21 +83,48 @@ __global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a)
                 const float wi = w[i] * inv;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    acc[2 * j] += wi * bf16_lo(ov[i][j]);
-                    acc[2 * j + 1] += wi * bf16_hi(ov[i][j]);
+                    if constexpr (IN32) {
+                        acc[j] += wi * __uint_as_float(ov[i][j]);
+                    } else {
+                        acc[2 * j] += wi * bf16_lo(ov[i][j]);
+                        acc[2 * j + 1] += wi * bf16_hi(ov[i][j]);
+                    }
                 }
             }
         }
         out_lse = m + __log2f(sum) * kLn2;
     }
-    u32x4 res;
+    const int64_t r_off = (int64_t)t * a.o_st + (int64_t)h * a.o_sh + chunk * EPL;
+    if constexpr (OUT32) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const __bf16 lo = (__bf16)acc[2 * j], hi = (__bf16)acc[2 * j + 1];
-        res[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        for (int j = 0; j < EPL; j += 4)
+            __builtin_nontemporal_store(f32x4{acc[j], acc[j + 1], acc[j + 2], acc[j + 3]},
+                                        (f32x4 *)((float *)a.o + r_off + j));
+    } else {
+        uint32_t res[EPL / 2];
+#pragma unroll
+        for (int j = 0; j < EPL / 2; ++j) {
+            const __bf16 lo = (__bf16)acc[2 * j], hi = (__bf16)acc[2 * j + 1];
+            res[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        if constexpr (EPL == 8)
+            __builtin_nontemporal_store(u32x4{res[0], res[1], res[2], res[3]}, (u32x4 *)((__bf16 *)a.o + r_off));
+        else
+            __builtin_nontemporal_store(u32x2{res[0], res[1]}, (u32x2 *)((__bf16 *)a.o + r_off));
     }
-    __builtin_nontemporal_store(res, (u32x4 *)((__bf16 *)a.o + (int64_t)t * a.o_st + (int64_t)h * a.o_sh + chunk * 8));
     if (chunk == 0) a.lse[lse_off] = out_lse;
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a)
+{
+    merge_body<D, false, false>(a);
+}
+
+template <int D, bool IN32, bool OUT32>
+__global__ void __launch_bounds__(kThreads) attn_merge_typed_kernel(const MergeArgs a)
+{
+    merge_body<D, IN32, OUT32>(a);
 }
 
 }  // namespace
@@ -97,8 +132,8 @@ __global__ void __launch_bounds__(kThreads) attn_merge_kernel(const MergeArgs a)
 // Rows of the forward launch that were split into parts: the parts' normalised fp32
 // (O_t, LSE_t) in the workspace merge the same way into the caller's O and LSE.  A
 // workgroup takes RPB rows of one split row; a lane owns 4 head dims.
-template <int D>
-__global__ void __launch_bounds__(kThreads) split_merge_kernel(const SplitMergeArgs a)
+template <int D, bool OUT32>
+__device__ __forceinline__ void split_merge_body(const SplitMergeArgs &a)
 {
     constexpr int TPR = D / 4;               // lanes per row (4 floats each)
     constexpr int RPB = kThreads / TPR;      // rows per workgroup
@@ -124,11 +159,28 @@ __global__ void __launch_bounds__(kThreads) split_merge_kernel(const SplitMergeA
         o *= 1.0f / sum;
         lse = m + __log2f(sum) * kLn2;
     }
-    bf16x4 ob;
+    const int64_t r_off = (int64_t)row * a.o_st + (int64_t)h * a.o_sh + c;
+    if constexpr (OUT32) {
+        *(f32x4 *)((float *)a.o + r_off) = o;
+    } else {
+        bf16x4 ob;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ob[e] = (__bf16)o[e];
-    *(bf16x4 *)((__bf16 *)a.o + (int64_t)row * a.o_st + (int64_t)h * a.o_sh + c) = ob;
+        for (int e = 0; e < 4; ++e) ob[e] = (__bf16)o[e];
+        *(bf16x4 *)((__bf16 *)a.o + r_off) = ob;
+    }
     if (c == 0) a.lse[(int64_t)h * a.lse_sh + row] = lse;
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads) split_merge_kernel(const SplitMergeArgs a)
+{
+    split_merge_body<D, false>(a);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads) split_merge_o32_kernel(const SplitMergeArgs a)
+{
+    split_merge_body<D, true>(a);
 }
 
 hipError_t launch_split_merge(const SplitMergeArgs &a, int d, hipStream_t stream)
@@ -136,22 +188,37 @@ hipError_t launch_split_merge(const SplitMergeArgs &a, int d, hipStream_t stream
     if (a.n_splits <= 0) return hipSuccess;
     const int rpb = kThreads / (d / 4);
     dim3 grid(a.n_splits, (kKernelBq + rpb - 1) / rpb);
-    if (d == 128)
+    if (a.o_f32) {
+        if (d == 128)
+            hipLaunchKernelGGL(split_merge_o32_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL(split_merge_o32_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+    } else if (d == 128) {
         hipLaunchKernelGGL(split_merge_kernel<128>, grid, dim3(kThreads), 0, stream, a);
-    else
+    } else {
         hipLaunchKernelGGL(split_merge_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_attn_merge(const MergeArgs &a, int d, hipStream_t stream)
 {
     if (a.n_tok <= 0 || a.n_head <= 0) return hipSuccess;
-    const int rpb = kThreads / (d / 8);
+    const int rpb = kThreads / (d / (a.parts_f32 ? 4 : 8));
     dim3 grid((unsigned)(((int64_t)a.n_tok + rpb - 1) / rpb * a.n_head));
-    if (d == 128)
-        hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(attn_merge_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, a); };
+    const int sel = (a.parts_f32 ? 2 : 0) + (a.o_f32 ? 1 : 0);
+    if (d == 128) {
+        if (sel == 0) go(attn_merge_kernel<128>);
+        else if (sel == 1) go(attn_merge_typed_kernel<128, false, true>);
+        else if (sel == 2) go(attn_merge_typed_kernel<128, true, false>);
+        else go(attn_merge_typed_kernel<128, true, true>);
+    } else {
+        if (sel == 0) go(attn_merge_kernel<64>);
+        else if (sel == 1) go(attn_merge_typed_kernel<64, false, true>);
+        else if (sel == 2) go(attn_merge_typed_kernel<64, true, false>);
+        else go(attn_merge_typed_kernel<64, true, true>);
+    }
     return hipGetLastError();
 }
 

@@ -178,6 +178,7 @@ struct FwdArgs {
                                    // slot O [128][d] then LSE [128], fp32
     int32_t n_bins;
     int32_t n_entries, n_pieces;   // sizes of meta.entries / meta.pieces (bounds of vector loads)
+    int32_t o_f32;                 // O is fp32 (else bf16)
 };
 hipError_t launch_attn_fwd(const FwdArgs &a, int d, hipStream_t stream);
 
@@ -186,7 +187,7 @@ hipError_t launch_attn_fwd(const FwdArgs &a, int d, hipStream_t stream);
 constexpr size_t kStaticWorkspaceBytes = (size_t)32 << 20;
 hipError_t static_workspace(float **ptr);
 
-// Merge of split rows: partial results in the workspace -> O (bf16) and LSE.
+// Merge of split rows: partial results in the workspace -> O (bf16 or fp32) and LSE.
 struct SplitMergeArgs {
     const float *ws;
     const Split *splits;
@@ -194,6 +195,7 @@ struct SplitMergeArgs {
     void *o;
     float *lse;
     int32_t o_st, o_sh, lse_sh;
+    int32_t o_f32;                 // O is fp32 (else bf16)
 };
 hipError_t launch_split_merge(const SplitMergeArgs &a, int d, hipStream_t stream);
 
@@ -267,6 +269,7 @@ struct MergeArgs {
     void *o;
     float *lse;
     int64_t o_st, o_sh;
+    int32_t parts_f32, o_f32;      // partials / result are fp32 (else bf16)
 };
 hipError_t launch_attn_merge(const MergeArgs &a, int d, hipStream_t stream);
 

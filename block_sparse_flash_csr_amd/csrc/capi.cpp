@@ -23,7 +23,8 @@ constexpr int kBinsPerCu = 2;  // forward workgroups resident per CU (LDS and VG
 std::atomic<float> g_rescale_tau{8.0f};
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
-bool stride_ok(int64_t s) { return s >= 0 && (s & 7) == 0; }
+// Strides in elements: non-negative, 16-byte multiples (8 bf16 or, with f32, 4 fp32).
+bool stride_ok(int64_t s, bool f32 = false) { return s >= 0 && (s & (f32 ? 3 : 7)) == 0; }
 
 bsfa_status check_slices(const bsfa_slice *s, int32_t n, int32_t sq, int32_t sk)
 {
@@ -739,7 +740,18 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
                           int64_t lse_stride_head, void *workspace, int64_t workspace_bytes_cap,
                           void *stream)
 {
+    return bsfa_attn_fwd_typed(q, k, v, p, scale, o, BSFA_DTYPE_BF16, lse, lse_stride_head, workspace,
+                               workspace_bytes_cap, stream);
+}
+
+bsfa_status bsfa_attn_fwd_typed(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
+                                const bsfa_plan *p, float scale, bsfa_tensor *o, int32_t o_dtype, float *lse,
+                                int64_t lse_stride_head, void *workspace, int64_t workspace_bytes_cap,
+                                void *stream)
+{
     if (!q || !k || !v || !p || !o) return BSFA_ERR_ARG;
+    if (o_dtype != BSFA_DTYPE_BF16 && o_dtype != BSFA_DTYPE_F32) return BSFA_ERR_ARG;
+    const bool o32 = o_dtype == BSFA_DTYPE_F32;
     if (workspace_bytes_cap < 0) return BSFA_ERR_ARG;
     if (p->n_slots > 0) {
         // split rows: their parts write partial results into the caller's workspace
@@ -763,8 +775,10 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     const int32_t n_head[4] = {p->hq, p->hkv, p->hkv, p->hq};
     const bsfa_tensor *ts[4] = {q, k, v, o};
     for (int t = 0; t < 4; ++t) {
+        // 16-byte rows: strides in multiples of 8 bf16 (4 fp32 for an fp32 O)
+        const bool f32 = t == 3 && o32;
         if (ts[t]->ptr && !aligned16(ts[t]->ptr)) return BSFA_ERR_ALIGN;
-        if (!stride_ok(ts[t]->stride_tok) || !stride_ok(ts[t]->stride_head)) return BSFA_ERR_ALIGN;
+        if (!stride_ok(ts[t]->stride_tok, f32) || !stride_ok(ts[t]->stride_head, f32)) return BSFA_ERR_ALIGN;
         // the kernels size their buffer ranges as rows x stride_tok: a tensor with a token
         // needs stride_tok >= d even when it has only one
         if (n_tok[t] > 0 && ts[t]->stride_tok < p->d) return BSFA_ERR_SHAPE;
@@ -801,6 +815,7 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     a.n_bins = (int32_t)p->bin_ptr.size() - 1;
     a.n_entries = (int32_t)p->nnz();
     a.n_pieces = (int32_t)p->npieces();
+    a.o_f32 = o32 ? 1 : 0;
     if (p->sq == 0) return BSFA_OK;
     const hipStream_t s = (hipStream_t)stream;
     if (s != p->ustream) {
@@ -829,6 +844,7 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
         m.o_st = a.o_st;
         m.o_sh = a.o_sh;
         m.lse_sh = a.lse_sh;
+        m.o_f32 = a.o_f32;
         if (launch_split_merge(m, p->d, s) != hipSuccess) return BSFA_ERR_HIP;
     }
     return BSFA_OK;
@@ -929,17 +945,32 @@ bsfa_status bsfa_attn_merge(const void *const *o_parts, const float *const *lse_
                             int64_t lse_stride_head, int32_t n_tok, int32_t n_head, int32_t d,
                             bsfa_tensor *o, float *lse, void *stream)
 {
+    return bsfa_attn_merge_typed(o_parts, BSFA_DTYPE_BF16, lse_parts, n, part_stride_tok, part_stride_head,
+                                 lse_stride_head, n_tok, n_head, d, o, BSFA_DTYPE_BF16, lse, stream);
+}
+
+bsfa_status bsfa_attn_merge_typed(const void *const *o_parts, int32_t parts_dtype, const float *const *lse_parts,
+                                  int32_t n, int64_t part_stride_tok, int64_t part_stride_head,
+                                  int64_t lse_stride_head, int32_t n_tok, int32_t n_head, int32_t d,
+                                  bsfa_tensor *o, int32_t o_dtype, float *lse, void *stream)
+{
     if (!o_parts || !lse_parts || !o) return BSFA_ERR_ARG;
+    if ((parts_dtype != BSFA_DTYPE_BF16 && parts_dtype != BSFA_DTYPE_F32) ||
+        (o_dtype != BSFA_DTYPE_BF16 && o_dtype != BSFA_DTYPE_F32))
+        return BSFA_ERR_ARG;
+    const bool p32 = parts_dtype == BSFA_DTYPE_F32, o32 = o_dtype == BSFA_DTYPE_F32;
     if (n < 1 || n > BSFA_MERGE_MAX_PARTS || n_tok < 0 || n_head < 0 || n_head > 65535)
         return BSFA_ERR_ARG;
     if (d != 64 && d != 128) return BSFA_ERR_UNSUPPORTED;
     if (n_tok == 0 || n_head == 0) return BSFA_OK;   // nothing to merge; pointers may be NULL
     if (!lse) return BSFA_ERR_ARG;
-    // one workgroup per (16 tokens, head) at d 128 (32 at d 64) in a 1-D grid
-    if (((int64_t)n_tok + 15) / 16 * n_head >= INT32_MAX) return BSFA_ERR_UNSUPPORTED;
+    // one workgroup per (16 tokens, head) at d 128 with bf16 partials (8 with fp32
+    // partials; twice as many at d 64) in a 1-D grid
+    const int64_t rpb = p32 ? 8 : 16;
+    if (((int64_t)n_tok + rpb - 1) / rpb * n_head >= INT32_MAX) return BSFA_ERR_UNSUPPORTED;
     if (lse_stride_head < n_tok) return BSFA_ERR_ARG;
-    if (!stride_ok(part_stride_tok) || !stride_ok(part_stride_head) || !stride_ok(o->stride_tok) ||
-        !stride_ok(o->stride_head))
+    if (!stride_ok(part_stride_tok, p32) || !stride_ok(part_stride_head, p32) || !stride_ok(o->stride_tok, o32) ||
+        !stride_ok(o->stride_head, o32))
         return BSFA_ERR_ALIGN;
     if (!o->ptr) return BSFA_ERR_ARG;
     if (!aligned16(o->ptr)) return BSFA_ERR_ALIGN;
@@ -960,6 +991,8 @@ bsfa_status bsfa_attn_merge(const void *const *o_parts, const float *const *lse_
     a.lse = lse;
     a.o_st = o->stride_tok;
     a.o_sh = o->stride_head;
+    a.parts_f32 = p32 ? 1 : 0;
+    a.o_f32 = o32 ? 1 : 0;
     if (launch_attn_merge(a, d, (hipStream_t)stream) != hipSuccess) return BSFA_ERR_HIP;
     return BSFA_OK;
 }

@@ -221,6 +221,23 @@ bsfa_status bsfa_attn_fwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
                           int64_t lse_stride_head, void *workspace, int64_t workspace_bytes,
                           void *stream);
 
+/* ---- fp32 outputs ([UA] 3.2: a partial result is its normalised output and LSE) ----
+ * bsfa_attn_fwd and bsfa_attn_merge write bf16 outputs.  The _typed forms take the
+ * element type of O (and of the merge's partials): BSFA_DTYPE_BF16 or BSFA_DTYPE_F32.
+ * An fp32 O holds the normalised fp32 value that the bf16 output is rounded from (round
+ * to nearest even), so a bf16 call and an fp32 call on the same inputs and plan give
+ * bf16(O_f32) == O_bf16 bit for bit and the same LSE; it keeps the half-ulp rounding of
+ * a bf16 output (up to 2^-9 |O|) out of KV-split partials that are merged afterwards.
+ * An fp32 O is a [tokens, heads, d] fp32 tensor view (bsfa_tensor, element strides)
+ * with 16-byte aligned base and strides that are multiples of 4 elements; everything
+ * else is as for bsfa_attn_fwd.  Errors as bsfa_attn_fwd, plus BSFA_ERR_ARG for an
+ * unknown o_dtype. */
+enum { BSFA_DTYPE_BF16 = 0, BSFA_DTYPE_F32 = 1 };
+bsfa_status bsfa_attn_fwd_typed(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
+                                const bsfa_plan *plan, float scale, bsfa_tensor *o, int32_t o_dtype,
+                                float *lse, int64_t lse_stride_head, void *workspace,
+                                int64_t workspace_bytes, void *stream);
+
 /* ---- forward without allocation ------------------------------------------------
  * For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): bsfa_attn_fwd with the split rows'
@@ -282,6 +299,16 @@ bsfa_status bsfa_attn_merge(const void *const *o_parts, const float *const *lse_
                             int64_t part_stride_tok, int64_t part_stride_head,
                             int64_t lse_stride_head, int32_t n_tok, int32_t n_head, int32_t d,
                             bsfa_tensor *o, float *lse, void *stream);
+
+/* bsfa_attn_merge with the partials' and the result's element types given
+ * (BSFA_DTYPE_BF16 / BSFA_DTYPE_F32, independently).  fp32 tensors need strides that are
+ * multiples of 4 elements; with fp32 partials the limit is ceil(n_tok / 8) * n_head < 2^31.
+ * Errors as bsfa_attn_merge, plus BSFA_ERR_ARG for an unknown type. */
+bsfa_status bsfa_attn_merge_typed(const void *const *o_parts, int32_t parts_dtype,
+                                  const float *const *lse_parts, int32_t n, int64_t part_stride_tok,
+                                  int64_t part_stride_head, int64_t lse_stride_head, int32_t n_tok,
+                                  int32_t n_head, int32_t d, bsfa_tensor *o, int32_t o_dtype, float *lse,
+                                  void *stream);
 
 /* ---- device mask compiler ------------------------------------------------------
  * The tile CSR of a slice mask built on the GPU ([MA] "Blackwell adaptation": block-

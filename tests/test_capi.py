@@ -222,6 +222,34 @@ def test_merge_rejects_bad_arguments():
     assert lib.bsfa_attn_merge(nulls, nulls, 2, 1024, 128, 0, 0, 8, 96, ctypes.byref(empty), None, None) == 4
 
 
+def test_typed_entry_points_reject_bad_types_and_strides():
+    """The fp32-output forms: unknown element types, and fp32 strides that are not
+    16-byte multiples, fail before any HIP call; an fp32 stride of 4 elements passes the
+    stride check (the call then stops at the missing result pointer)."""
+    lib = api.library()
+    t = api.Tensor(ctypes.c_void_p(16), 1024, 128)
+    ptrs = (ctypes.c_void_p * 2)(16, 32)
+    lptr = (ctypes.c_void_p * 2)(16, 32)
+    buf = ctypes.c_void_p(16)
+
+    def merge(pdt, odt, p_st=1024, o=t):
+        return lib.bsfa_attn_merge_typed(ptrs, pdt, lptr, 2, p_st, 128, 64, 64, 8, 128, ctypes.byref(o), odt,
+                                         buf, None)
+
+    assert merge(2, 0) == 1 and merge(0, -1) == 1            # unknown types
+    assert merge(1, 0, p_st=1022) == 3                         # fp32 partial rows not 16-byte aligned
+    assert merge(0, 0, p_st=1020) == 3                         # bf16 stride: multiple of 8 needed
+    assert merge(1, 1, o=api.Tensor(ctypes.c_void_p(16), 1026, 128)) == 3
+    nul = api.Tensor(ctypes.c_void_p(None), 1020, 128)
+    assert merge(1, 1, p_st=1020, o=nul) == 1                  # strides accepted, no result pointer
+    p = api.Plan.from_slices([(0, 64, 0, 64, 1)], 64, 64, 1, 1, 128)
+    tp = [ctypes.byref(api.Tensor(ctypes.c_void_p(16), 128, 128))] * 3
+    o = api.Tensor(ctypes.c_void_p(16), 128, 128)
+    for bad in (2, -1, 7):
+        assert lib.bsfa_attn_fwd_typed(*tp, p.handle, 0.1, ctypes.byref(o), bad, buf, 64, None, 0, None) == 1
+    assert lib.bsfa_attn_fwd_typed(*tp, p.handle, 0.1, ctypes.byref(o), 1, buf, 64, None, 0, None) == 8  # not uploaded
+
+
 def test_backward_rejects_bad_arguments():
     """Checks of the gradient entry that fail before any HIP call."""
     lib = api.library()
