@@ -302,8 +302,20 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
                  "flops_per_pair": 10 * w.d, "pairs_per_head": info["pairs"],
                  "note": "dQ, dK, dV (fp32) from LSE and dO; algorithmic flops = 2.5x the forward's"}
     log(f"{name}: {ms:.3f} ms  {fl / ms * 1e-9:.1f} TFLOPS (algorithmic)")
+    # the same backward given the forward's fp32 O: D_i = dO_i . O_i inside the dQ kernel,
+    # no D pass (two kernels)
+    o32, _ = api.attn_fwd(q, k, v, plan, w.scale, stream=stream, out_dtype=torch.float32)
+    f32 = lambda: api.attn_bwd(q, k, v, g, lse, plan, w.scale, dq=dq, dk=dk, dv=dv, delta=delta,
+                               stream=stream, o=o32)
+    sustain(f32, warm_s)
+    ms32 = float(np.median(event_times(f32, reps * 2, stream)))
+    out[name]["from_fp32_o"] = {"kernel_ms": ms32, "tflops": fl / ms32 * 1e-9,
+                                "frac_of_peak": fl / ms32 * 1e-9 / PEAK_BF16_TFLOPS,
+                                "note": "D from the forward's fp32 O (bsfa_attn_bwd_o32): dQ and dK/dV kernels only"}
+    log(f"{name} from fp32 O: {ms32:.3f} ms  {fl / ms32 * 1e-9:.1f} TFLOPS (algorithmic)")
+    torch.cuda.synchronize()
     plan.close()
-    del q, k, v, g, o, lse, dq, dk, dv, delta
+    del q, k, v, g, o, o32, lse, dq, dk, dv, delta
     torch.cuda.empty_cache()
 
     # Mask compile: host plan creation (compile + column view + schedule) against the

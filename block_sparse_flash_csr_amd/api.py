@@ -96,6 +96,8 @@ def library():
                                           ctypes.POINTER(Tensor), I32, P, P]
     lib.bsfa_attn_bwd.argtypes = [ctypes.POINTER(Tensor)] * 4 + [P, I64, P, ctypes.c_float,
                                                                  P, P, P, P, P]
+    lib.bsfa_attn_bwd_o32.argtypes = [ctypes.POINTER(Tensor)] * 5 + [P, I64, P, ctypes.c_float,
+                                                                     P, P, P, P, P]
     lib.bsfa_plan_export_pieces.argtypes = [P, P, P, I64]
     lib.bsfa_dcsr_build.argtypes = [P, I32, I32, I32, I32, I32, P, PP]
     lib.bsfa_dcsr_build_blocks.argtypes = [P, I32, I32, I32, I32, I32, I32, P, PP]
@@ -113,7 +115,7 @@ def library():
     for name in ("bsfa_plan_create", "bsfa_plan_from_varlen", "bsfa_plan_from_blocks",
                  "bsfa_plan_upload", "bsfa_plan_get_info", "bsfa_plan_export_csr",
                  "bsfa_plan_export_schedule", "bsfa_plan_export_units", "bsfa_attn_fwd",
-                 "bsfa_attn_fwd_noalloc", "bsfa_attn_fwd_typed", "bsfa_attn_merge_typed",
+                 "bsfa_attn_fwd_noalloc", "bsfa_attn_fwd_typed", "bsfa_attn_merge_typed", "bsfa_attn_bwd_o32",
                  "bsfa_attn_merge", "bsfa_attn_bwd", "bsfa_plan_export_pieces", "bsfa_dcsr_build",
                  "bsfa_dcsr_build_blocks", "bsfa_dcsr_view_get", "bsfa_dcsr_export", "bsfa_plan_from_dcsr"):
         getattr(lib, name).restype = I32
@@ -409,9 +411,11 @@ def attn_fwd(q, k, v, plan: Plan, scale: float, out=None, lse=None, workspace=No
 
 
 def attn_bwd(q, k, v, dout, lse, plan: Plan, scale: float, dq=None, dk=None, dv=None,
-             delta=None, stream=None):
+             delta=None, stream=None, o=None):
     """Gradients of the plan's masked attention.  q/dout [sq, hq, d], k/v [sk, hkv, d]
-    bf16; lse [hq, >= sq] fp32 from the forward.
+    bf16; lse [hq, >= sq] fp32 from the forward.  o: the forward's fp32 output
+    (attn_fwd(..., out_dtype=torch.float32)), optional: with it D_i = dO_i . O_i comes from
+    O and the separate D pass is skipped.
 
     Returns (dQ [sq, hq, d], dK [sk, hkv, d], dV [sk, hkv, d]) fp32; delta (D_i =
     sum_j P_ij dP_ij, shaped like lse) is scratch the call fills."""
@@ -440,8 +444,20 @@ def attn_bwd(q, k, v, dout, lse, plan: Plan, scale: float, dq=None, dk=None, dv=
         assert t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shp, name
     assert delta.dtype == torch.float32 and delta.stride() == lse.stride() and delta.shape == lse.shape
     tq, tk, tv, tg = _tview(q), _tview(k), _tview(v), _tview(dout)
-    _check("bsfa_attn_bwd", library().bsfa_attn_bwd(
-        ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(tg),
+    if o is None:
+        _check("bsfa_attn_bwd", library().bsfa_attn_bwd(
+            ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(tg),
+            ctypes.c_void_p(lse.data_ptr()), lse.stride(0), plan.handle, float(scale),
+            ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()),
+            ctypes.c_void_p(delta.data_ptr()), _stream_handle(stream)))
+        return dq, dk, dv
+    if o.dtype != torch.float32:
+        raise ValueError("o must be the forward's fp32 output (attn_fwd(..., out_dtype=torch.float32))")
+    if tuple(o.shape) != (sq, hq, d):
+        raise ValueError(f"o shape {tuple(o.shape)} does not match the plan ({sq}, {hq}, {d})")
+    to = _tview(o)
+    _check("bsfa_attn_bwd_o32", library().bsfa_attn_bwd_o32(
+        ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(tg), ctypes.byref(to),
         ctypes.c_void_p(lse.data_ptr()), lse.stride(0), plan.handle, float(scale),
         ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()),
         ctypes.c_void_p(delta.data_ptr()), _stream_handle(stream)))

@@ -19,7 +19,9 @@
 //
 // Design (own, for CDNA4):
 //   * Kernels 1 and 2 are one kernel body: kernel 1 forms only S^T and dP^T and sums
-//     P dP per query row; kernel 2 reads that D and adds the dQ product.
+//     P dP per query row; kernel 2 reads that D and adds the dQ product.  A call that
+//     passes the forward's fp32 O skips kernel 1: kernel 2 forms D_i = dO_i . O_i from
+//     it (the fp32 value, without the bf16 output's rounding) and stores it for kernel 3.
 //   * Kernel 2 mirrors the forward's transposed products: S^T = K Q^T and
 //     dP^T = V dO^T with Q and dO held as B operands, so a lane owns one query column
 //     and its LSE_i, D_i are scalars; dQ^T += K^T dS^T takes K^T from the LDS tile with
@@ -363,10 +365,13 @@ __device__ __forceinline__ void delta_step(char *__restrict__ kd, char *__restri
             dsum = __builtin_fmaf(__builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, nl)), dp[b][r], dsum);
 }
 
-// DELTA: kernel 1 (D_i = sum_j P_ij dP_ij into `delta`); else kernel 2 (dQ, reading D).
-template <int D, bool DELTA>
-__global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
+// MODE 0: kernel 1 (D_i = sum_j P_ij dP_ij into `delta`); 1: kernel 2 (dQ, reading D);
+// 2: kernel 2 taking D_i = dO_i . O_i from the forward's fp32 O (and storing it in
+// `delta` for kernel 3), when the call has it.
+template <int D, int MODE>
+__device__ __forceinline__ void dq_body(const BwdArgs &a)
 {
+    constexpr bool DELTA = MODE == 0;
     using C = BCfg<D>;
     using L = DqTiles<D>;
     __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
@@ -391,7 +396,28 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
     // kernel 1: this lane's partial sum of P dP (lanes l and l ^ 32 cover the two halves
     // of each 64-key step); kernel 2: D_i of this lane's row as kernel 1 stored it
     float dlt = 0.f;
-    if constexpr (!DELTA) dlt = qvalid ? a.delta[(int64_t)h * a.lse_sh + qrow] : 0.f;
+    if constexpr (MODE == 1) dlt = qvalid ? a.delta[(int64_t)h * a.lse_sh + qrow] : 0.f;
+    if constexpr (MODE == 2) {
+        // this lane's half of the row's dims (16 ks + 8 hh .. + 7, as gf holds dO), then
+        // the other half from lane l ^ 32
+        float part = 0.f;
+        if (qvalid) {
+            const float *orow = a.o + (int64_t)qrow * a.o_st + (int64_t)h * a.o_sh;
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+                const f32x4 o0 = *(const f32x4 *)(orow + 16 * ks + 8 * hh);
+                const f32x4 o1 = *(const f32x4 *)(orow + 16 * ks + 8 * hh + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    part = __builtin_fmaf((float)gf[ks][e], o0[e], part);
+                    part = __builtin_fmaf((float)gf[ks][4 + e], o1[e], part);
+                }
+            }
+        }
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(part), __float_as_int(part), false, false);
+        dlt = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+        if (qvalid && hh == 0) a.delta[(int64_t)h * a.lse_sh + qrow] = dlt;
+    }
     f32x16 acc[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
@@ -481,6 +507,18 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
                 *(f32x4 *)(out + 32 * db + 8 * g4 + 4 * hh) = w;
             }
     }
+}
+
+template <int D, bool DELTA>
+__global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(const BwdArgs a)
+{
+    dq_body<D, DELTA ? 0 : 1>(a);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2) bwd_dq_o32_kernel(const BwdArgs a)
+{
+    dq_body<D, 2>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -726,7 +764,9 @@ __global__ void __launch_bounds__(2 * kThreads, 1) bwd_dkdv2_kernel(const BwdArg
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream)
 {
-    if (a.sq > 0) {
+    if (a.sq > 0 && a.o) {
+        hipLaunchKernelGGL(bwd_dq_o32_kernel<D>, dim3(a.n_qt * a.hq), dim3(kThreads), 0, stream, a);
+    } else if (a.sq > 0) {
         hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(a.n_qt * a.hq), dim3(kThreads), 0, stream, a);
         hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(a.n_qt * a.hq), dim3(kThreads), 0, stream, a);
     }

@@ -212,6 +212,8 @@ struct BwdArgs {
     float scale, c;                      // c = scale * log2(e)
     DeviceMeta meta;
     int32_t n_entries, n_pieces;
+    const float *o;                      // the forward's fp32 O (D_i = dO_i . O_i), or null
+    int32_t o_st, o_sh;
 };
 hipError_t launch_attn_bwd(const BwdArgs &a, int d, hipStream_t stream);
 

@@ -863,8 +863,11 @@ bsfa_status bsfa_attn_fwd_noalloc(const bsfa_tensor *q, const bsfa_tensor *k, co
     return bsfa_attn_fwd(q, k, v, p, scale, o, lse, lse_stride_head, ws, (int64_t)kStaticWorkspaceBytes, stream);
 }
 
-bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
-                          const bsfa_tensor *dout, const float *lse, int64_t lse_stride_head,
+namespace {
+
+// The backward; o (the forward's fp32 O) may be null: D then comes from its own pass.
+bsfa_status attn_bwd_impl(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
+                          const bsfa_tensor *dout, const bsfa_tensor *o, const float *lse, int64_t lse_stride_head,
                           const bsfa_plan *p, float scale, float *dq, float *dk, float *dv, float *delta,
                           void *stream)
 {
@@ -892,6 +895,14 @@ bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
         if (ts[t]->stride_tok > (1 << 24) || ts[t]->stride_head > INT32_MAX) return BSFA_ERR_UNSUPPORTED;
     }
     if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(delta)) return BSFA_ERR_ALIGN;
+    if (o && p->sq > 0) {
+        // fp32 [sq, hq, d]: 16-byte rows, a row never overlapped by the next
+        if (!o->ptr) return BSFA_ERR_ARG;
+        if (!aligned16(o->ptr) || !stride_ok(o->stride_tok, true) || !stride_ok(o->stride_head, true))
+            return BSFA_ERR_ALIGN;
+        if (o->stride_tok < p->d || (p->hq > 1 && o->stride_head < p->d)) return BSFA_ERR_SHAPE;
+        if (o->stride_tok > (1 << 24) || o->stride_head > INT32_MAX) return BSFA_ERR_UNSUPPORTED;
+    }
     BwdArgs a{};
     a.q = q->ptr;
     a.k = k->ptr;
@@ -923,6 +934,11 @@ bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     a.meta = p->dev;
     a.n_entries = (int32_t)p->nnz();
     a.n_pieces = (int32_t)p->npieces();
+    if (o && p->sq > 0) {
+        a.o = (const float *)o->ptr;
+        a.o_st = (int32_t)o->stride_tok;
+        a.o_sh = (int32_t)o->stride_head;
+    }
     const hipStream_t s = (hipStream_t)stream;
     if (s != p->ustream) {
         std::lock_guard<std::mutex> lk(p->streams_mu);
@@ -938,6 +954,25 @@ bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
     if (rs != BSFA_OK) return rs;
     if (launch_attn_bwd(a, p->d, s) != hipSuccess) return BSFA_ERR_HIP;
     return BSFA_OK;
+}
+
+}  // namespace
+
+bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
+                          const bsfa_tensor *dout, const float *lse, int64_t lse_stride_head,
+                          const bsfa_plan *p, float scale, float *dq, float *dk, float *dv, float *delta,
+                          void *stream)
+{
+    return attn_bwd_impl(q, k, v, dout, nullptr, lse, lse_stride_head, p, scale, dq, dk, dv, delta, stream);
+}
+
+bsfa_status bsfa_attn_bwd_o32(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
+                              const bsfa_tensor *dout, const bsfa_tensor *o, const float *lse,
+                              int64_t lse_stride_head, const bsfa_plan *p, float scale, float *dq, float *dk,
+                              float *dv, float *delta, void *stream)
+{
+    if (!o) return BSFA_ERR_ARG;
+    return attn_bwd_impl(q, k, v, dout, o, lse, lse_stride_head, p, scale, dq, dk, dv, delta, stream);
 }
 
 bsfa_status bsfa_attn_merge(const void *const *o_parts, const float *const *lse_parts, int32_t n,

@@ -282,6 +282,18 @@ bsfa_status bsfa_attn_bwd(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa
                           const bsfa_plan *plan, float scale, float *dq, float *dk, float *dv,
                           float *delta, void *stream);
 
+/* bsfa_attn_bwd given the forward's fp32 output o (bsfa_attn_fwd_typed with
+ * BSFA_DTYPE_F32, same inputs and plan): D_i = dO_i . O_i is formed from it (the fp32
+ * value the bf16 output is rounded from, so the bf16 rounding stays out of D) inside
+ * the dQ kernel, and the separate D pass is skipped (two kernels instead of three).
+ * o: fp32 [sq, hq, d], 16-byte aligned, strides multiples of 4 elements, stride_tok >= d;
+ * may be NULL's ptr only when sq == 0.  delta still receives D.  Everything else, errors
+ * included, as bsfa_attn_bwd; BSFA_ERR_ARG for a NULL o. */
+bsfa_status bsfa_attn_bwd_o32(const bsfa_tensor *q, const bsfa_tensor *k, const bsfa_tensor *v,
+                              const bsfa_tensor *dout, const bsfa_tensor *o, const float *lse,
+                              int64_t lse_stride_head, const bsfa_plan *plan, float scale, float *dq,
+                              float *dk, float *dv, float *delta, void *stream);
+
 /* ---- merge of KV-split partials ([UA] 3.2) -----------------------------------
  * For n partial results (O_t, LSE_t) of the same queries over disjoint key sets:
  *   M = max_t LSE_t, LSE = M + ln sum_t exp(LSE_t - M), O = sum_t exp(LSE_t - LSE) O_t;

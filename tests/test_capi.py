@@ -269,6 +269,9 @@ def test_backward_rejects_bad_arguments():
     assert call(p, lse=None) == 1      # no LSE
     assert call(p, delta=None) == 1    # no delta scratch
     assert call(p) == 8                # not uploaded
+    assert lib.bsfa_attn_bwd_o32(*tp, None, buf, 64, p.handle, 0.1, buf, buf, buf, buf, None) == 1  # no O
+    o = api.Tensor(ctypes.c_void_p(16), 8, 8)
+    assert lib.bsfa_attn_bwd_o32(*tp, ctypes.byref(o), buf, 64, p.handle, 0.1, buf, buf, buf, buf, None) == 8
 
 
 def test_device_compiler_rejects_bad_arguments():
