@@ -1,7 +1,8 @@
 /* A C99 consumer of libbsfa.so with no Python and no torch: builds a varlen causal plan
  * through the C ABI, runs the forward on HIP device buffers it allocates itself and
  * writes O and LSE for the Python test to compare with the oracle.  Also checks that
- * invalid calls return their documented status codes before touching the GPU.
+ * invalid calls return their documented status codes before touching the GPU, and that
+ * the typed entry point's fp32 O rounds to the bf16 O bit for bit with the same LSE.
  *
  * usage: abi_forward DIR
  *   DIR/case.txt: sq hq hkv d n_docs scale, then n_docs + 1 cu_seqlens
@@ -110,6 +111,33 @@ int main(int argc, char **argv)
         return fail("hipMemcpy", "outputs");
     if (!write_file(dir, "o.bin", o, nq * 2) || !write_file(dir, "lse.bin", lse, (size_t)hq * sq * 4))
         return fail("write", "o/lse.bin");
+
+    /* the typed entry point: fp32 O rounds (to nearest even) to the bf16 O, same LSE */
+    void *dO32 = NULL, *dl32 = NULL;
+    if (hipMalloc(&dO32, nq * 4) != hipSuccess || hipMalloc(&dl32, (size_t)hq * sq * 4) != hipSuccess)
+        return fail("hipMalloc", "fp32 output");
+    bsfa_tensor to32 = {dO32, (int64_t)hq * d, d};
+    if (bsfa_attn_fwd_typed(&tq, &tk, &tv, plan, scale, &to32, 7, (float *)dl32, sq, NULL, 0, NULL) != BSFA_ERR_ARG)
+        return fail("status", "an unknown output type must give BSFA_ERR_ARG");
+    if ((st = bsfa_attn_fwd_typed(&tq, &tk, &tv, plan, scale, &to32, BSFA_DTYPE_F32, (float *)dl32, sq, NULL, 0,
+                                  NULL)) != BSFA_OK)
+        return fail("bsfa_attn_fwd_typed", bsfa_status_str(st));
+    if (hipDeviceSynchronize() != hipSuccess) return fail("hipDeviceSynchronize", "fp32 forward");
+    uint32_t *o32 = (uint32_t *)malloc(nq * 4);
+    float *lse32 = (float *)malloc((size_t)hq * sq * 4);
+    if (hipMemcpy(o32, dO32, nq * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(lse32, dl32, (size_t)hq * sq * 4, hipMemcpyDeviceToHost) != hipSuccess)
+        return fail("hipMemcpy", "fp32 outputs");
+    for (size_t i = 0; i < nq; ++i) {
+        const uint32_t b = o32[i];
+        const uint16_t r = (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);   /* finite values */
+        if (r != o[i]) return fail("fp32 O", "does not round to the bf16 O");
+    }
+    if (memcmp(lse32, lse, (size_t)hq * sq * 4) != 0) return fail("fp32 O", "LSE differs from the bf16 call's");
+    hipFree(dO32);
+    hipFree(dl32);
+    free(o32);
+    free(lse32);
     bsfa_plan_destroy(plan);
     hipFree(dq);
     hipFree(dk);

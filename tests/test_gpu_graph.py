@@ -78,10 +78,12 @@ def test_forward_replayed_from_a_graph(noalloc):
     plan.close()
 
 
-def test_backward_and_merge_replayed_from_a_graph():
-    """The three backward kernels and the merge kernel captured once and replayed with new
+@pytest.mark.parametrize("fp32", [False, True])
+def test_backward_and_merge_replayed_from_a_graph(fp32):
+    """The backward kernels and the merge kernel captured once and replayed with new
     inputs; each replay bit-identical to eager calls (none of them clears memory with a
-    memset node: every output element is written by a kernel)."""
+    memset node: every output element is written by a kernel).  fp32: the backward from
+    the forward's fp32 O (two kernels) and the merge of fp32 partials into an fp32 result."""
     import torch
     rng = np.random.default_rng(93)
     sq, sk, hq, hkv, d = 700, 700, 4, 2, 128
@@ -92,7 +94,8 @@ def test_backward_and_merge_replayed_from_a_graph():
     qb, kb, vb = W.random_inputs(rng, sq, sk, hq, hkv, d)
     q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
     g_o = dev_bf16(W.random_grad(rng, sq, hq, d))
-    o, lse = api.attn_fwd(q, k, v, plan, scale)
+    o, lse = api.attn_fwd(q, k, v, plan, scale, out_dtype=torch.float32 if fp32 else None)
+    o_in = o if fp32 else None
     parts_o = [torch.empty_like(o) for _ in range(3)]
     parts_l = [torch.empty_like(lse) for _ in range(3)]
     bufs = {n: torch.empty(s, dtype=torch.float32, device="cuda")
@@ -100,7 +103,8 @@ def test_backward_and_merge_replayed_from_a_graph():
     m_o, m_l = torch.empty_like(o), torch.empty_like(lse)
 
     def work(dst, mo, ml):
-        api.attn_bwd(q, k, v, g_o, lse, plan, scale, dq=dst["dq"], dk=dst["dk"], dv=dst["dv"], delta=dst["delta"])
+        api.attn_bwd(q, k, v, g_o, lse, plan, scale, dq=dst["dq"], dk=dst["dk"], dv=dst["dv"], delta=dst["delta"],
+                     o=o_in)
         api.attn_merge(parts_o, parts_l, out=mo, lse=ml)
 
     work(bufs, m_o, m_l)   # eager warm-up
@@ -120,7 +124,7 @@ def test_backward_and_merge_replayed_from_a_graph():
         g_o.copy_(dev_bf16(W.random_grad(rr, sq, hq, d)))
         api.attn_fwd(q, k, v, plan, scale, out=o, lse=lse)
         for t in range(3):
-            parts_o[t].copy_(dev_bf16(W.random_grad(rr, sq, hq, d)))
+            parts_o[t].copy_(dev_bf16(W.random_grad(rr, sq, hq, d)))     # (converted when fp32)
             parts_l[t].copy_(torch.from_numpy(rr.standard_normal((hq, sq)).astype(np.float32)).cuda())
         torch.cuda.synchronize()
         g.replay()
@@ -129,7 +133,8 @@ def test_backward_and_merge_replayed_from_a_graph():
         torch.cuda.synchronize()
         for n in bufs:
             assert torch.equal(bufs[n], ref[n]), f"replay {r}: {n} differs from eager"
-        assert torch.equal(m_o.view(torch.int16), r_o.view(torch.int16)) and torch.equal(m_l, r_l), \
+        bits = torch.int32 if fp32 else torch.int16
+        assert torch.equal(m_o.view(bits), r_o.view(bits)) and torch.equal(m_l, r_l), \
             f"replay {r}: merge differs from eager"
         say(f"replay {r}: gradients and merge bit-identical to the eager calls")
     del g
