@@ -88,6 +88,27 @@ def test_bwd_from_fp32_o_plans(kind):
     check_grads(run_o32(qb, kb, vb, gb, slices, 0.1), oracle.attn_bwd(qb, kb, vb, gb, slices, 0.1), what)
 
 
+def test_bwd_from_fp32_o_masked_rows_and_empty_mask():
+    """Rows without keys (O = 0, LSE = -inf, D = 0), keys no query reaches, an empty mask."""
+    sq, sk, d = 384, 256, 128
+    rng = np.random.default_rng(10)
+    qb, kb, vb = W.random_inputs(rng, sq, sk, 2, 2, d)
+    cases = [("masked rows", [(0, 128, 0, 256, 1), (256, 384, 100, 140, 1)]),
+             ("unreached keys", [(0, 128, 0, 100, 0), (256, 384, 100, 140, 1)]),
+             ("empty mask", [])]
+    for i, (what, slices) in enumerate(cases):
+        gb = W.random_grad(np.random.default_rng(1003 + i), sq, 2, d)
+        say(f"bwd from fp32 O, {what}")
+        got = run_o32(qb, kb, vb, gb, slices, 0.1)
+        check_grads(got, oracle.attn_bwd(qb, kb, vb, gb, slices, 0.1), f"bwd from fp32 O, {what}")
+        if what == "masked rows":
+            assert np.all(got[0][128:256] == 0), "rows without keys have dQ = 0"
+        if what == "unreached keys":
+            assert np.all(got[1][140:] == 0) and np.all(got[2][140:] == 0)
+        if what == "empty mask":
+            assert all(np.all(g == 0) for g in got)
+
+
 def test_bwd_from_fp32_o_at_full_size():
     """Varlen causal, 16384 tokens, 16 heads, d 128, backward from the fp32 O: sampled dQ
     rows and dK, dV keys against the oracle, the sum_j dV identity, determinism, and D
