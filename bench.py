@@ -195,8 +195,75 @@ def headline(args, api, W):
     kt = event_times(lambda: api.attn_fwd(q, k, v, plan, w.scale, out=o, lse=lse, stream=stream),
                      max(args.steps, 20), stream)
     kernel_ms = float(np.mean(kt))
+    # the core clock the forward runs at (the published peak assumes 2.4 GHz)
+    clock = gfx_clock(lambda: api.attn_fwd(q, k, v, plan, w.scale, out=o, lse=lse, stream=stream), 2.0)
     plan.close()
-    return w, info, flops, ms_per_step, kernel_ms, host_ms
+    return w, info, flops, ms_per_step, kernel_ms, host_ms, clock
+
+
+def gfx_clock(fn, seconds):
+    """GPU core clock while fn() runs back to back: the driver's GPU metrics table
+    (current_gfxclks, MHz, one value per XCD) read through amdsmi every 10 ms over
+    `seconds` of launches.  The table refreshes coarsely, so only the samples of the
+    window's second half count.  None when amdsmi is not usable here."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception:
+        return None
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+        h = None
+        for x in handles:
+            try:
+                if bus is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(x).split(":")[1], 16) == bus:
+                    h = x
+            except Exception:
+                pass
+        if h is None:
+            if len(handles) != 1:
+                return None
+            h = handles[0]
+        samples, stop = [], [False]
+
+        def sampler():
+            while not stop[0]:
+                try:
+                    c = amdsmi.amdsmi_get_gpu_metrics_info(h).get("current_gfxclks")
+                    if isinstance(c, list):
+                        vals = [v for v in c if isinstance(v, int) and 0 < v < 10000]
+                        if vals:
+                            samples.append((time.perf_counter(), vals))
+                except Exception:
+                    pass
+                time.sleep(0.01)
+
+        th = threading.Thread(target=sampler, daemon=True)
+        t0 = time.perf_counter()
+        th.start()
+        while time.perf_counter() < t0 + seconds:
+            for _ in range(20):
+                fn()
+            torch.cuda.synchronize()
+        stop[0] = True
+        th.join()
+        late = [v for t, v in samples if t >= t0 + seconds / 2]
+        n = min((len(v) for v in late), default=0)
+        if not late or n == 0:
+            return None
+        per_xcd = np.mean(np.array([v[:n] for v in late], dtype=np.float64), axis=0)
+        return {"mhz_mean": float(np.mean(per_xcd)), "mhz_per_xcd": [int(round(x)) for x in per_xcd],
+                "samples": len(late)}
+    except Exception:
+        return None
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
 
 def sustain(f, seconds):
@@ -640,12 +707,15 @@ def main():
         counter_pass(api, W)
         return
 
-    w, info, flops, ms_per_step, kernel_ms, host_ms = headline(args, api, W)
+    w, info, flops, ms_per_step, kernel_ms, host_ms, clock = headline(args, api, W)
     value = flops / (ms_per_step * 1e-3) * 1e-12
     achieved = flops / (kernel_ms * 1e-3) * 1e-12
     log(f"headline: step {ms_per_step:.4f} ms ({value:.1f} TFLOPS; host issue {host_ms:.4f} ms), "
         f"forward kernel {kernel_ms:.4f} ms "
         f"({achieved:.1f} TFLOPS, {achieved / PEAK_BF16_TFLOPS:.3f} of peak)")
+    if clock is not None:
+        log(f"clock under the headline forward: {clock['mhz_mean']:.0f} MHz (XCDs {clock['mhz_per_xcd']}); "
+            f"{achieved / (PEAK_BF16_TFLOPS * clock['mhz_mean'] / 2400.0):.3f} of the bf16 peak at that clock")
     others = {} if args.quick else other_workloads(api, W, warm_s=0.5 * args.prewarm_s)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
     if not args.no_cpu_baseline:
@@ -690,6 +760,11 @@ def main():
                      "mfma_busy_source": "rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs), "
                                          "committed counter summary; null once the kernel changed"},
         "cpu_baseline": cpu,
+        "clock": None if clock is None else dict(
+            clock, source="amdsmi GPU metrics (current_gfxclks per XCD) sampled while the headline forward "
+                          "runs back to back, after the timed steps",
+            peak_at_measured_clock=PEAK_BF16_TFLOPS * clock["mhz_mean"] / 2400.0,
+            frac_at_measured_clock=achieved / (PEAK_BF16_TFLOPS * clock["mhz_mean"] / 2400.0)),
         "other_workloads": others,
     }
     print(json.dumps(result), flush=True)
