@@ -52,7 +52,7 @@ def assert_rounds_to(o16, l16, o32, l32, what):
     assert torch.equal(l16, l32), f"{what}: LSE differs between the two output types"
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_fp32_output_rounds_to_the_bf16_output_workloads(cfg):
     w = W.WORKLOADS[cfg]()
     say(f"fp32 vs bf16 O: {w.name}")
@@ -86,10 +86,11 @@ def test_fp32_output_rounds_to_the_bf16_output_plans(kind):
     compare(o32.cpu().numpy(), l32.cpu().numpy().T, o_ref, lse_ref.T, f"{kind} fp32 O")
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(64))
 def test_fp32_output_sweep_meets_the_bar(seed):
-    """The forward sweep's cases, with fp32 O: all of them, the two whose bf16 output is a
-    known breach included, meet max|dO| <= 1e-2 and max|dLSE| <= 1e-3."""
+    """The forward sweep's cases and 40 more of its generator, with fp32 O: all of them, the
+    two whose bf16 output is a known breach included, meet max|dO| <= 1e-2 and
+    max|dLSE| <= 1e-3."""
     import torch
     _, sq, sk, hq, hkv, d, bk, slices, scale, qb, kb, vb = draw_case(seed)
     what = f"sweep fwd fp32 O seed={seed} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} bk={bk}"
