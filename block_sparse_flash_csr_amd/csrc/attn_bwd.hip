@@ -397,27 +397,6 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a)
     // of each 64-key step); kernel 2: D_i of this lane's row as kernel 1 stored it
     float dlt = 0.f;
     if constexpr (MODE == 1) dlt = qvalid ? a.delta[(int64_t)h * a.lse_sh + qrow] : 0.f;
-    if constexpr (MODE == 2) {
-        // this lane's half of the row's dims (16 ks + 8 hh .. + 7, as gf holds dO), then
-        // the other half from lane l ^ 32
-        float part = 0.f;
-        if (qvalid) {
-            const float *orow = a.o + (int64_t)qrow * a.o_st + (int64_t)h * a.o_sh;
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                const f32x4 o0 = *(const f32x4 *)(orow + 16 * ks + 8 * hh);
-                const f32x4 o1 = *(const f32x4 *)(orow + 16 * ks + 8 * hh + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    part = __builtin_fmaf((float)gf[ks][e], o0[e], part);
-                    part = __builtin_fmaf((float)gf[ks][4 + e], o1[e], part);
-                }
-            }
-        }
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(part), __float_as_int(part), false, false);
-        dlt = __int_as_float(sw[0]) + __int_as_float(sw[1]);
-        if (qvalid && hh == 0) a.delta[(int64_t)h * a.lse_sh + qrow] = dlt;
-    }
     f32x16 acc[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
@@ -443,6 +422,28 @@ __device__ __forceinline__ void dq_body(const BwdArgs &a)
         const int kend = min(kv0 + a.bk_plan, a.sk);
         tile_dma<D>(rsrc_of(kh, a.k_st, kv0, kend), a.k_st, smem + L::K0, wave, lane);
         tile_dma<D>(rsrc_of(vh, a.v_st, kv0, kend), a.v_st, smem + L::V0, wave, lane);
+    }
+    // (after the first tiles' loads are issued, so that the O rows arrive beside them)
+    if constexpr (MODE == 2) {
+        // this lane's half of the row's dims (16 ks + 8 hh .. + 7, as gf holds dO), then
+        // the other half from lane l ^ 32
+        float part = 0.f;
+        if (qvalid) {
+            const float *orow = a.o + (int64_t)qrow * a.o_st + (int64_t)h * a.o_sh;
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+                const f32x4 o0 = *(const f32x4 *)(orow + 16 * ks + 8 * hh);
+                const f32x4 o1 = *(const f32x4 *)(orow + 16 * ks + 8 * hh + 4);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    part = __builtin_fmaf((float)gf[ks][x], o0[x], part);
+                    part = __builtin_fmaf((float)gf[ks][4 + x], o1[x], part);
+                }
+            }
+        }
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(part), __float_as_int(part), false, false);
+        dlt = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+        if (qvalid && hh == 0) a.delta[(int64_t)h * a.lse_sh + qrow] = dlt;
     }
     while (e < e1) {
         const i32x4 en = ((cptr_i32x4)a.meta.entries)[e];   // col, piece_begin, piece_count, tag
