@@ -558,7 +558,8 @@ COUNTER_ORDER = ((1, 20), (2, 20), (3, 20), (4, 5), (5, 5))
 def counter_pass(api, W):
     """Fixed launch sequence for hardware-counter runs: for each workload in
     COUNTER_ORDER, its forward launched that many times back to back (workload 5: the
-    8 chunk forwards and the merge, repeated), and after workload 2 its backward 5 times.
+    8 chunk forwards and the merge, repeated), and after workload 2 its backward 5 times,
+    one forward with fp32 output and the backward from that O 5 times.
     No other forward or merge kernel runs, so a counter file maps onto workloads by
     dispatch order and kernel name."""
     import torch
@@ -595,7 +596,14 @@ def counter_pass(api, W):
                 api.attn_bwd(q, k, v, g, lse, plans[0], w.scale, stream=stream)
             torch.cuda.synchronize()
             log(f"counter pass: backward of workload {cfg} x 5")
-            del g
+            # the backward from the forward's fp32 O (dQ with D from O, dK/dV) x 5, after one
+            # forward with fp32 output (a kernel of its own name)
+            o32, lse32 = api.attn_fwd(q, k, v, plans[0], w.scale, stream=stream, out_dtype=torch.float32)
+            for _ in range(5):
+                api.attn_bwd(q, k, v, g, lse32, plans[0], w.scale, stream=stream, o=o32)
+            torch.cuda.synchronize()
+            log(f"counter pass: backward from the fp32 O of workload {cfg} x 5")
+            del g, o32, lse32
         for p in plans:
             p.close()
         del q, k, v
