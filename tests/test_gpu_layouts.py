@@ -115,3 +115,42 @@ def test_merge_of_strided_partials_equals_contiguous():
     om, lm = oracle.merge(po, pl)
     o_gpu = W.bf16_to_f32(host_bits(o)).transpose(1, 0, 2).reshape(h * t, d)
     compare(o_gpu, lse.contiguous().cpu().numpy().reshape(h * t), om, lm, "strided merge")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp32_outputs_as_views_equal_contiguous(d):
+    """An fp32 O written into a wider fp32 buffer (its token stride padded by 4 elements,
+    heads interleaved with a spare head), a backward from that view, and a merge of fp32
+    partials that are views with an fp32 result view: each equal, bit for bit, to the same
+    call on contiguous tensors."""
+    import torch
+    rng = np.random.default_rng(71 + d)
+    s, hq, hkv = 300, 4, 2
+    qb, kb, vb = W.random_inputs(rng, s, s, hq, hkv, d)
+    gb = W.random_grad(rng, s, hq, d)
+    q, k, v, g = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), dev_bf16(gb)
+    plan = api.Plan.from_slices(W.random_slices(rng, s, s, 6) + [(0, s, 0, s, 1)], s, s, hq, hkv, d).upload()
+    say(f"fp32 outputs as views, d={d}")
+    wide = torch.full((s, hq + 1, d + 4), float("nan"), dtype=torch.float32, device="cuda")
+    ov = wide[:, 1:, :d]
+    assert not ov.is_contiguous() and ov.stride(0) % 4 == 0 and ov.stride(1) % 4 == 0
+    o_c, l_c = api.attn_fwd(q, k, v, plan, 0.1, out_dtype=torch.float32)
+    o_v, l_v = api.attn_fwd(q, k, v, plan, 0.1, out=ov)
+    g_c = api.attn_bwd(q, k, v, g, l_c, plan, 0.1, o=o_c)
+    g_v = api.attn_bwd(q, k, v, g, l_v, plan, 0.1, o=ov)
+    torch.cuda.synchronize()
+    assert torch.equal(o_c, ov) and torch.equal(l_c, l_v)
+    assert torch.isnan(wide[:, 0]).all() and torch.isnan(wide[:, :, d:]).all(), "wrote outside the view"
+    for x, y in zip(g_c, g_v):
+        assert torch.equal(x, y)
+    # merge: three fp32 partials as views of one buffer, fp32 result as a view
+    parts_buf = torch.from_numpy(rng.standard_normal((s, 3 * hq, d + 8)).astype(np.float32)).cuda()
+    parts = [parts_buf[:, i * hq:(i + 1) * hq, :d] for i in range(3)]
+    lses = [torch.from_numpy(rng.standard_normal((hq, s)).astype(np.float32)).cuda() for _ in range(3)]
+    m_c, ml_c = api.attn_merge([p.contiguous() for p in parts], lses, out_dtype=torch.float32)
+    res = torch.full((s, hq, d + 4), float("nan"), dtype=torch.float32, device="cuda")
+    m_v, ml_v = api.attn_merge(parts, lses, out=res[:, :, :d])
+    torch.cuda.synchronize()
+    assert torch.equal(m_c, res[:, :, :d]) and torch.equal(ml_c, ml_v)
+    assert torch.isnan(res[:, :, d:]).all(), "merge wrote outside the view"
+    plan.close()
