@@ -339,6 +339,10 @@ def other_workloads(api, W, reps=10, warm_s=0.5):
     out[name] = {"kernel_ms": ms, "tflops": fl / ms * 1e-9, "frac_of_peak": fl / ms * 1e-9 / PEAK_BF16_TFLOPS,
                  "pairs_per_head": info["pairs"],
                  "note": "not a reference workload: the headline mask at head dim 64 (vector-bound)"}
+    ctr = counters.get(name)
+    if ctr is not None:
+        out[name].update(mfma_busy_pct=ctr["mfma_busy_pct"], l2_hit_pct=ctr["l2_hit_pct"],
+                         hbm_bytes=ctr["hbm_bytes_per_launch"], hbm_gbs=ctr["hbm_bytes_per_launch"] / ms * 1e-6)
     log(f"{name}: {ms:.3f} ms  {fl / ms * 1e-9:.1f} TFLOPS")
     plan.close()
     del q, k, v, o, lse
@@ -559,7 +563,8 @@ def counter_pass(api, W):
     """Fixed launch sequence for hardware-counter runs: for each workload in
     COUNTER_ORDER, its forward launched that many times back to back (workload 5: the
     8 chunk forwards and the merge, repeated), and after workload 2 its backward 5 times,
-    one forward with fp32 output and the backward from that O 5 times.
+    one forward with fp32 output and the backward from that O 5 times, then the headline
+    mask at head dim 64 20 times.
     No other forward or merge kernel runs, so a counter file maps onto workloads by
     dispatch order and kernel name."""
     import torch
@@ -604,6 +609,16 @@ def counter_pass(api, W):
             torch.cuda.synchronize()
             log(f"counter pass: backward from the fp32 O of workload {cfg} x 5")
             del g, o32, lse32
+            # the headline mask at head dim 64 x 20 (the benchmark's d = 64 line)
+            q64, k64, v64 = (W.device_normal_bf16((w.sq, w.hq, 64), sd) for sd in (641, 642, 643))
+            p64 = api.Plan.from_slices(w.slices, w.sq, w.sk, w.hq, w.hkv, 64).upload(stream)
+            o64 = torch.empty((w.sq, w.hq, 64), dtype=torch.bfloat16, device="cuda")
+            for _ in range(20):
+                api.attn_fwd(q64, k64, v64, p64, 1.0 / np.sqrt(64), out=o64, lse=lse, stream=stream)
+            torch.cuda.synchronize()
+            log("counter pass: the headline mask at d = 64 x 20")
+            p64.close()
+            del q64, k64, v64, o64
         for p in plans:
             p.close()
         del q, k, v
