@@ -86,21 +86,25 @@ def test_fp32_output_rounds_to_the_bf16_output_plans(kind):
     compare(o32.cpu().numpy(), l32.cpu().numpy().T, o_ref, lse_ref.T, f"{kind} fp32 O")
 
 
-@pytest.mark.parametrize("seed", range(64))
+@pytest.mark.parametrize("seed", range(256))
 def test_fp32_output_sweep_meets_the_bar(seed):
-    """The forward sweep's cases and 40 more of its generator, with fp32 O: all of them, the
-    two whose bf16 output is a known breach included, meet max|dO| <= 1e-2 and
-    max|dLSE| <= 1e-3."""
+    """The forward sweep's cases and 232 more of its generator, with fp32 O: all of them,
+    the two whose bf16 output is a known breach included, meet max|dO| <= 1e-2 and
+    max|dLSE| <= 1e-3; the bf16 call's output is that fp32 output rounded to nearest even,
+    bit for bit, and its LSE is the same, so a bf16 output that misses the 1e-2 bar misses
+    it by its own rounding only (at most half a bf16 step of |O|)."""
     import torch
     _, sq, sk, hq, hkv, d, bk, slices, scale, qb, kb, vb = draw_case(seed)
     what = f"sweep fwd fp32 O seed={seed} sq={sq} sk={sk} hq={hq} hkv={hkv} d={d} bk={bk}"
     say(what)
     plan = api.Plan.from_slices(slices, sq, sk, hq, hkv, d, bk=bk).upload()
-    o, lse = api.attn_fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), plan, scale, out_dtype=torch.float32)
-    torch.cuda.synchronize()
+    o16, l16, o, lse = both_outputs(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), plan, scale)
     plan.close()
+    assert_rounds_to(o16, l16, o, lse, what)
     o_ref, lse_ref = oracle.attn_fwd(qb, kb, vb, slices, scale)
     compare(o.cpu().numpy(), lse.cpu().numpy().T, o_ref, lse_ref.T, what)
+    err16 = float(np.max(np.abs(W.bf16_to_f32(host_bits(o16)).astype(np.float64) - o_ref))) if o_ref.size else 0.0
+    say(f"{what}: bf16 output max|dO| {err16:.3e}{' (beyond 1e-2 by its rounding)' if err16 > 1e-2 else ''}")
 
 
 def test_fp32_output_one_hot_rows_d64():
