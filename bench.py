@@ -280,6 +280,32 @@ def sustain(f, seconds):
             return
 
 
+def gemm_reference(W, n=8192, reps=20, warm_s=1.0):
+    """What dense bf16 matrix work reaches on this part in the same run: torch.mm of two
+    contiguous n x n bf16 matrices (the vendor's tuned GEMM library), event-timed after
+    warm_s seconds of untimed launches, with the core clock sampled while it runs.  A
+    measured reference beside the attention kernel's fraction of the published peak; not
+    part of the path."""
+    import torch
+    a = W.device_normal_bf16((n, n), 811)
+    b = W.device_normal_bf16((n, n), 812)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    f = lambda: torch.mm(a, b, out=c)
+    sustain(f, warm_s)
+    ms = float(np.median(event_times(f, reps, stream)))
+    clock = gfx_clock(f, 2.0)
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) * 1e-12
+    out = {"op": f"torch.mm bf16 {n}x{n} @ {n}x{n} (fp32 accumulation, bf16 output)",
+           "ms": ms, "tflops": tflops, "frac_of_peak": tflops / PEAK_BF16_TFLOPS,
+           "clock_mhz": None if clock is None else clock["mhz_mean"]}
+    if clock is not None:
+        out["frac_at_measured_clock"] = tflops / (PEAK_BF16_TFLOPS * clock["mhz_mean"] / 2400.0)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def other_workloads(api, W, reps=10, warm_s=0.5):
     """Kernel-time figures of the remaining workloads (event-timed, plan prebuilt, each
     after warm_s seconds of untimed launches of the same call)."""
@@ -740,6 +766,11 @@ def main():
         log(f"clock under the headline forward: {clock['mhz_mean']:.0f} MHz (XCDs {clock['mhz_per_xcd']}); "
             f"{achieved / (PEAK_BF16_TFLOPS * clock['mhz_mean'] / 2400.0):.3f} of the bf16 peak at that clock")
     others = {} if args.quick else other_workloads(api, W, warm_s=0.5 * args.prewarm_s)
+    gemm = gemm_reference(W)
+    log(f"reference bf16 GEMM ({gemm['op']}): {gemm['ms']:.3f} ms, {gemm['tflops']:.1f} TFLOPS, "
+        f"{gemm['frac_of_peak']:.3f} of peak"
+        + ("" if gemm["clock_mhz"] is None else
+           f", clock {gemm['clock_mhz']:.0f} MHz ({gemm['frac_at_measured_clock']:.3f} at that clock)"))
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
     if not args.no_cpu_baseline:
         # the oracle beside every other workload, after all GPU timing (the GPU is idle)
@@ -788,6 +819,7 @@ def main():
                           "runs back to back, after the timed steps",
             peak_at_measured_clock=PEAK_BF16_TFLOPS * clock["mhz_mean"] / 2400.0,
             frac_at_measured_clock=achieved / (PEAK_BF16_TFLOPS * clock["mhz_mean"] / 2400.0)),
+        "gemm_reference": gemm,
         "other_workloads": others,
     }
     print(json.dumps(result), flush=True)
