@@ -350,6 +350,17 @@ def workspace_for(plan: Plan, device="cuda"):
     return torch.empty(n // 4, dtype=torch.float32, device=device)
 
 
+def _on_device(**named):
+    """The library hands these addresses to the GPU as they are: each tensor must live on
+    the current CUDA device (a host tensor's address would reach a kernel)."""
+    import torch
+    dev = torch.cuda.current_device() if torch.cuda.is_available() else None
+    for name, t in named.items():
+        if t is not None and (not t.is_cuda or t.device.index != dev):
+            raise ValueError(f"{name} must be a CUDA tensor on the current device "
+                             f"(cuda:{dev}), got one on {t.device}")
+
+
 DTYPE_BF16, DTYPE_F32 = 0, 1   # element types of O for the typed entry points
 
 
@@ -388,6 +399,9 @@ def attn_fwd(q, k, v, plan: Plan, scale: float, out=None, lse=None, workspace=No
     assert out_dtype is None or out.dtype == out_dtype
     assert tuple(out.shape) == (sq, hq, d)
     assert lse.dtype == torch.float32 and lse.stride(1) == 1 and lse.shape[0] == hq
+    if lse.shape[1] < sq:
+        raise ValueError(f"lse covers {lse.shape[1]} tokens, fewer than the {sq} queries")
+    _on_device(q=q, k=k, v=v, out=out, lse=lse, workspace=workspace)
     if workspace is None and plan.info()["workspace_bytes"] > 0:
         workspace = workspace_for(plan, q.device)
         if stream is not None:
@@ -431,6 +445,9 @@ def attn_bwd(q, k, v, dout, lse, plan: Plan, scale: float, dq=None, dk=None, dv=
         assert t.dtype == torch.bfloat16, f"{name} must be bf16"
     assert q.dtype == torch.bfloat16
     assert lse.dtype == torch.float32 and lse.stride(1) == 1 and lse.shape[0] == hq
+    if lse.shape[1] < sq:
+        raise ValueError(f"lse covers {lse.shape[1]} tokens, fewer than the {sq} queries")
+    _on_device(q=q, k=k, v=v, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv, delta=delta, o=o)
     dev = q.device
     if dq is None:
         dq = torch.empty((sq, hq, d), dtype=torch.float32, device=dev)
@@ -487,9 +504,17 @@ def attn_merge(o_parts, lse_parts, out=None, lse=None, stream=None, out_dtype=No
         out = torch.empty((t, h, d), dtype=out_dtype or torch.bfloat16, device=o_parts[0].device)
     o_code = _dtype_code(out)
     assert out_dtype is None or out.dtype == out_dtype
+    if tuple(out.shape) != (t, h, d):
+        raise ValueError(f"out shape {tuple(out.shape)} does not match the partials ({t}, {h}, {d})")
     if lse is None:
         lse = torch.empty((h, lst), dtype=torch.float32, device=o_parts[0].device)
+    if lse.dtype != torch.float32 or lse.dim() != 2 or lse.shape[0] != h or lse.shape[1] < t \
+            or lse.stride(1) != 1:
+        raise ValueError(f"lse must be fp32 [{h}, >= {t}] with contiguous tokens, got "
+                         f"{lse.dtype} {tuple(lse.shape)}")
     assert lse.stride(0) == lst
+    _on_device(**{f"o_parts[{i}]": p for i, p in enumerate(o_parts)},
+               **{f"lse_parts[{i}]": l for i, l in enumerate(lse_parts)}, out=out, lse=lse)
     optrs = (ctypes.c_void_p * n)(*[p.data_ptr() for p in o_parts])
     lptrs = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lse_parts])
     to = _tview(out)

@@ -181,6 +181,35 @@ def test_merge_binding_rejects_strided_head_dim_and_short_lse():
         api.attn_merge(parts, short)
 
 
+def test_bindings_refuse_host_tensors_and_short_outputs():
+    """Every tensor a kernel touches must be a CUDA tensor of the current device, and the
+    outputs must cover the call's rows; the bindings refuse the rest before any device
+    call (here all tensors are host tensors, so the shape checks must come first)."""
+    import torch
+    sq, sk, hq, hkv, d = 100, 90, 2, 1, 64
+    plan = api.Plan.from_slices([(0, sq, 0, sk, 1)], sq, sk, hq, hkv, d)
+    q = torch.zeros((sq, hq, d), dtype=torch.bfloat16)
+    k = v = torch.zeros((sk, hkv, d), dtype=torch.bfloat16)
+    lse = torch.zeros((hq, sq))
+    with pytest.raises(ValueError, match="lse covers"):
+        api.attn_fwd(q, k, v, plan, 0.1, lse=torch.zeros((hq, 256))[:, :sq - 1])
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        api.attn_fwd(q, k, v, plan, 0.1)
+    with pytest.raises(ValueError, match="lse covers"):
+        api.attn_bwd(q, k, v, q, lse[:, :sq - 1], plan, 0.1)
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        api.attn_bwd(q, k, v, q, lse, plan, 0.1)
+    plan.close()
+    parts = [torch.zeros((8, 2, 128), dtype=torch.bfloat16)] * 2
+    lses = [torch.zeros((2, 8))] * 2
+    with pytest.raises(ValueError, match="out shape"):
+        api.attn_merge(parts, lses, out=torch.zeros((7, 2, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="lse must be"):
+        api.attn_merge(parts, lses, lse=torch.zeros((2, 16))[:, :7])
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        api.attn_merge(parts, lses)
+
+
 def test_rescale_threshold_setting():
     """The conditional-rescale threshold accepts 0..64 (log2 units) and refuses the rest."""
     lib = api.library()
