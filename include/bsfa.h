@@ -20,7 +20,9 @@
  * Conventions for every call:
  *   - Status codes only; nothing throws across this boundary.  Arguments are
  *     validated before any device work is enqueued; a rejected call writes nothing.
- *   - Device pointers are HIP device memory owned by the caller.  "stream" is a
+ *   - Device pointers are HIP device memory of the current device, owned by the
+ *     caller.  The library does not inspect where an address points (a host address
+ *     would reach the kernels as it is); the Python binding checks its tensors.  "stream" is a
  *     hipStream_t passed as void* (NULL = the default stream).  Device work is
  *     enqueued on that stream and the call returns without synchronising.
  *   - Tensors are bf16 with the head dimension contiguous; token and head strides
@@ -299,8 +301,9 @@ bsfa_status bsfa_attn_bwd_o32(const bsfa_tensor *q, const bsfa_tensor *k, const 
  *   M = max_t LSE_t, LSE = M + ln sum_t exp(LSE_t - M), O = sum_t exp(LSE_t - LSE) O_t;
  * rows where every LSE_t is -inf get O = 0, LSE = -inf.
  * o_parts / lse_parts: host arrays of n device pointers; every O_t is a bf16
- * [n_tok, n_head, d] tensor with the strides of o_parts_view, every LSE_t an fp32
- * [n_head, lse_stride_head] array.  o (bf16, strides from o->stride_*) and lse receive
+ * [n_tok, n_head, d] tensor with element strides part_stride_tok and part_stride_head
+ * (multiples of 8, head dim contiguous), every LSE_t an fp32 [n_head, lse_stride_head]
+ * array.  o (bf16, strides from o->stride_*) and lse receive
  * the result and must not overlap any partial.  1 <= n <= BSFA_MERGE_MAX_PARTS,
  * d in {64, 128}, ceil(n_tok / 16) * n_head < 2^31.  With n_tok == 0 or n_head == 0 the
  * call does nothing and returns BSFA_OK (its pointers may then be NULL).  Partials and result are streamed
