@@ -289,11 +289,22 @@ __device__ __forceinline__ uint64_t range_bits(int lo, int hi)
     return upto_hi & ~((1ull << lo) - 1ull);
 }
 
-// One score through the mask: bit off of w keeps it, else -inf.
+// One score through the mask: bit off of w keeps it, else -inf.  At head dim 64, where
+// the vector work binds, the bit is extracted sign-extended and a three-input bitwise
+// select picks the score or -inf (two vector instructions, no compare through VCC and
+// its wait state); at head dim 128 that form measured within noise, and the compiler's
+// own compare-and-select stays.
+template <int D>
 __device__ __forceinline__ float masked(float x, int32_t w, int off)
 {
-    const int32_t keep = (w << (31 - off)) >> 31;
-    return __int_as_float((keep & __float_as_int(x)) | (~keep & __float_as_int(-INFINITY)));
+    if constexpr (D == 64) {
+        const int32_t keep = __builtin_amdgcn_sbfe(w, off, 1);
+        // truth table 0xCA: keep ? x : -inf, bit by bit
+        return __int_as_float(__builtin_amdgcn_bitop3_b32(keep, __float_as_int(x), __float_as_int(-INFINITY), 0xCA));
+    } else {
+        const int32_t keep = (w << (31 - off)) >> 31;
+        return __int_as_float((keep & __float_as_int(x)) | (~keep & __float_as_int(-INFINITY)));
+    }
 }
 
 __device__ __forceinline__ uint64_t piece_bits(int qrow, int base, int q_lo, int q_hi, int k_lo, int k_hi,
@@ -331,6 +342,7 @@ __device__ __forceinline__ uint64_t mask_bits_pf(const Step &cur, const PiecePai
 // Rejected scores become -inf: bit off of the mask word selects between the score and
 // -inf.  off(kb, r) = kb*32 + 8*(r>>2) + (r&3) is the offset of accumulator register r of
 // block kb from base.
+template <int D>
 __device__ __forceinline__ void apply_bits(uint64_t m, f32x16 (&s)[2])
 {
 #pragma unroll
@@ -338,7 +350,7 @@ __device__ __forceinline__ void apply_bits(uint64_t m, f32x16 (&s)[2])
         const int32_t w = (int32_t)(kb ? (uint32_t)(m >> 32) : (uint32_t)m);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            s[kb][r] = masked(s[kb][r], w, 8 * (r >> 2) + (r & 3));
+            s[kb][r] = masked<D>(s[kb][r], w, 8 * (r >> 2) + (r & 3));
         }
     }
 }
@@ -644,7 +656,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs &a)
             __syncthreads();
             f32x16 sA[2], sB[2];
             scores<D>(smem + C::K_OFF0, ln, qf, sA);
-            if (needs_mask(st0)) apply_bits(mask_bits(a, st0, qrow, hh), sA);
+            if (needs_mask(st0)) apply_bits<D>(mask_bits(a, st0, qrow, hh), sA);
             float mxA = tile_max(sA, c), mxB = 0.f;
             acc.m = fmaxf(acc.m, mxA);   // O, l are still zero: start at the first tile's max
 
@@ -685,9 +697,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdArgs &a)
                 step_body<D>(smem + K_FREE, smem + V_NEXT, smem + K_NEXT, smem + V_CUR, kld, has2, vld, has1, ln,
                              wave, qf, cur, c, acc, nxt, mx_raw);
                 if constexpr (kLazyMax<D>) {
-                    if (m1) apply_bits(bits, nxt);   // the maxima are taken only when needed
+                    if (m1) apply_bits<D>(bits, nxt);   // the maxima are taken only when needed
                 } else if (m1) {
-                    apply_bits(bits, nxt);
+                    apply_bits<D>(bits, nxt);
                     mx_nxt = tile_max(nxt, c);
                 } else if (has1) {
                     mx_nxt = wave_cross_half_max(mx_raw) * c;
