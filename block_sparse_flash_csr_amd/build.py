@@ -12,7 +12,7 @@ LIB = os.path.join(HERE, "libbsfa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["capi.cpp", "mask_compile.cpp", "schedule.cpp", "attn_fwd.hip", "attn_merge.hip", "attn_bwd.hip",
-           "mask_dev.hip", "mask_blocks_dev.hip", "plan_dev.hip"]
+           "mask_dev.hip", "mask_blocks_dev.hip", "plan_dev.hip", "dev_sort.hip"]
 # Packed fp32 (v_pk_*_f32) is disabled for every device pass.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -15,9 +15,8 @@
 // exclusive scans give row_ptr and the rows' first pieces; one wave per query tile then
 // writes its entries in key-tile order (a ballot per 64 blocks gives each block its
 // slot).
-#include <hipcub/hipcub.hpp>
-
 #include "dcsr_blocks.h"
+#include "dev_sort.h"
 
 namespace bsfa {
 namespace {
@@ -143,26 +142,18 @@ __global__ void blk_write_kernel(const DcsrBlockArgs a)
 
 }  // namespace
 
-size_t dcsr_blocks_scan_temp_bytes(int32_t n)
-{
-    // a failed query leaves 0: the scan itself then fails and is reported
-    size_t t = 0;
-    if (hipcub::DeviceScan::ExclusiveSum(nullptr, t, (const int32_t *)nullptr, (int32_t *)nullptr, n) != hipSuccess)
-        return 0;
-    return t;
-}
+size_t dcsr_blocks_scan_temp_bytes(int32_t n) { return dev_scan_temp_bytes(n); }
 
 hipError_t launch_dcsr_blocks(const DcsrBlockArgs &a, hipStream_t stream)
 {
     hipLaunchKernelGGL(blk_zero_kernel, dim3(1), dim3(64), 0, stream, a.totals);
     const unsigned rows = (unsigned)((a.n_qt + 1 + 3) / 4);
     hipLaunchKernelGGL(blk_count_kernel, dim3(rows), dim3(kThreadsBlk), 0, stream, a);
-    size_t tb = a.temp_bytes;
-    hipError_t err = hipcub::DeviceScan::ExclusiveSum(a.temp, tb, (const int32_t *)a.row_cnt, a.row_ptr,
-                                                      a.n_qt + 1, stream);
+    hipError_t err = dev_exclusive_scan((const int32_t *)a.row_cnt, a.row_ptr, (int64_t)a.n_qt + 1, a.temp,
+                                        a.temp_bytes, stream);
     if (err != hipSuccess) return err;
-    tb = a.temp_bytes;
-    err = hipcub::DeviceScan::ExclusiveSum(a.temp, tb, (const int32_t *)a.row_pcnt, a.row_poff, a.n_qt + 1, stream);
+    err = dev_exclusive_scan((const int32_t *)a.row_pcnt, a.row_poff, (int64_t)a.n_qt + 1, a.temp, a.temp_bytes,
+                             stream);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(blk_tail_kernel, dim3(1), dim3(64), 0, stream, a);
     if (a.n_qt > 0 && a.nbq > 0)

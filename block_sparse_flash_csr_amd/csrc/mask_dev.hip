@@ -12,14 +12,16 @@
 //   1. expand: the host lists every (slice, query tile) pair with the key-tile range the
 //      slice reaches there and the pair's output offset (O(sum of query tiles per
 //      slice)); one wave per pair writes the keys (tile << sbits) | slice;
-//   2. radix sort of the keys (hipCUB), so a tile's incidences are adjacent and in
+//   2. stable radix sort of the keys (dev_sort.hip), so a tile's incidences are adjacent and in
 //      slice order, tiles in (query tile, key tile) order;
 //   3. heads of equal-tile runs -> entry numbers (exclusive scan);
 //   4. per entry: full / partial, admitted pairs (closed form for one slice, a per-row
 //      bitmap union for several), piece count;
 //   5. piece offsets (exclusive scan), then col, tag, piece_ptr, pieces, row_ptr and the
 //      totals.
-#include <hipcub/hipcub.hpp>
+#include <algorithm>
+
+#include "dev_sort.h"
 
 #include "bsfa_internal.h"
 
@@ -233,15 +235,7 @@ inline unsigned grid_of(int64_t n) { return (unsigned)((n + kThreadsDev - 1) / k
 
 size_t dcsr_sort_temp_bytes(int64_t n, int32_t end_bit)
 {
-    // a failed query leaves 0: the sort or scan itself then fails and is reported
-    size_t a = 0, b = 0;
-    if (hipcub::DeviceRadixSort::SortKeys(nullptr, a, (const uint64_t *)nullptr, (uint64_t *)nullptr, (int)n, 0,
-                                          end_bit) != hipSuccess)
-        return 0;
-    if (hipcub::DeviceScan::ExclusiveSum(nullptr, b, (const int32_t *)nullptr, (int32_t *)nullptr, (int)n) !=
-        hipSuccess)
-        return 0;
-    return std::max(a, b);
+    return std::max(dev_sort_keys_temp_bytes(n, end_bit), dev_scan_temp_bytes(n));
 }
 
 hipError_t launch_dcsr(const DcsrArgs &a, hipStream_t stream)
@@ -255,21 +249,18 @@ hipError_t launch_dcsr(const DcsrArgs &a, hipStream_t stream)
     if (n == 0) return hipGetLastError();
     hipLaunchKernelGGL(expand_kernel, dim3((unsigned)((a.n_pairs + 3) / 4)), dim3(kThreadsDev), 0, stream,
                        a.pair_info, a.pair_off, a.n_pairs, g, a.keys_in);
-    size_t tb = a.temp_bytes;
-    hipError_t err = hipcub::DeviceRadixSort::SortKeys(a.temp, tb, (const uint64_t *)a.keys_in, a.keys, (int)n, 0,
-                                                       a.end_bit, stream);
+    hipError_t err = dev_sort_keys_u64((const uint64_t *)a.keys_in, a.keys, n, a.end_bit, a.temp, a.temp_bytes,
+                                       stream);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(head_kernel, dim3(grid_of(n)), dim3(kThreadsDev), 0, stream, (const uint64_t *)a.keys, n,
                        a.sbits, a.flag);
-    tb = a.temp_bytes;
-    err = hipcub::DeviceScan::ExclusiveSum(a.temp, tb, (const int32_t *)a.flag, a.seg, (int)n, stream);
+    err = dev_exclusive_scan((const int32_t *)a.flag, a.seg, n, a.temp, a.temp_bytes, stream);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_of(n)), dim3(kThreadsDev), 0, stream, a.e_pieces, n, 0);
     hipLaunchKernelGGL(entry_kernel, dim3(grid_of(n)), dim3(kThreadsDev), 0, stream, (const uint64_t *)a.keys,
                        (const int32_t *)a.flag, (const int32_t *)a.seg, n, g, a.slices, a.e_first, a.e_n, a.e_full,
                        a.e_pieces, a.totals);
-    tb = a.temp_bytes;
-    err = hipcub::DeviceScan::ExclusiveSum(a.temp, tb, (const int32_t *)a.e_pieces, a.p_off, (int)n, stream);
+    err = dev_exclusive_scan((const int32_t *)a.e_pieces, a.p_off, n, a.temp, a.temp_bytes, stream);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(write_kernel, dim3(grid_of(n)), dim3(kThreadsDev), 0, stream, (const uint64_t *)a.keys,
                        (const int32_t *)a.flag, (const int32_t *)a.seg, n, g, a.slices, (const int32_t *)a.e_first,

@@ -11,7 +11,7 @@
 // radix sort of the entries' key tiles (values: entry numbers), so within one key tile
 // the entries stay in ascending entry order, i.e. ascending query tile, exactly as the
 // host builds it.
-#include <hipcub/hipcub.hpp>
+#include "dev_sort.h"
 
 #include "bsfa_internal.h"
 
@@ -113,16 +113,7 @@ hipError_t launch_plan_counts(const DevPlanArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-size_t plan_sort_temp_bytes(int64_t nnz, int32_t end_bit)
-{
-    // a failed query leaves 0: the sort itself then fails and is reported
-    size_t t = 0;
-    if (hipcub::DeviceRadixSort::SortPairs(nullptr, t, (const int32_t *)nullptr, (int32_t *)nullptr,
-                                           (const int32_t *)nullptr, (int32_t *)nullptr, (int)nnz, 0, end_bit) !=
-        hipSuccess)
-        return 0;
-    return t;
-}
+size_t plan_sort_temp_bytes(int64_t nnz, int32_t end_bit) { return dev_sort_pairs_temp_bytes(nnz, end_bit); }
 
 hipError_t launch_plan_image(const DevPlanArgs &a, hipStream_t stream)
 {
@@ -131,9 +122,8 @@ hipError_t launch_plan_image(const DevPlanArgs &a, hipStream_t stream)
                        a.piece_ptr, a.nnz, a.entries, a.iota);
     hipLaunchKernelGGL(row_of_kernel, dim3(grid_of(a.nnz)), dim3(kThreadsPlan), 0, stream, a.row_ptr, a.n_qt,
                        a.nnz, a.row_of);
-    size_t tb = a.temp_bytes;
-    const hipError_t err = hipcub::DeviceRadixSort::SortPairs(a.temp, tb, a.col, a.keys_out, (const int32_t *)a.iota,
-                                                              a.sorted_e, (int)a.nnz, 0, a.end_bit, stream);
+    const hipError_t err = dev_sort_pairs_u32((const uint32_t *)a.col, (uint32_t *)a.keys_out, (const int32_t *)a.iota,
+                                              a.sorted_e, a.nnz, a.end_bit, a.temp, a.temp_bytes, stream);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(tlist_kernel, dim3(grid_of(a.nnz)), dim3(kThreadsPlan), 0, stream,
                        (const int32_t *)a.sorted_e, (const int32_t *)a.row_of, a.nnz, a.t_list);

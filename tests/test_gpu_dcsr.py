@@ -132,6 +132,39 @@ def test_plan_from_device_csr_equals_host_plan(cfg):
     dev.close()
 
 
+def test_plan_from_device_csr_at_65536_tokens():
+    """A causal mask of 65,536 tokens (131,328 entries: the column view's stable sort runs
+    over 33 workgroups of keys in two digit passes, the compiler's key sort over three):
+    the plan over the device CSR equals the host plan, and the forward and the backward,
+    which walks the column view, are bit-identical."""
+    import torch
+    S, hq, hkv, d = 65536, 2, 1, 64
+    sl = [(0, S, 0, S, 1)]
+    say(f"plan from device CSR: causal s{S} hq={hq} hkv={hkv} d={d}")
+    host = api.Plan.from_slices(sl, S, S, hq, hkv, d)
+    dc = api.DeviceCsr(sl, S, S)
+    dev = dc.plan(hq, hkv, d)
+    dc.close()
+    assert host.info()["nnz"] == 512 * 513 // 2
+    _same_plan(host, dev, f"causal s{S}")
+    rng = np.random.default_rng(65536)
+    qb, kb, vb = W.random_inputs(rng, S, S, hq, hkv, d)
+    q, k, v = api.to_device_bf16(qb), api.to_device_bf16(kb), api.to_device_bf16(vb)
+    host.upload()
+    dev.upload()
+    oh, lh = api.attn_fwd(q, k, v, host, 0.125)
+    od, ld = api.attn_fwd(q, k, v, dev, 0.125)
+    g = api.to_device_bf16(W.random_grad(rng, S, hq, d))
+    gh = api.attn_bwd(q, k, v, g, lh, host, 0.125)
+    gd = api.attn_bwd(q, k, v, g, ld, dev, 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(oh.view(torch.int16), od.view(torch.int16)) and torch.equal(lh, ld)
+    for name, x, y in zip(("dQ", "dK", "dV"), gh, gd):
+        assert torch.equal(x, y), name
+    host.close()
+    dev.close()
+
+
 def test_plan_from_device_csr_split_rows_and_ragged_tails():
     """Few query rows against long keys (rows split into parts), ragged extents, head
     dim 64 and 64-key plan tiles; the forward on the device CSR's plan equals the host
