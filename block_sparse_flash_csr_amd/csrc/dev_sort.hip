@@ -11,9 +11,11 @@
 // exclusive-scanned, which gives every (digit, workgroup) its first output slot; (3) each
 // workgroup walks its keys in index order, 256 at a time: the lanes of a wave holding
 // the same digit find one another with 8 ballots (a key's rank = lanes below it with
-// that digit), the waves are ordered through their digit counts in LDS, and the key goes
-// to slot + rank.  Keys with equal digits keep their order, so the passes compose to a
-// stable sort.  No atomics outside LDS counters; results do not depend on timing.
+// that digit), the waves are ordered through their digit counts in LDS, and the key is
+// staged in LDS at its digit's start + its rank; the staged keys then go out in order,
+// each digit's run to consecutive slots from the digit's first slot.  Keys with equal
+// digits keep their order, so the passes compose to a stable sort.  No atomics outside
+// LDS counters; results do not depend on timing.
 #include "dev_sort.h"
 
 #include <climits>
@@ -134,21 +136,46 @@ __global__ void __launch_bounds__(kT) rs_hist_kernel(const K *__restrict__ keys,
 }
 
 // Stable scatter of one digit pass; off holds the exclusive scan of the digit table.
+// The workgroup first orders its keys by digit in LDS (stable), then writes each digit's
+// run to consecutive output slots, so that neighbouring threads store to neighbouring
+// addresses.
 template <typename K, bool PAIRS>
 __global__ void __launch_bounds__(kT) rs_scatter_kernel(const K *__restrict__ keys, const int32_t *__restrict__ vals,
                                                         int64_t n, int shift, const int32_t *__restrict__ off,
                                                         int32_t nblk, K *__restrict__ keys_out,
                                                         int32_t *__restrict__ vals_out)
 {
-    __shared__ int32_t slot[256];            // next output slot of every digit
-    __shared__ int32_t wcnt[kWaves][256];    // per-wave digit counts of the current round
+    __shared__ K skey[kTile];                       // the tile's keys in digit order
+    __shared__ int32_t sval[PAIRS ? kTile : 1];
+    __shared__ int32_t gslot[256];                  // first output slot of every digit
+    __shared__ int32_t lstart[256];                 // first staged position of every digit
+    __shared__ int32_t run[256];                    // keys of every digit staged so far
+    __shared__ int32_t wcnt[kWaves][256];           // per-wave digit counts of the current round
+    __shared__ int32_t wsum[kWaves];
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
-    slot[t] = off[(int64_t)t * nblk + blockIdx.x];
+    const int64_t base = (int64_t)blockIdx.x * kTile;
+    const int32_t count = (int32_t)(n - base < kTile ? n - base : kTile);   // keys of this tile
+
+    // this tile's digit counts -> where each digit starts in the staged order
+    run[t] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+        const int64_t k = base + i * kT + t;
+        if (k < n) atomicAdd(&run[(int)((keys[k] >> shift) & 0xFFu)], 1);
+    }
+    __syncthreads();
+    int32_t total;
+    const int32_t c = run[t];
+    lstart[t] = block_excl_scan(c, wsum, total);
+    run[t] = 0;
+    gslot[t] = off[(int64_t)t * nblk + blockIdx.x];
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) wcnt[ww][t] = 0;
     __syncthreads();
+
+    // stage the keys in index order within each digit
     const uint64_t below = (1ull << lane) - 1ull;
-    const int64_t base = (int64_t)blockIdx.x * kTile;
     for (int i = 0; i < kItems; ++i) {
         const int64_t k = base + i * kT + t;
         const bool valid = k < n;
@@ -167,22 +194,36 @@ __global__ void __launch_bounds__(kT) rs_scatter_kernel(const K *__restrict__ ke
         if (valid && rank == 0) wcnt[w][d] = __popcll(same);
         __syncthreads();
         if (valid) {
-            int64_t pos = (int64_t)slot[d] + rank;
-            for (int ww = 0; ww < w; ++ww) pos += wcnt[ww][d];
-            if (pos >= 0 && pos < n) {   // always true when the counts agree
-                keys_out[pos] = key;
-                if (PAIRS) vals_out[pos] = val;
+            int32_t lp = lstart[d] + run[d] + rank;
+            for (int ww = 0; ww < w; ++ww) lp += wcnt[ww][d];
+            if (lp >= 0 && lp < count) {   // always true when the counts agree
+                skey[lp] = key;
+                if (PAIRS) sval[lp] = val;
             }
         }
         __syncthreads();
-        int32_t c = 0;
+        int32_t cw = 0;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-            c += wcnt[ww][t];
+            cw += wcnt[ww][t];
             wcnt[ww][t] = 0;
         }
-        slot[t] += c;
+        run[t] += cw;
         __syncthreads();
+    }
+
+    // write the staged keys: digit d's j-th key goes to gslot[d] + j
+    for (int i = 0; i < kItems; ++i) {
+        const int32_t j = i * kT + t;
+        if (j < count) {
+            const K key = skey[j];
+            const int d = (int)((key >> shift) & 0xFFu);
+            const int64_t pos = (int64_t)gslot[d] + (j - lstart[d]);
+            if (pos >= 0 && pos < n) {   // always true when the counts agree
+                keys_out[pos] = key;
+                if (PAIRS) vals_out[pos] = sval[j];
+            }
+        }
     }
 }
 
